@@ -1,0 +1,246 @@
+"""TiDAR decode-step hot path on MI355X (gfx950): thin Python binding.
+
+The three calls of ``include/tidar.h`` -- ``step_attention``,
+``verify_greedy`` and ``kv_commit`` -- under the same names, taking torch
+tensors that live on the GPU.  This module only checks shapes and dtypes,
+marshals pointers and the current HIP stream, and allocates outputs /
+workspace with torch when the caller does not pass them.  Every step of the
+computation runs in the HIP kernels of ``libtidar.so``; there is no other
+implementation, and every call fails loudly (ImportError) when the library has not
+been built (``python -m diffusion_drafted_self_amd.build``).
+
+Tensor layouts (row-major, contiguous):
+  q [B][R][Hq][D], k_step/v_step [B][R][Hkv][D],
+  k_cache [B][Hkv][S_max][D], v_cache [B][Hkv][D][S_max] (values transposed),
+  lens [B] int32, ar_logits [B][k+1][V] f32, draft_logits [B][k][k][V] f32,
+  cand [B][k] int32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtidar.so")
+
+TIDAR_OK, TIDAR_EINVAL, TIDAR_EUNSUPPORTED, TIDAR_EWORKSPACE, TIDAR_ELAUNCH = 0, -1, -2, -3, -4
+TIDAR_BF16, TIDAR_F32 = 0, 1
+
+# every symbol include/tidar.h declares, with its ctypes signature
+_c_int, _c_size, _p, _f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+SIGNATURES = {
+    "tidar_strerror": (ctypes.c_char_p, [_c_int]),
+    "tidar_abi_version": (_c_int, []),
+    "tidar_step_attention_workspace": (_c_int, [_c_int] * 10 + [ctypes.POINTER(_c_size)]),
+    "tidar_step_attention": (_c_int, [_c_int] * 9 + [_f, _c_int] + [_p] * 9 + [_c_size, _p]),
+    "tidar_verify_workspace": (_c_int, [_c_int] * 3 + [ctypes.POINTER(_c_size)]),
+    "tidar_verify_greedy": (_c_int, [_c_int] * 3 + [_p] * 6 + [_c_size, _p]),
+    "tidar_kv_commit": (_c_int, [_c_int] * 7 + [_p] * 7 + [_p]),
+}
+
+
+class TidarError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed with status {status}: {strerror(status)}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m diffusion_drafted_self_amd.build` "
+                          "(the TiDAR path has no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.tidar_abi_version() != 1:
+        raise ImportError("libtidar.so ABI version mismatch; rebuild it")
+    return lib
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libtidar.so (loaded on first use; raises ImportError if it
+    has not been built)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
+def strerror(status: int) -> str:
+    return lib().tidar_strerror(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != TIDAR_OK:
+        raise TidarError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TIDAR_BF16
+    if t.dtype == torch.float32:
+        return TIDAR_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _need(t, name, dtype=None, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _workspace(nbytes: int, device, given):
+    if given is not None:
+        _need(given, "workspace", torch.uint8, 1, device)
+        return given
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------------ attention
+def step_attention_workspace_bytes(dtype_code: int, B: int, Hq: int, Hkv: int, D: int, S_max: int,
+                                   max_len: int, k: int, n_groups: int, kv_chunk: int = 0) -> int:
+    n = _c_size(0)
+    _check("tidar_step_attention_workspace",
+           lib().tidar_step_attention_workspace(dtype_code, B, Hq, Hkv, D, S_max, max_len, k, n_groups,
+                                               kv_chunk, ctypes.byref(n)))
+    return n.value
+
+
+def step_attention(q, k_step, v_step, k_cache, v_cache, lens, k: int, n_groups: int, sm_scale: float,
+                   max_len: int = None, out=None, lse=None, want_lse: bool = True, workspace=None,
+                   kv_chunk: int = 0):
+    """Structured-mask attention of one TiDAR step.  Returns (out, lse).
+
+    ``max_len`` is the host-side upper bound on ``lens`` (reading it from the
+    device costs a synchronisation when omitted)."""
+    _need(q, "q", ndim=4)
+    dev = q.device
+    dt = q.dtype
+    B, R, Hq, D = q.shape
+    _need(k_step, "k_step", dt, 4, dev)
+    _need(v_step, "v_step", dt, 4, dev)
+    _need(k_cache, "k_cache", dt, 4, dev)
+    _need(v_cache, "v_cache", dt, 4, dev)
+    _need(lens, "lens", torch.int32, 1, dev)
+    Hkv = k_step.shape[2]
+    S_max = k_cache.shape[2]
+    if R != k + n_groups * k:
+        raise ValueError(f"q has {R} step rows, expected k + n_groups*k = {k + n_groups * k}")
+    if tuple(k_step.shape) != (B, R, Hkv, D) or tuple(v_step.shape) != (B, R, Hkv, D):
+        raise ValueError("k_step/v_step must be [B][R][Hkv][D]")
+    if tuple(k_cache.shape) != (B, Hkv, S_max, D) or tuple(v_cache.shape) != (B, Hkv, D, S_max):
+        raise ValueError("k_cache must be [B][Hkv][S_max][D] and v_cache [B][Hkv][D][S_max]")
+    if lens.shape[0] != B:
+        raise ValueError("lens must be [B]")
+    if max_len is None:
+        max_len = int(lens.max().item()) if B > 0 else 0
+    code = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", dt, 4, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, R), dtype=torch.float32, device=dev)
+    elif lse is not None:
+        _need(lse, "lse", torch.float32, 3, dev)
+        if tuple(lse.shape) != (B, Hq, R):
+            raise ValueError("lse must be [B][Hq][R]")
+    nbytes = step_attention_workspace_bytes(code, B, Hq, Hkv, D, S_max, max_len, k, n_groups, kv_chunk)
+    ws = _workspace(nbytes, dev, workspace)
+    _check("tidar_step_attention",
+           lib().tidar_step_attention(code, B, Hq, Hkv, D, S_max, int(max_len), k, n_groups, float(sm_scale),
+                                     int(kv_chunk), _ptr(q), _ptr(k_step), _ptr(v_step), _ptr(k_cache),
+                                     _ptr(v_cache), _ptr(lens), _ptr(out), _ptr(lse), _ptr(ws),
+                                     ws.numel(), _stream()))
+    return out, lse
+
+
+# ------------------------------------------------------------------------ verify
+def verify_workspace_bytes(B: int, k: int, V: int) -> int:
+    n = _c_size(0)
+    _check("tidar_verify_workspace", lib().tidar_verify_workspace(B, k, V, ctypes.byref(n)))
+    return n.value
+
+
+def verify_greedy(ar_logits, draft_logits, cand, accept_len=None, next_cand=None, workspace=None):
+    """Greedy verification of the carried candidates.  Returns (accept_len, next_cand)."""
+    _need(ar_logits, "ar_logits", torch.float32, 3)
+    dev = ar_logits.device
+    B, k1, V = ar_logits.shape
+    k = k1 - 1
+    _need(cand, "cand", torch.int32, 2, dev)
+    if tuple(cand.shape) != (B, k):
+        raise ValueError("cand must be [B][k]")
+    if k > 1 or draft_logits is not None:
+        _need(draft_logits, "draft_logits", torch.float32, 4, dev)
+        if tuple(draft_logits.shape) != (B, k, k, V):
+            raise ValueError("draft_logits must be [B][k][k][V]")
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    else:
+        _need(accept_len, "accept_len", torch.int32, 1, dev)
+    if next_cand is None:
+        next_cand = torch.empty((B, k), dtype=torch.int32, device=dev)
+    else:
+        _need(next_cand, "next_cand", torch.int32, 2, dev)
+    ws = _workspace(verify_workspace_bytes(B, k, V), dev, workspace)
+    _check("tidar_verify_greedy",
+           lib().tidar_verify_greedy(B, k, V, _ptr(ar_logits), _ptr(draft_logits), _ptr(cand), _ptr(accept_len),
+                                    _ptr(next_cand), _ptr(ws), ws.numel(), _stream()))
+    return accept_len, next_cand
+
+
+# ------------------------------------------------------------------------ commit
+def kv_commit(k_cache, v_cache, lens, k_step, v_step, accept_len, k: int, err_flags=None):
+    """Append the accepted candidate rows to the caches in place and advance
+    ``lens``.  Returns ``err_flags`` (or None when not requested)."""
+    _need(k_cache, "k_cache", ndim=4)
+    dev, dt = k_cache.device, k_cache.dtype
+    B, Hkv, S_max, D = k_cache.shape
+    _need(v_cache, "v_cache", dt, 4, dev)
+    _need(k_step, "k_step", dt, 4, dev)
+    _need(v_step, "v_step", dt, 4, dev)
+    _need(lens, "lens", torch.int32, 1, dev)
+    _need(accept_len, "accept_len", torch.int32, 1, dev)
+    R = k_step.shape[1]
+    if tuple(v_cache.shape) != (B, Hkv, D, S_max):
+        raise ValueError("v_cache must be [B][Hkv][D][S_max]")
+    if tuple(k_step.shape) != (B, R, Hkv, D) or tuple(v_step.shape) != (B, R, Hkv, D):
+        raise ValueError("k_step/v_step must be [B][R][Hkv][D]")
+    if err_flags is not None:
+        _need(err_flags, "err_flags", torch.int32, 1, dev)
+    _check("tidar_kv_commit",
+           lib().tidar_kv_commit(_dtype_code(k_cache), B, Hkv, D, S_max, R, k, _ptr(k_cache), _ptr(v_cache),
+                                _ptr(lens), _ptr(k_step), _ptr(v_step), _ptr(accept_len), _ptr(err_flags),
+                                _stream()))
+    return err_flags
+
+
+__all__ = ["step_attention", "step_attention_workspace_bytes", "verify_greedy", "verify_workspace_bytes",
+           "kv_commit", "strerror", "lib", "TidarError", "LIB_PATH", "SIGNATURES"]

@@ -1,0 +1,68 @@
+"""Builds libtidar.so for gfx950 in-tree with hipcc (no JIT cache, no install).
+
+The library is the only native artefact: the kernels (attention, verify,
+commit) and the C ABI of include/tidar.h.  Every HIP source is compiled with
+packed fp32 instructions disabled."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libtidar.so")
+SOURCES = ["attention.hip", "verify.hip", "commit.hip", "capi.cpp"]
+ARCH = "gfx950"
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the TiDAR library needs ROCm's hipcc to build")
+
+
+def _quiet(text: str) -> str:
+    # the host pass does not know the packed-fp32 feature flag; that warning is expected
+    return "\n".join(l for l in text.splitlines() if "packed-fp32-ops" not in l)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libtidar.so; returns its path."""
+    hipcc = _hipcc()
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
+             "-I", INCLUDE, "-I", CSRC,
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+    procs, objs = [], []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        objs.append(obj)
+        cmd = [hipcc] + flags + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    failed = []
+    for src, cmd, p in procs:
+        out, _ = p.communicate()
+        out = _quiet(out)
+        if p.returncode != 0:
+            failed.append(f"{src}: {' '.join(cmd)}\n{out}")
+        elif verbose and out.strip():
+            print(out, file=sys.stderr)
+    if failed:
+        raise RuntimeError("HIP build failed:\n" + "\n".join(failed))
+    tmp = LIB + ".tmp"
+    link = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    p = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if p.returncode != 0:
+        raise RuntimeError("link failed: " + " ".join(link) + "\n" + p.stdout)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,250 @@
+// C ABI of the TiDAR decode-step hot path: host-side validation, split
+// planning, workspace carving and kernel launches.  No allocation, no
+// synchronisation, no state kept between calls.
+#include "tidar.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxK = 16;
+constexpr int kTileKeys = 64;           // keys per attention tile
+constexpr int kMaxChunkF32 = 1024;      // LDS score buffer of the f32 kernel
+constexpr int kVerifyChunk = 4096;      // logits per argmax workgroup
+constexpr long kTargetWorkgroups = 1024; // about four per CU on 256 CUs
+
+bool aligned(const void* p, uintptr_t a) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+long cdiv(long a, long b) { return (a + b - 1) / b; }
+
+struct AttnPlan {
+  int R, G, M, waves, n_rowblk, chunk, n_split;
+  size_t o_bytes, ml_bytes, total;
+};
+
+// Split plan of the step attention.  Rows of one (b, kvh): M = R*G in
+// 32-row MFMA tiles; a workgroup takes `waves` tiles, picked to leave the
+// fewest padding waves.  Keys: `chunk` positions per workgroup, chosen so
+// the grid holds about kTargetWorkgroups workgroups but chunks stay >= 256
+// keys (each chunk's partial output costs M*(D+2)*4 bytes of traffic).
+int plan_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_len, int k,
+                   int n_groups, int kv_chunk, AttnPlan* p) {
+  if (dtype != TIDAR_BF16 && dtype != TIDAR_F32) return TIDAR_EUNSUPPORTED;
+  if (D != 64 && D != 128) return TIDAR_EUNSUPPORTED;
+  if (k > kMaxK) return TIDAR_EUNSUPPORTED;
+  if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || k < 1) return TIDAR_EINVAL;
+  if (n_groups != 0 && n_groups != k) return TIDAR_EINVAL;
+  if (S_max < 1 || S_max % 8 != 0 || max_len < 0 || max_len > S_max) return TIDAR_EINVAL;
+  if (kv_chunk < 0 || kv_chunk % kTileKeys != 0) return TIDAR_EINVAL;
+  if (dtype == TIDAR_F32 && kv_chunk > kMaxChunkF32) return TIDAR_EINVAL;
+
+  p->R = k + n_groups * k;
+  p->G = Hq / Hkv;
+  p->M = p->R * p->G;
+  const long keys = (long)max_len + p->R;
+
+  const int n_tiles = (int)cdiv(p->M, 32);
+  int best_w = 4, best_pad = 1 << 30;
+  for (int w = 4; w >= 1; --w) {
+    const int pad = (int)cdiv(n_tiles, w) * w - n_tiles;
+    if (pad < best_pad) { best_pad = pad; best_w = w; }
+  }
+  p->waves = best_w;
+  p->n_rowblk = (int)cdiv(n_tiles, best_w);
+
+  long chunk = kv_chunk;
+  if (chunk == 0) {
+    if (dtype == TIDAR_F32) {
+      chunk = std::min<long>(kMaxChunkF32, (long)round_up(keys, kTileKeys));
+    } else {
+      const long base = std::max<long>(1, (long)B * Hkv * p->n_rowblk);
+      long n_split = cdiv(kTargetWorkgroups, base);
+      n_split = std::max<long>(1, std::min<long>(n_split, cdiv(keys, 256)));
+      chunk = (long)round_up(cdiv(keys, n_split), kTileKeys);
+    }
+  }
+  p->chunk = (int)chunk;
+  p->n_split = (int)cdiv(keys, chunk);
+
+  const long blocks = (long)B * Hkv * p->n_split * (dtype == TIDAR_F32 ? p->M : p->n_rowblk);
+  if (blocks > 0x7fffffffL) return TIDAR_EUNSUPPORTED;
+
+  const size_t parts = (size_t)B * Hkv * p->n_split * p->M;
+  p->o_bytes = round_up(parts * D * sizeof(float), 256);
+  p->ml_bytes = round_up(parts * sizeof(float2), 256);
+  p->total = p->o_bytes + p->ml_bytes;
+  return TIDAR_OK;
+}
+
+struct VerifyPlan {
+  int n_chunks;
+  size_t ar_bytes, draft_bytes, group_bytes, total;
+};
+
+int plan_verify(int B, int k, int V, VerifyPlan* p) {
+  if (k > kMaxK) return TIDAR_EUNSUPPORTED;
+  if (B < 0 || k < 1 || V < 1) return TIDAR_EINVAL;
+  if ((long)B * (k + 1) > 65535) return TIDAR_EUNSUPPORTED;  // grid y limit
+  p->n_chunks = (int)cdiv(V, kVerifyChunk);
+  p->ar_bytes = round_up((size_t)B * (k + 1) * p->n_chunks * sizeof(float2), 256);
+  p->draft_bytes = round_up((size_t)B * (k - 1) * p->n_chunks * sizeof(float2), 256);
+  p->group_bytes = round_up((size_t)B * sizeof(int32_t), 256);
+  p->total = p->ar_bytes + p->draft_bytes + p->group_bytes;
+  return TIDAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tidar_strerror(int status) {
+  switch (status) {
+    case TIDAR_OK: return "ok";
+    case TIDAR_EINVAL: return "invalid argument (shape, pointer, alignment or value)";
+    case TIDAR_EUNSUPPORTED: return "unsupported configuration (dtype, head dim, k or size)";
+    case TIDAR_EWORKSPACE: return "workspace missing or too small";
+    case TIDAR_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int tidar_abi_version(void) { return 1; }
+
+int tidar_step_attention_workspace(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_len,
+                                   int k, int n_groups, int kv_chunk, size_t* bytes) {
+  if (!bytes) return TIDAR_EINVAL;
+  AttnPlan p;
+  const int st = plan_attention(dtype, B, Hq, Hkv, D, S_max, max_len, k, n_groups, kv_chunk, &p);
+  if (st != TIDAR_OK) return st;
+  *bytes = p.total;
+  return TIDAR_OK;
+}
+
+int tidar_step_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_len,
+                         int k, int n_groups, float sm_scale, int kv_chunk,
+                         const void* q, const void* k_step, const void* v_step,
+                         const void* k_cache, const void* v_cache, const int32_t* lens,
+                         void* out, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  AttnPlan p;
+  const int st = plan_attention(dtype, B, Hq, Hkv, D, S_max, max_len, k, n_groups, kv_chunk, &p);
+  if (st != TIDAR_OK) return st;
+  if (!(sm_scale > 0.f) || !(sm_scale < 3.0e38f)) return TIDAR_EINVAL;
+  if (B == 0) return TIDAR_OK;
+  if (!aligned(q, 16) || !aligned(k_step, 16) || !aligned(v_step, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(out, 16) || !aligned(lens, 4))
+    return TIDAR_EINVAL;
+  if (lse && !aligned(lse, 4)) return TIDAR_EINVAL;
+  if (!aligned(workspace, 256) || workspace_bytes < p.total) return TIDAR_EWORKSPACE;
+
+  tidar::AttnArgs a;
+  a.q = q;
+  a.k_step = k_step;
+  a.v_step = v_step;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.lens = lens;
+  a.out = out;
+  a.lse = lse;
+  a.o_part = static_cast<float*>(workspace);
+  a.ml_part = reinterpret_cast<float2*>(static_cast<char*>(workspace) + p.o_bytes);
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = p.G;
+  a.D = D;
+  a.S_max = S_max;
+  a.max_len = max_len;
+  a.k = k;
+  a.R = p.R;
+  a.M = p.M;
+  a.chunk = p.chunk;
+  a.n_split = p.n_split;
+  a.waves = p.waves;
+  a.n_rowblk = p.n_rowblk;
+  a.scale_log2 = sm_scale * 1.44269504088896340736f;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = dtype == TIDAR_BF16 ? tidar::launch_attention_bf16(a, s) : tidar::launch_attention_f32(a, s);
+  return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
+}
+
+int tidar_verify_workspace(int B, int k, int V, size_t* bytes) {
+  if (!bytes) return TIDAR_EINVAL;
+  VerifyPlan p;
+  const int st = plan_verify(B, k, V, &p);
+  if (st != TIDAR_OK) return st;
+  *bytes = p.total;
+  return TIDAR_OK;
+}
+
+int tidar_verify_greedy(int B, int k, int V, const float* ar_logits, const float* draft_logits,
+                        const int32_t* cand, int32_t* accept_len, int32_t* next_cand,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  VerifyPlan p;
+  const int st = plan_verify(B, k, V, &p);
+  if (st != TIDAR_OK) return st;
+  if (B == 0) return TIDAR_OK;
+  if (!aligned(ar_logits, 16) || !aligned(cand, 4) || !aligned(accept_len, 4) || !aligned(next_cand, 4))
+    return TIDAR_EINVAL;
+  if (k > 1 && !aligned(draft_logits, 16)) return TIDAR_EINVAL;
+  if (!aligned(workspace, 256) || workspace_bytes < p.total) return TIDAR_EWORKSPACE;
+
+  tidar::VerifyArgs a;
+  a.ar_logits = ar_logits;
+  a.draft_logits = draft_logits;
+  a.cand = cand;
+  a.accept_len = accept_len;
+  a.next_cand = next_cand;
+  char* ws = static_cast<char*>(workspace);
+  a.part_ar = reinterpret_cast<float2*>(ws);
+  a.part_draft = reinterpret_cast<float2*>(ws + p.ar_bytes);
+  a.group = reinterpret_cast<int32_t*>(ws + p.ar_bytes + p.draft_bytes);
+  a.B = B;
+  a.k = k;
+  a.V = V;
+  a.chunk_elems = kVerifyChunk;
+  a.n_chunks = p.n_chunks;
+  const hipError_t e = tidar::launch_verify(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
+}
+
+int tidar_kv_commit(int dtype, int B, int Hkv, int D, int S_max, int R, int k,
+                    void* k_cache, void* v_cache, int32_t* lens,
+                    const void* k_step, const void* v_step, const int32_t* accept_len,
+                    int32_t* err_flags, void* stream) {
+  if (dtype != TIDAR_BF16 && dtype != TIDAR_F32) return TIDAR_EUNSUPPORTED;
+  if (D != 64 && D != 128) return TIDAR_EUNSUPPORTED;
+  if (B < 0 || Hkv < 1 || S_max < 1 || S_max % 8 != 0 || R < 1 || k < 1 || k > R) return TIDAR_EINVAL;
+  if (B == 0) return TIDAR_OK;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_step, 16) || !aligned(v_step, 16) ||
+      !aligned(lens, 4) || !aligned(accept_len, 4))
+    return TIDAR_EINVAL;
+  if (err_flags && !aligned(err_flags, 4)) return TIDAR_EINVAL;
+
+  tidar::CommitArgs a;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.lens = lens;
+  a.k_step = k_step;
+  a.v_step = v_step;
+  a.accept_len = accept_len;
+  a.err_flags = err_flags;
+  a.B = B;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.S_max = S_max;
+  a.R = R;
+  a.k = k;
+  a.elem_bytes = dtype == TIDAR_BF16 ? 2 : 4;
+  const hipError_t e = tidar::launch_commit(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Device-side types and helpers shared by the TiDAR kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tidar {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+// Running-max start value: finite, so a chunk that sees no key keeps
+// exp2(m_old - m_new) == 1 and contributes exp2(-inf - m) == 0.
+constexpr float kNoMax = -1.0e30f;
+
+// Visibility of step row j (0..R-1) from step row r, for k candidates.
+// Candidates are scored strictly left to right; the slot group g (the
+// outcome "candidates 0..g survive") sees those candidates and its own k
+// slots ("TiDAR : l'hybride de NVIDIA qui rédige par diffusion et parle de
+// manière autorégressive", nodesdaily.com, paragraph on masking).  Settled
+// positions are visible to every row and never reach this test.
+__device__ __forceinline__ bool step_visible(int r, int j, int k) {
+  if (r < k) return j <= r;
+  const int g = (r - k) / k;
+  if (j < k) return j <= g;
+  return (j - k) / k == g;
+}
+
+// Block index remap for a 8-XCD part: the hardware hands consecutive
+// workgroup ids round-robin to the XCDs, so ids i, i+8, i+16, ... share an
+// XCD (and its L2).  The returned logical id makes runs of consecutive
+// logical ids land on one XCD.
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblk) {
+  const int per = nblk >> 3;
+  return (bid < (per << 3)) ? ((bid & 7) * per + (bid >> 3)) : bid;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+}  // namespace tidar

@@ -1,0 +1,61 @@
+// Host-side launch interface between the C ABI (capi.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tidar {
+
+// Split plan and arguments of the step-attention kernels.  Query rows of
+// one (sequence, KV head) are numbered m = r*G + j (step row r, head j of
+// the group), M = R*G of them.  Keys are the [prefix ; step] sequence of
+// L+R positions, cut into chunks of `chunk` positions.
+struct AttnArgs {
+  const void* q;
+  const void* k_step;
+  const void* v_step;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* lens;
+  void* out;
+  float* lse;
+  float* o_part;   // [B][Hkv][n_split][M][D]  unnormalised partial outputs
+  float2* ml_part; // [B][Hkv][n_split][M]     (running max in log2 units, sum)
+  int B, Hq, Hkv, G, D, S_max, max_len, k, R, M;
+  int chunk, n_split;
+  int waves, n_rowblk;  // bf16 path: waves per workgroup, row blocks per (b, kvh)
+  float scale_log2;     // sm_scale * log2(e)
+};
+
+hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t s);
+
+struct VerifyArgs {
+  const float* ar_logits;
+  const float* draft_logits;
+  const int32_t* cand;
+  int32_t* accept_len;
+  int32_t* next_cand;
+  float2* part_ar;     // [B*(k+1)][n_chunks] (value, index bits)
+  float2* part_draft;  // [B*(k-1)][n_chunks]
+  int32_t* group;      // [B]
+  int B, k, V, chunk_elems, n_chunks;
+};
+
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
+
+struct CommitArgs {
+  void* k_cache;
+  void* v_cache;
+  int32_t* lens;
+  const void* k_step;
+  const void* v_step;
+  const int32_t* accept_len;
+  int32_t* err_flags;
+  int B, Hkv, D, S_max, R, k, elem_bytes;
+};
+
+hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
+
+}  // namespace tidar

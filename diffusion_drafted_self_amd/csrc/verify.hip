@@ -1,0 +1,153 @@
+// Greedy verification and next-draft selection on gfx950.
+//
+// Candidates are confirmed strictly left to right; the drafts prepared for
+// the confirmed outcome become the next candidates ("TiDAR : l'hybride de
+// NVIDIA qui rédige par diffusion et parle de manière autorégressive",
+// nodesdaily.com, paragraph on drafting for every outcome).
+//
+// The work is a streaming argmax over fp32 logit rows (HBM-bound):
+//   argmax_partial_kernel<false>  (chunk, AR row): 16 B loads, per-thread
+//       (value, index) with strict '>' (indices ascend inside a thread, so
+//       the lowest index wins ties), wave shuffles, then LDS across waves.
+//   verify_select_kernel   one wave per sequence: reduces each AR row's
+//       chunk results in order i = 0..k and stops at the first mismatch:
+//       accept length, bonus token, draft group.
+//   argmax_partial_kernel<true>   the selected group's draft rows 1..k-1.
+//   draft_finalize_kernel  one wave per sequence: the next drafts.
+// Ties compare as (value, lower index); -0.0 == +0.0 by IEEE compare.
+#include <climits>
+
+#include "common.h"
+#include "launch.h"
+
+namespace tidar {
+
+namespace {
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    if (better(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+}
+
+template <bool DRAFT>
+__global__ __launch_bounds__(256) void argmax_partial_kernel(VerifyArgs a) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int chunk = blockIdx.x;
+  const int row = blockIdx.y;
+  const float* src;
+  float2* dst;
+  if (!DRAFT) {
+    src = a.ar_logits + (size_t)row * a.V;
+    dst = a.part_ar + (size_t)row * a.n_chunks + chunk;
+  } else {
+    const int b = row / (a.k - 1);
+    const int mm = 1 + row % (a.k - 1);
+    const int g = a.group[b];
+    src = a.draft_logits + (((size_t)b * a.k + g) * a.k + mm) * a.V;
+    dst = a.part_draft + (size_t)row * a.n_chunks + chunk;
+  }
+  const int lo = chunk * a.chunk_elems;
+  const int hi = min(a.V, lo + a.chunk_elems);
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  if ((a.V & 3) == 0) {
+    for (int i = lo + 4 * (int)threadIdx.x; i < hi; i += 4 * 256) {
+      const float4 x = *(const float4*)(src + i);
+      if (x.x > bv) { bv = x.x; bi = i; }
+      if (x.y > bv) { bv = x.y; bi = i + 1; }
+      if (x.z > bv) { bv = x.z; bi = i + 2; }
+      if (x.w > bv) { bv = x.w; bi = i + 3; }
+    }
+  } else {
+    for (int i = lo + (int)threadIdx.x; i < hi; i += 256) {
+      const float x = src[i];
+      if (x > bv) { bv = x; bi = i; }
+    }
+  }
+  wave_argmax(bv, bi);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    sv[wave] = bv;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (better(sv[w], si[w], bv, bi)) {
+        bv = sv[w];
+        bi = si[w];
+      }
+    *dst = make_float2(bv, __int_as_float(bi));
+  }
+}
+
+// Reduce the chunk results of one row; every lane returns the row argmax.
+__device__ __forceinline__ int reduce_row(const float2* part, int n_chunks) {
+  const int lane = threadIdx.x & 63;
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  for (int c = lane; c < n_chunks; c += 64) {
+    const float2 p = part[c];
+    const int pi = __float_as_int(p.y);
+    if (better(p.x, pi, bv, bi)) {
+      bv = p.x;
+      bi = pi;
+    }
+  }
+  wave_argmax(bv, bi);
+  return bi;
+}
+
+__global__ __launch_bounds__(64) void verify_select_kernel(VerifyArgs a) {
+  const int b = blockIdx.x;
+  int acc = 0, bonus = 0;
+  for (int i = 0; i <= a.k; ++i) {
+    const int t = reduce_row(a.part_ar + ((size_t)b * (a.k + 1) + i) * a.n_chunks, a.n_chunks);
+    if (i < a.k && a.cand[(size_t)b * a.k + i] == t) {
+      ++acc;
+    } else {
+      bonus = t;
+      break;
+    }
+  }
+  if (threadIdx.x == 0) {
+    a.accept_len[b] = acc;
+    a.next_cand[(size_t)b * a.k] = bonus;
+    a.group[b] = (acc > 0 ? acc : 1) - 1;
+  }
+}
+
+__global__ __launch_bounds__(64) void draft_finalize_kernel(VerifyArgs a) {
+  const int b = blockIdx.x;
+  for (int mm = 1; mm < a.k; ++mm) {
+    const int t = reduce_row(a.part_draft + ((size_t)b * (a.k - 1) + (mm - 1)) * a.n_chunks, a.n_chunks);
+    if (threadIdx.x == 0) a.next_cand[(size_t)b * a.k + mm] = t;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  hipLaunchKernelGGL(argmax_partial_kernel<false>, dim3(a.n_chunks, a.B * (a.k + 1)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(verify_select_kernel, dim3(a.B), dim3(64), 0, s, a);
+  if (a.k > 1) {
+    hipLaunchKernelGGL(argmax_partial_kernel<true>, dim3(a.n_chunks, a.B * (a.k - 1)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(draft_finalize_kernel, dim3(a.B), dim3(64), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tidar

@@ -1,0 +1,170 @@
+/*
+ * tidar.h -- C ABI of the TiDAR decode-step hot path on MI355X (gfx950).
+ *
+ * One TiDAR decode step is a single forward pass whose query block holds,
+ * per sequence, the k draft candidates carried over from the previous step
+ * and k groups of k blank slots, one group for each verification outcome
+ * ("TiDAR : l'hybride de NVIDIA qui rédige par diffusion et parle de manière
+ * autorégressive", nodesdaily.com, paragraphs on the three zones and on
+ * drafting for every outcome).  The three calls below are the hot path of
+ * that step: the structured-mask attention of one layer, greedy verification
+ * of the candidates with selection of the next drafts, and the KV-cache
+ * commit / evict.
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers, row-major, 16-byte aligned.
+ *     The caller owns every buffer; the library never allocates, frees or
+ *     keeps state between calls, and never synchronises the device.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *     the default stream).  Calls are re-entrant across streams and buffers.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid call returns a negative status and enqueues nothing.  A launch
+ *     failure reported by the runtime returns TIDAR_ELAUNCH.  Faults inside
+ *     kernels surface at the caller's next synchronisation, as usual in HIP.
+ *   - bf16 means IEEE bfloat16 (round-to-nearest-even on output); f32 means
+ *     IEEE binary32.  Attention accumulates in f32 for both.
+ *
+ * Step block layout (a reading of the pages, which fix no layout):
+ *   R = k + n_groups*k rows per sequence, n_groups in {0, k}.
+ *   Row i < k            : candidate i (position L+i).
+ *   Row k + g*k + s      : slot s of group g, the group for the outcome
+ *                          "candidates 0..g survive" (position L+g+1+s).
+ *   Query head h reads KV head h / (Hq/Hkv).
+ */
+#ifndef TIDAR_H
+#define TIDAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  TIDAR_OK = 0,
+  TIDAR_EINVAL = -1,       /* bad shape, pointer, alignment or value */
+  TIDAR_EUNSUPPORTED = -2, /* valid request outside what is built (dtype, D, k) */
+  TIDAR_EWORKSPACE = -3,   /* workspace missing or smaller than required */
+  TIDAR_ELAUNCH = -4       /* the HIP runtime refused a launch */
+};
+
+enum { TIDAR_BF16 = 0, TIDAR_F32 = 1 };
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* tidar_strerror(int status);
+
+/* ABI version of this header (incremented on any signature change). */
+int tidar_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Step attention of one layer.
+ *
+ * Computes, for every sequence b, query head h and step row r,
+ *   out[b][r][h] = softmax_c(sm_scale * q[b][r][h] . key_c) . value_c
+ * over the keys visible to row r (the three-zone mask: paragraph on masking
+ * of the nodesdaily.com page, section "2. Single Forward Pass & Structured
+ * Attention Mask" of "TiDAR: Think in Diffusion, Talk in Autoregression",
+ * mauroscia.it):
+ *   - every row sees settled positions 0..lens[b]-1 (from the caches);
+ *   - candidate i sees step rows 0..i (strictly causal scoring);
+ *   - slot (g, s) sees step rows 0..g and the k rows of its own group g.
+ * The mask is evaluated arithmetically, never materialised.  Keys are split
+ * into chunks of `kv_chunk` positions of the [prefix ; step] sequence, each
+ * chunk reduced on its own and merged with a log-sum-exp rescale.
+ *
+ *   dtype      TIDAR_BF16 or TIDAR_F32, the element type of q, k_step,
+ *              v_step, k_cache, v_cache and out.
+ *   B, Hq, Hkv, D   batch, query heads, KV heads (Hq % Hkv == 0), head dim
+ *              (64 or 128).
+ *   S_max      cache capacity per (b, KV head); a multiple of 8.
+ *   max_len    host-side upper bound on every lens[b] (0 <= max_len <=
+ *              S_max); sizes the launch without a device sync.  A sequence
+ *              whose lens[b] exceeds it (or is negative) gets NaN outputs.
+ *   k          number of candidates, 1..16;  n_groups: 0 or k.
+ *   sm_scale   softmax scale (> 0), e.g. 1/sqrt(D).
+ *   kv_chunk   key positions per chunk; 0 lets the library choose.  Must be
+ *              a multiple of 64 otherwise (at most 1024 for TIDAR_F32).
+ *   q          [B][R][Hq][D]
+ *   k_step, v_step  [B][R][Hkv][D]   keys/values of the step rows (RoPE
+ *              already applied by the caller).
+ *   k_cache    [B][Hkv][S_max][D]    settled keys; rows >= lens[b] unused.
+ *   v_cache    [B][Hkv][D][S_max]    settled values, stored TRANSPOSED
+ *              (position fastest); columns >= lens[b] unused.
+ *   lens       [B] int32 settled length per sequence (device memory).
+ *   out        [B][R][Hq][D]         (written).
+ *   lse        [B][Hq][R] f32, natural-log softmax denominator of
+ *              sm_scale*q.k over visible keys (written); may be NULL.
+ *   workspace  device scratch of at least the size reported by
+ *              tidar_step_attention_workspace() for the same arguments.
+ * ---------------------------------------------------------------------- */
+int tidar_step_attention_workspace(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_len,
+                                   int k, int n_groups, int kv_chunk, size_t* bytes);
+
+int tidar_step_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_len,
+                         int k, int n_groups, float sm_scale, int kv_chunk,
+                         const void* q, const void* k_step, const void* v_step,
+                         const void* k_cache, const void* v_cache, const int32_t* lens,
+                         void* out, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* ------------------------------------------------------------------------
+ * Greedy verification and next-draft selection.
+ *
+ * Candidates are confirmed strictly left to right; whichever outcome is
+ * confirmed, the drafts prepared for it become the next candidates
+ * (nodesdaily.com page, paragraph on drafting for every outcome).
+ *   t_i          = argmax_v ar_logits[b][i][v], i = 0..k (lowest index wins
+ *                  ties; -0.0 ties +0.0; logits must be finite).
+ *   accept_len[b]= largest a <= k with cand[b][i] == t_i for every i < a.
+ *   next_cand[b][0] = t_a (the exact AR token after the accepted prefix).
+ *   g            = max(a, 1) - 1.
+ *   next_cand[b][m] = argmax_v draft_logits[b][g][m][v], m = 1..k-1.
+ *
+ *   ar_logits    [B][k+1][V] f32: row 0 is the AR distribution at
+ *                candidate 0's position (carried from the previous pass),
+ *                row i >= 1 the output of candidate row i-1.
+ *   draft_logits [B][k][k][V] f32: output of slot s of group g; only the
+ *                selected group's rows 1..k-1 are read.  May be NULL when
+ *                k == 1.
+ *   cand         [B][k] int32.
+ *   accept_len   [B] int32 (written);  next_cand [B][k] int32 (written).
+ *   workspace    at least tidar_verify_workspace() bytes.
+ * ---------------------------------------------------------------------- */
+int tidar_verify_workspace(int B, int k, int V, size_t* bytes);
+
+int tidar_verify_greedy(int B, int k, int V, const float* ar_logits, const float* draft_logits,
+                        const int32_t* cand, int32_t* accept_len, int32_t* next_cand,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * KV-cache commit / evict, in place.
+ *
+ * The settled cache is reused and rejected entries are evicted
+ * (nodesdaily.com page, paragraph on the three zones; "KV Cache" section of
+ * the mauroscia.it page).  For every sequence b with a = accept_len[b]:
+ *   k_cache[b][h][lens[b]+i][:]  = k_step[b][i][h][:]     i < a, every h
+ *   v_cache[b][h][:][lens[b]+i]  = v_step[b][i][h][:]
+ *   lens[b] += a
+ * Rejected candidates and every slot row are never written.  A sequence
+ * with lens[b] + a > S_max (flag 1) or a outside 0..k (flag 2) is left
+ * untouched.
+ *
+ *   dtype        element type of the caches and step rows.
+ *   R            rows per sequence of k_step / v_step ([B][R][Hkv][D]).
+ *   k            number of candidates (bound on accept_len), 1 <= k <= R.
+ *   lens         [B] int32, read and updated in place.
+ *   accept_len   [B] int32.
+ *   err_flags    [B] int32 (written: 0 ok, 1 overflow, 2 bad length); may
+ *                be NULL.
+ * ---------------------------------------------------------------------- */
+int tidar_kv_commit(int dtype, int B, int Hkv, int D, int S_max, int R, int k,
+                    void* k_cache, void* v_cache, int32_t* lens,
+                    const void* k_step, const void* v_step, const int32_t* accept_len,
+                    int32_t* err_flags, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TIDAR_H */

@@ -1,0 +1,113 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the header
+declares, and rejects invalid calls on the host before anything is enqueued
+(so these calls never touch a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def T():
+    import diffusion_drafted_self_amd as tidar
+    if not os.path.exists(tidar.LIB_PATH):
+        from diffusion_drafted_self_amd.build import build
+        build()
+    tidar.lib()
+    return tidar
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "tidar.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tidar_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(T):
+    names = _declared()
+    assert set(names) == set(T.SIGNATURES), names
+    raw = ctypes.CDLL(T.LIB_PATH)
+    for n in names:
+        assert getattr(raw, n) is not None
+
+
+def test_strerror_and_version(T):
+    assert T.lib().tidar_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, 7):
+        assert T.strerror(code)
+
+
+def _ws(T, *args):
+    n = ctypes.c_size_t(0)
+    st = T.lib().tidar_step_attention_workspace(*args, ctypes.byref(n))
+    return st, n.value
+
+
+def test_attention_workspace_validation(T):
+    ok = (0, 16, 32, 8, 128, 4160, 4096, 8, 8, 0)
+    assert _ws(T, *ok)[0] == 0
+    bad = {
+        "dtype": ((7,) + ok[1:], -2), "head dim": (ok[:4] + (96,) + ok[5:], -2),
+        "k too large": (ok[:7] + (17, 17, 0), -2), "k zero": (ok[:7] + (0, 0, 0), -1),
+        "n_groups": (ok[:8] + (3, 0), -1), "S_max % 8": (ok[:5] + (4161,) + ok[6:], -1),
+        "max_len > S_max": (ok[:6] + (4168,) + ok[7:], -1), "kv_chunk % 64": (ok[:9] + (100,), -1),
+        "f32 chunk": ((1,) + ok[1:9] + (2048,), -1), "Hq % Hkv": (ok[:2] + (30,) + ok[3:], -1),
+        "B < 0": ((0, -1) + ok[2:], -1),
+    }
+    for name, (args, want) in bad.items():
+        assert _ws(T, *args)[0] == want, name
+
+
+def test_attention_workspace_size(T):
+    # B*Hkv*n_split*M partial rows of D f32 plus (max, sum), each rounded to 256 B
+    B, Hq, Hkv, D, S, L, k, chunk = 3, 8, 2, 128, 1024, 1000, 4, 192
+    R, M = k + k * k, (k + k * k) * 4
+    n_split = -(-(L + R) // chunk)
+    rows = B * Hkv * n_split * M
+    want = -(-rows * D * 4 // 256) * 256 + -(-rows * 8 // 256) * 256
+    assert _ws(T, 0, B, Hq, Hkv, D, S, L, k, k, chunk) == (0, want)
+    assert _ws(T, 0, 0, Hq, Hkv, D, S, L, k, k, 0)[1] == 0
+
+
+def test_attention_call_rejects_before_launch(T):
+    f = T.lib().tidar_step_attention
+    p = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: every call below fails validation
+    args = [0, 2, 8, 2, 128, 256, 100, 4, 4, 0.1, 0] + [p] * 6 + [p, None, p, 1 << 20, None]
+    bad_ws = list(args); bad_ws[20] = 16
+    assert f(*bad_ws) == -3
+    bad_scale = list(args); bad_scale[9] = 0.0
+    assert f(*bad_scale) == -1
+    bad_ptr = list(args); bad_ptr[11] = ctypes.c_void_p(0x100004)
+    assert f(*bad_ptr) == -1
+    null_ptr = list(args); null_ptr[12] = None
+    assert f(*null_ptr) == -1
+    empty = [0, 0, 8, 2, 128, 256, 0, 4, 4, 0.1, 0] + [None] * 9 + [0, None]
+    assert f(*empty) == 0
+
+
+def test_verify_validation_and_size(T):
+    n = ctypes.c_size_t(0)
+    L = T.lib()
+    assert L.tidar_verify_workspace(16, 8, 128256, ctypes.byref(n)) == 0
+    chunks = -(-128256 // 4096)
+    want = sum(-(-x // 256) * 256 for x in (16 * 9 * chunks * 8, 16 * 7 * chunks * 8, 16 * 4))
+    assert n.value == want
+    assert L.tidar_verify_workspace(16, 17, 100, ctypes.byref(n)) == -2
+    assert L.tidar_verify_workspace(16, 0, 100, ctypes.byref(n)) == -1
+    assert L.tidar_verify_workspace(16, 4, 0, ctypes.byref(n)) == -1
+    p = ctypes.c_void_p(0x100000)
+    assert L.tidar_verify_greedy(2, 4, 100, p, p, p, p, p, p, 8, None) == -3
+    assert L.tidar_verify_greedy(2, 4, 100, p, None, p, p, p, p, 1 << 20, None) == -1
+
+
+def test_commit_validation(T):
+    L = T.lib()
+    p = ctypes.c_void_p(0x100000)
+    assert L.tidar_kv_commit(0, 2, 8, 96, 64, 72, 8, p, p, p, p, p, p, None, None) == -2
+    assert L.tidar_kv_commit(0, 2, 8, 128, 64, 4, 8, p, p, p, p, p, p, None, None) == -1
+    assert L.tidar_kv_commit(0, 2, 8, 128, 60, 72, 8, p, p, p, p, p, p, None, None) == -1
+    assert L.tidar_kv_commit(0, 2, 8, 128, 64, 72, 8, p, None, p, p, p, p, None, None) == -1
+    assert L.tidar_kv_commit(0, 0, 8, 128, 64, 72, 8, None, None, None, None, None, None, None, None) == 0
