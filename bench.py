@@ -1,0 +1,291 @@
+"""Benchmark of one TiDAR decode step on one MI355X.
+
+A step is the whole hot path over one batch: structured-mask step attention
+(one layer), greedy verification with next-draft selection, and the KV
+commit / evict.  The workload is the 8B-shaped step (batch 16, 32 query / 8
+KV heads of 128, settled prefix 4096, k = 8 candidates + 64 draft slots,
+verify over a 128256-entry vocabulary with planted accept lengths U{0..8}),
+bf16, synthetic seeded inputs already resident in HBM.
+
+Timing: W untimed warmup steps, then K steps between HIP events on the
+launch stream.  Inputs rotate over replicas totalling >= 2 GB so the 256 MB
+Infinity Cache cannot serve them warm.  After each step the settled lengths
+are restored (a 64-byte device copy) so every step is the same workload.
+The attention call is bracketed by its own events for the roofline figure.
+
+Prints ONE JSON line.  Options:
+  --gpus N          only N = 1 is supported (one GPU per process, no collectives)
+  --steps K --warmup W
+  --no-cpu-baseline skip the oracle timing (for profiler runs)
+  --calibrate-copy  run only a plain device copy of known size (for scaling
+                    the FETCH_SIZE / WRITE_SIZE counters)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV-cache GB/s and decode-step latency (µs) for TiDAR step attention, % of HBM peak"
+HBM_PEAK_GBPS = 8000.0
+COPY_CALIB_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_step_8b_traffic.txt")
+ATTN_SOURCES = [os.path.join(ROOT, "diffusion_drafted_self_amd", "csrc", n)
+                for n in ("attention.hip", "common.h", "launch.h")]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--cold-bytes", type=float, default=2.0e9)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--kv-chunk", type=int, default=0, help="key positions per attention chunk (0: library plan)")
+    p.add_argument("--workload", default="step_8b", choices=["step_8b", "step_1p5b", "step_8b_long"],
+                   help="synthetic workload (the reported line is the 8B-shaped step)")
+    return p.parse_args()
+
+
+def attention_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, or None when absent or taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, val = line.split("=", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("kernel_source_sha") != attention_source_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def step_bytes(shape, V, accept):
+    """Algorithmic bytes of one step (each byte moved once).
+    attention: settled K+V + step K+V + Q + O; verify: (k+1) AR rows and k-1
+    draft rows of f32 logits; commit: accepted K/V rows read and written."""
+    s = shape
+    esz = 2
+    kv_prefix = sum(s.lens) * s.Hkv * 2 * s.D * esz
+    kv_step = s.B * s.R * s.Hkv * 2 * s.D * esz
+    qo = 2 * s.B * s.R * s.Hq * s.D * esz
+    attn = kv_prefix + kv_step + qo
+    verify = s.B * (2 * s.k) * V * 4
+    commit = int(sum(accept)) * s.Hkv * s.D * esz * 2 * 2
+    flops = 4 * s.D * s.Hq * sum(s.R * L for L in s.lens)
+    return attn, verify, commit, kv_prefix + kv_step, flops
+
+
+def visible_step_pairs(k, n_groups):
+    """Visible (row, step key) pairs of the step block: candidates k(k+1)/2,
+    group g: k*(g+1) own-candidate + k*k own-group entries."""
+    return k * (k + 1) // 2 + sum(k * (g + 1) + k * k for g in range(n_groups))
+
+
+def calibrate_copy():
+    import torch
+    dev = torch.device("cuda:0")
+    n = COPY_CALIB_BYTES // 2
+    a = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_each_way": COPY_CALIB_BYTES, "launches": 5}))
+
+
+def cpu_baseline(wl, d, v, a_planted):
+    """The oracle (as it stands) on the same workload: three full steps."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits, threadpool_info
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    import oracle
+    import workloads as W
+
+    cores = len(os.sched_getaffinity(0))
+    s = wl.attn
+    f = {n: W.to_f32(x, "bf16") for n, x in d.items() if n != "lens"}
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
+    try:
+        if ctx:
+            ctx.__enter__()
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1) if threadpool_limits else cores
+        # warm-up on one sequence
+        oracle.attention_ref(f["q"], f["k_step"], f["v_step"], f["k_cache"], f["v_cache"], d["lens"], s.k,
+                             s.n_groups, s.sm_scale, pairs=[(0, h) for h in range(s.Hq)])
+        n_steps = 3
+        t0 = time.perf_counter()
+        for _ in range(n_steps):
+            oracle.attention_ref(f["q"], f["k_step"], f["v_step"], f["k_cache"], f["v_cache"], d["lens"], s.k,
+                                 s.n_groups, s.sm_scale)
+            acc, _ = oracle.verify_ref(v["ar_logits"], v["draft_logits"], v["cand"])
+            oracle.commit_ref(d["k_cache"], d["v_cache"], d["lens"], d["k_step"], d["v_step"], acc, s.k)
+        dt = (time.perf_counter() - t0) / n_steps
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    attn, ver, com, _, _ = step_bytes(s, wl.V, a_planted)
+    return {"value": round((attn + ver + com) / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "seconds_per_step": round(dt, 3),
+            "sample": f"{n_steps} full {wl.name} steps (attention over all {s.B}x{s.Hq} heads, verify, commit), "
+                      f"float64 NumPy, {threads} BLAS threads on {cores} host cores"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one GPU, with no "
+              "collectives (each GPU would run the same step on its own share of the batch).", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    import numpy as np
+    import torch
+
+    import diffusion_drafted_self_amd as tidar
+    import workloads as W
+
+    if not os.path.exists(tidar.LIB_PATH):
+        from __graft_entry__ import build
+        build()
+    dev = torch.device("cuda:0")
+    wl = W.WORKLOADS[args.workload]()
+    s = wl.attn
+
+    d = W.attention_inputs(s, seed=args.seed, config_id=wl.config_id, tail="zero")
+    v = W.verify_inputs(s.B, s.k, wl.V, seed=args.seed, config_id=wl.config_id, accept=wl.accept)
+    a_planted = v["planted"]
+
+    def to_dev(x, bf16):
+        x = np.ascontiguousarray(x)
+        if bf16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    base = {n: to_dev(x, n != "lens") for n, x in d.items()}
+    base.update({n: to_dev(v[n], False) for n in ("ar_logits", "draft_logits", "cand")})
+    per_rep = sum(t.numel() * t.element_size() for t in base.values())
+    n_rep = max(2, math.ceil(args.cold_bytes / per_rep))
+    ws_a = tidar.step_attention_workspace_bytes(0, s.B, s.Hq, s.Hkv, s.D, s.S_max, s.max_len, s.k, s.n_groups,
+                                                args.kv_chunk)
+    ws_v = tidar.verify_workspace_bytes(s.B, s.k, wl.V)
+    reps = []
+    for _ in range(n_rep):
+        r = {n: t.clone() for n, t in base.items()}
+        r["lens0"] = base["lens"].clone()
+        r["out"] = torch.empty_like(base["q"])
+        r["lse"] = torch.empty((s.B, s.Hq, s.R), dtype=torch.float32, device=dev)
+        r["ws_a"] = torch.zeros(max(ws_a, 256), dtype=torch.uint8, device=dev)
+        r["ws_v"] = torch.empty(ws_v, dtype=torch.uint8, device=dev)
+        r["acc"] = torch.empty(s.B, dtype=torch.int32, device=dev)
+        r["next"] = torch.empty((s.B, s.k), dtype=torch.int32, device=dev)
+        r["err"] = torch.empty(s.B, dtype=torch.int32, device=dev)
+        reps.append(r)
+    del base
+    torch.cuda.synchronize()
+
+    def attention(r):
+        tidar.step_attention(r["q"], r["k_step"], r["v_step"], r["k_cache"], r["v_cache"], r["lens"], s.k,
+                             s.n_groups, s.sm_scale, max_len=s.max_len, out=r["out"], lse=r["lse"],
+                             workspace=r["ws_a"], kv_chunk=args.kv_chunk)
+
+    def verify_commit(r):
+        tidar.verify_greedy(r["ar_logits"], r["draft_logits"], r["cand"], accept_len=r["acc"], next_cand=r["next"],
+                            workspace=r["ws_v"])
+        tidar.kv_commit(r["k_cache"], r["v_cache"], r["lens"], r["k_step"], r["v_step"], r["acc"], s.k, r["err"])
+        r["lens"].copy_(r["lens0"])
+
+    stream = torch.cuda.current_stream()
+    K, Wu = args.steps, args.warmup
+    ev_a = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(Wu):
+        r = reps[i % n_rep]
+        attention(r)
+        verify_commit(r)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        r = reps[(Wu + i) % n_rep]
+        ev_a[i][0].record(stream)
+        attention(r)
+        ev_a[i][1].record(stream)
+        verify_commit(r)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    step_ms = t_start.elapsed_time(t_end) / K
+    attn_ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev_a)
+    attn_ms_mean = sum(attn_ms) / K
+
+    # the accepted lengths the GPU produced must be the planted ones (exact by construction)
+    acc = reps[0]["acc"].cpu().numpy()
+    if a_planted is not None:
+        assert acc.tolist() == a_planted.tolist(), "verify result differs from the planted accept lengths"
+    else:
+        a_planted = acc
+    assert int(reps[0]["err"].abs().sum()) == 0
+
+    attn_b, ver_b, com_b, kv_b, flops = step_bytes(s, wl.V, a_planted)
+    flops_step = 4 * s.D * s.Hq * s.B * visible_step_pairs(s.k, s.n_groups)
+    step_gbps = (attn_b + ver_b + com_b) / (step_ms * 1e-3) / 1e9
+    attn_gbps = attn_b / (attn_ms_mean * 1e-3) / 1e9
+    traffic = read_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(step_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wu,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "kv_chunk": args.kv_chunk or "auto", "batch": s.B, "q_heads": s.Hq, "kv_heads": s.Hkv, "head_dim": s.D,
+                   "prefix": s.lens[0], "k": s.k, "draft_groups": s.n_groups, "step_rows": s.R, "vocab": wl.V,
+                   "accept": wl.accept, "cold_replicas": n_rep},
+        "step_us": round(step_ms * 1e3, 2),
+        "attention_us": round(attn_ms_mean * 1e3, 2),
+        "attention_us_p50": round(attn_ms[K // 2] * 1e3, 2),
+        "attention_kv_gbps": round(kv_b / (attn_ms_mean * 1e-3) / 1e9, 2),
+        "attention_hbm_frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
+        "attention_tflops": round((flops + flops_step) / (attn_ms_mean * 1e-3) / 1e12, 2),
+        "verify_commit_us": round((step_ms - attn_ms_mean) * 1e3, 2),
+        "roofline": {"bound": "hbm", "kernel": "tidar_step_attention", "achieved": round(attn_gbps, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes": attn_b},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, d, v, a_planted)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -11,7 +11,8 @@ been built (``python -m diffusion_drafted_self_amd.build``).
 
 Tensor layouts (row-major, contiguous):
   q [B][R][Hq][D], k_step/v_step [B][R][Hkv][D],
-  k_cache [B][Hkv][S_max][D], v_cache [B][Hkv][D][S_max] (values transposed),
+  k_cache [B][Hkv][S_max][D], v_cache [B][Hkv][S_max/64][D][64] (values in
+  pages of 64 positions, each page transposed),
   lens [B] int32, ar_logits [B][k+1][V] f32, draft_logits [B][k][k][V] f32,
   cand [B][k] int32.
 """
@@ -120,6 +121,18 @@ def _workspace(nbytes: int, device, given):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+VALUE_PAGE = 64
+
+
+def _check_caches(k_cache, v_cache, B, Hkv, S_max, D):
+    if S_max % VALUE_PAGE:
+        raise ValueError(f"cache capacity {S_max} must be a multiple of {VALUE_PAGE}")
+    if tuple(k_cache.shape) != (B, Hkv, S_max, D):
+        raise ValueError("k_cache must be [B][Hkv][S_max][D]")
+    if tuple(v_cache.shape) != (B, Hkv, S_max // VALUE_PAGE, D, VALUE_PAGE):
+        raise ValueError("v_cache must be [B][Hkv][S_max/64][D][64]")
+
+
 # ------------------------------------------------------------------------ attention
 def step_attention_workspace_bytes(dtype_code: int, B: int, Hq: int, Hkv: int, D: int, S_max: int,
                                    max_len: int, k: int, n_groups: int, kv_chunk: int = 0) -> int:
@@ -144,7 +157,7 @@ def step_attention(q, k_step, v_step, k_cache, v_cache, lens, k: int, n_groups: 
     _need(k_step, "k_step", dt, 4, dev)
     _need(v_step, "v_step", dt, 4, dev)
     _need(k_cache, "k_cache", dt, 4, dev)
-    _need(v_cache, "v_cache", dt, 4, dev)
+    _need(v_cache, "v_cache", dt, 5, dev)
     _need(lens, "lens", torch.int32, 1, dev)
     Hkv = k_step.shape[2]
     S_max = k_cache.shape[2]
@@ -152,8 +165,7 @@ def step_attention(q, k_step, v_step, k_cache, v_cache, lens, k: int, n_groups: 
         raise ValueError(f"q has {R} step rows, expected k + n_groups*k = {k + n_groups * k}")
     if tuple(k_step.shape) != (B, R, Hkv, D) or tuple(v_step.shape) != (B, R, Hkv, D):
         raise ValueError("k_step/v_step must be [B][R][Hkv][D]")
-    if tuple(k_cache.shape) != (B, Hkv, S_max, D) or tuple(v_cache.shape) != (B, Hkv, D, S_max):
-        raise ValueError("k_cache must be [B][Hkv][S_max][D] and v_cache [B][Hkv][D][S_max]")
+    _check_caches(k_cache, v_cache, B, Hkv, S_max, D)
     if lens.shape[0] != B:
         raise ValueError("lens must be [B]")
     if max_len is None:
@@ -223,14 +235,13 @@ def kv_commit(k_cache, v_cache, lens, k_step, v_step, accept_len, k: int, err_fl
     _need(k_cache, "k_cache", ndim=4)
     dev, dt = k_cache.device, k_cache.dtype
     B, Hkv, S_max, D = k_cache.shape
-    _need(v_cache, "v_cache", dt, 4, dev)
+    _need(v_cache, "v_cache", dt, 5, dev)
     _need(k_step, "k_step", dt, 4, dev)
     _need(v_step, "v_step", dt, 4, dev)
     _need(lens, "lens", torch.int32, 1, dev)
     _need(accept_len, "accept_len", torch.int32, 1, dev)
     R = k_step.shape[1]
-    if tuple(v_cache.shape) != (B, Hkv, D, S_max):
-        raise ValueError("v_cache must be [B][Hkv][D][S_max]")
+    _check_caches(k_cache, v_cache, B, Hkv, S_max, D)
     if tuple(k_step.shape) != (B, R, Hkv, D) or tuple(v_step.shape) != (B, R, Hkv, D):
         raise ValueError("k_step/v_step must be [B][R][Hkv][D]")
     if err_flags is not None:

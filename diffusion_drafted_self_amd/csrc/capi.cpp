@@ -15,9 +15,11 @@ namespace {
 
 constexpr int kMaxK = 16;
 constexpr int kTileKeys = 64;           // keys per attention tile
+constexpr int kValuePage = 64;          // positions per value-cache page
 constexpr int kMaxChunkF32 = 1024;      // LDS score buffer of the f32 kernel
 constexpr int kVerifyChunk = 4096;      // logits per argmax workgroup
-constexpr long kTargetWorkgroups = 1024; // about four per CU on 256 CUs
+constexpr long kTargetWorkgroups = 512;      // two per CU on 256 CUs
+constexpr long kSingleChunkWorkgroups = 192; // three quarters of the CUs busy without splitting keys
 
 bool aligned(const void* p, uintptr_t a) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -25,7 +27,7 @@ long cdiv(long a, long b) { return (a + b - 1) / b; }
 
 struct AttnPlan {
   int R, G, M, waves, n_rowblk, chunk, n_split;
-  size_t o_bytes, ml_bytes, total;
+  size_t cnt_bytes, o_bytes, ml_bytes, total;
 };
 
 // Split plan of the step attention.  Rows of one (b, kvh): M = R*G in
@@ -40,7 +42,7 @@ int plan_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_
   if (k > kMaxK) return TIDAR_EUNSUPPORTED;
   if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || k < 1) return TIDAR_EINVAL;
   if (n_groups != 0 && n_groups != k) return TIDAR_EINVAL;
-  if (S_max < 1 || S_max % 8 != 0 || max_len < 0 || max_len > S_max) return TIDAR_EINVAL;
+  if (S_max < 1 || S_max % kValuePage != 0 || max_len < 0 || max_len > S_max) return TIDAR_EINVAL;
   if (kv_chunk < 0 || kv_chunk % kTileKeys != 0) return TIDAR_EINVAL;
   if (dtype == TIDAR_F32 && kv_chunk > kMaxChunkF32) return TIDAR_EINVAL;
 
@@ -49,22 +51,29 @@ int plan_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_
   p->M = p->R * p->G;
   const long keys = (long)max_len + p->R;
 
+  // waves per workgroup: the largest of 4, 3, 2, 1 whose padding wastes at
+  // most 1/16 of the MFMA tiles (else the least padding)
   const int n_tiles = (int)cdiv(p->M, 32);
-  int best_w = 4, best_pad = 1 << 30;
+  int best_w = 1, best_pad = 1 << 30;
   for (int w = 4; w >= 1; --w) {
     const int pad = (int)cdiv(n_tiles, w) * w - n_tiles;
+    if (pad * 16 <= n_tiles) { best_w = w; best_pad = pad; break; }
     if (pad < best_pad) { best_pad = pad; best_w = w; }
   }
   p->waves = best_w;
   p->n_rowblk = (int)cdiv(n_tiles, best_w);
 
+  // key chunks: one chunk per (b, kvh, row block) whenever that already
+  // gives most CUs a workgroup -- every extra chunk costs a partial output
+  // of M*(D+2)*4 bytes written and read back -- else enough chunks to reach
+  // about kTargetWorkgroups workgroups, each at least 256 keys
   long chunk = kv_chunk;
   if (chunk == 0) {
     if (dtype == TIDAR_F32) {
       chunk = std::min<long>(kMaxChunkF32, (long)round_up(keys, kTileKeys));
     } else {
       const long base = std::max<long>(1, (long)B * Hkv * p->n_rowblk);
-      long n_split = cdiv(kTargetWorkgroups, base);
+      long n_split = base >= kSingleChunkWorkgroups ? 1 : cdiv(kTargetWorkgroups, base);
       n_split = std::max<long>(1, std::min<long>(n_split, cdiv(keys, 256)));
       chunk = (long)round_up(cdiv(keys, n_split), kTileKeys);
     }
@@ -75,10 +84,13 @@ int plan_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_
   const long blocks = (long)B * Hkv * p->n_split * (dtype == TIDAR_F32 ? p->M : p->n_rowblk);
   if (blocks > 0x7fffffffL) return TIDAR_EUNSUPPORTED;
 
-  const size_t parts = (size_t)B * Hkv * p->n_split * p->M;
+  // workspace: [partial outputs][partial (max, sum)]; none is needed when
+  // every sequence fits one chunk (bf16 path)
+  const size_t parts = (dtype == TIDAR_F32 || p->n_split > 1) ? (size_t)B * Hkv * p->n_split * p->M : 0;
+  p->cnt_bytes = 0;
   p->o_bytes = round_up(parts * D * sizeof(float), 256);
   p->ml_bytes = round_up(parts * sizeof(float2), 256);
-  p->total = p->o_bytes + p->ml_bytes;
+  p->total = p->cnt_bytes + p->o_bytes + p->ml_bytes;
   return TIDAR_OK;
 }
 
@@ -141,7 +153,7 @@ int tidar_step_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, in
       !aligned(v_cache, 16) || !aligned(out, 16) || !aligned(lens, 4))
     return TIDAR_EINVAL;
   if (lse && !aligned(lse, 4)) return TIDAR_EINVAL;
-  if (!aligned(workspace, 256) || workspace_bytes < p.total) return TIDAR_EWORKSPACE;
+  if (p.total > 0 && (!aligned(workspace, 256) || workspace_bytes < p.total)) return TIDAR_EWORKSPACE;
 
   tidar::AttnArgs a;
   a.q = q;
@@ -152,8 +164,9 @@ int tidar_step_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, in
   a.lens = lens;
   a.out = out;
   a.lse = lse;
-  a.o_part = static_cast<float*>(workspace);
-  a.ml_part = reinterpret_cast<float2*>(static_cast<char*>(workspace) + p.o_bytes);
+  char* ws = static_cast<char*>(workspace);
+  a.o_part = reinterpret_cast<float*>(ws + p.cnt_bytes);
+  a.ml_part = reinterpret_cast<float2*>(ws + p.cnt_bytes + p.o_bytes);
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
@@ -169,6 +182,7 @@ int tidar_step_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, in
   a.waves = p.waves;
   a.n_rowblk = p.n_rowblk;
   a.scale_log2 = sm_scale * 1.44269504088896340736f;
+  a.single_chunk_direct = dtype == TIDAR_BF16;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = dtype == TIDAR_BF16 ? tidar::launch_attention_bf16(a, s) : tidar::launch_attention_f32(a, s);
@@ -221,7 +235,7 @@ int tidar_kv_commit(int dtype, int B, int Hkv, int D, int S_max, int R, int k,
                     int32_t* err_flags, void* stream) {
   if (dtype != TIDAR_BF16 && dtype != TIDAR_F32) return TIDAR_EUNSUPPORTED;
   if (D != 64 && D != 128) return TIDAR_EUNSUPPORTED;
-  if (B < 0 || Hkv < 1 || S_max < 1 || S_max % 8 != 0 || R < 1 || k < 1 || k > R) return TIDAR_EINVAL;
+  if (B < 0 || Hkv < 1 || S_max < 1 || S_max % kValuePage != 0 || R < 1 || k < 1 || k > R) return TIDAR_EINVAL;
   if (B == 0) return TIDAR_OK;
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_step, 16) || !aligned(v_step, 16) ||
       !aligned(lens, 4) || !aligned(accept_len, 4))

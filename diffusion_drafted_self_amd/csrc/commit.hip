@@ -6,7 +6,7 @@
 // section of "TiDAR: Think in Diffusion, Talk in Autoregression",
 // mauroscia.it).  One workgroup per sequence appends the a accepted
 // candidate rows (step rows 0..a-1) at positions lens..lens+a-1 -- keys as
-// 16 B row copies, values transposed into the [D][S_max] value cache -- then
+// 16 B row copies, values transposed into their 64-position value page -- then
 // advances lens in place.  Rejected candidates and slot rows are evicted by
 // never being written.  The work is a few KB per sequence: latency-bound.
 #include "common.h"
@@ -45,7 +45,8 @@ __global__ __launch_bounds__(256) void kv_commit_kernel(CommitArgs a) {
     const int rem = id % (a.D * acc);
     const int d = rem / acc, i = rem % acc;
     const size_t src = (((size_t)b * a.R + i) * a.Hkv + h) * a.D + d;
-    const size_t dst = (((size_t)b * a.Hkv + h) * a.D + d) * a.S_max + L + i;
+    const int pos = L + i;
+    const size_t dst = ((size_t)b * a.Hkv + h) * a.S_max * a.D + (size_t)(pos / 64) * a.D * 64 + d * 64 + pos % 64;
     if (esz == 2) ((uint16_t*)a.v_cache)[dst] = ((const uint16_t*)a.v_step)[src];
     else ((uint32_t*)a.v_cache)[dst] = ((const uint32_t*)a.v_step)[src];
   }

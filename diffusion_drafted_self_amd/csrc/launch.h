@@ -26,6 +26,7 @@ struct AttnArgs {
   int chunk, n_split;
   int waves, n_rowblk;  // bf16 path: waves per workgroup, row blocks per (b, kvh)
   float scale_log2;     // sm_scale * log2(e)
+  int single_chunk_direct;  // the split kernel writes sequences that fit one chunk (bf16 path)
 };
 
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t s);

@@ -41,6 +41,13 @@
 extern "C" {
 #endif
 
+/* Positions per value-cache page: the value cache of every (sequence, KV
+ * head) is S_max/TIDAR_VALUE_PAGE pages of [D][TIDAR_VALUE_PAGE], i.e. each
+ * page of 64 consecutive positions is stored transposed (position fastest).
+ * Key tiles of 64 positions and value pages are then both contiguous 16 KB
+ * blocks for D = 128. */
+#define TIDAR_VALUE_PAGE 64
+
 enum {
   TIDAR_OK = 0,
   TIDAR_EINVAL = -1,       /* bad shape, pointer, alignment or value */
@@ -77,7 +84,7 @@ int tidar_abi_version(void);
  *              v_step, k_cache, v_cache and out.
  *   B, Hq, Hkv, D   batch, query heads, KV heads (Hq % Hkv == 0), head dim
  *              (64 or 128).
- *   S_max      cache capacity per (b, KV head); a multiple of 8.
+ *   S_max      cache capacity per (b, KV head); a multiple of 64.
  *   max_len    host-side upper bound on every lens[b] (0 <= max_len <=
  *              S_max); sizes the launch without a device sync.  A sequence
  *              whose lens[b] exceeds it (or is negative) gets NaN outputs.
@@ -89,14 +96,18 @@ int tidar_abi_version(void);
  *   k_step, v_step  [B][R][Hkv][D]   keys/values of the step rows (RoPE
  *              already applied by the caller).
  *   k_cache    [B][Hkv][S_max][D]    settled keys; rows >= lens[b] unused.
- *   v_cache    [B][Hkv][D][S_max]    settled values, stored TRANSPOSED
- *              (position fastest); columns >= lens[b] unused.
+ *   v_cache    [B][Hkv][S_max/64][D][64]  settled values in pages of 64
+ *              positions, each page stored TRANSPOSED: the value of
+ *              position p, element d, is at [b][h][p/64][d][p%64].
+ *              Positions >= lens[b] unused.
  *   lens       [B] int32 settled length per sequence (device memory).
  *   out        [B][R][Hq][D]         (written).
  *   lse        [B][Hq][R] f32, natural-log softmax denominator of
  *              sm_scale*q.k over visible keys (written); may be NULL.
- *   workspace  device scratch of at least the size reported by
- *              tidar_step_attention_workspace() for the same arguments.
+ *   workspace  device scratch (256-byte aligned) of at least the size
+ *              reported by tidar_step_attention_workspace() for the same
+ *              arguments; may be NULL when that size is 0 (every sequence
+ *              fits one key chunk, bf16).
  * ---------------------------------------------------------------------- */
 int tidar_step_attention_workspace(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_len,
                                    int k, int n_groups, int kv_chunk, size_t* bytes);
@@ -144,13 +155,15 @@ int tidar_verify_greedy(int B, int k, int V, const float* ar_logits, const float
  * (nodesdaily.com page, paragraph on the three zones; "KV Cache" section of
  * the mauroscia.it page).  For every sequence b with a = accept_len[b]:
  *   k_cache[b][h][lens[b]+i][:]  = k_step[b][i][h][:]     i < a, every h
- *   v_cache[b][h][:][lens[b]+i]  = v_step[b][i][h][:]
+ *   v_cache[b][h][p/64][:][p%64] = v_step[b][i][h][:]       p = lens[b]+i
  *   lens[b] += a
  * Rejected candidates and every slot row are never written.  A sequence
  * with lens[b] + a > S_max (flag 1) or a outside 0..k (flag 2) is left
  * untouched.
  *
  *   dtype        element type of the caches and step rows.
+ *   S_max        cache capacity, a multiple of 64; caches laid out as for
+ *                tidar_step_attention.
  *   R            rows per sequence of k_step / v_step ([B][R][Hkv][D]).
  *   k            number of candidates (bound on accept_len), 1 <= k <= R.
  *   lens         [B] int32, read and updated in place.

@@ -21,7 +21,8 @@ import numpy as np
 
 
 def commit_ref(k_cache, v_cache, lens, k_step, v_step, accept_len, k):
-    """k_cache [B][Hkv][S][D], v_cache [B][Hkv][D][S] (values transposed),
+    """k_cache [B][Hkv][S][D], v_cache [B][Hkv][S/64][D][64] (pages of 64
+    positions, each stored transposed),
     k_step/v_step [B][R][Hkv][D], lens/accept_len [B].  Works on any element
     type (it is a copy).  Returns new (k_cache, v_cache, lens, err_flags)."""
     kc = np.array(k_cache, copy=True)
@@ -39,7 +40,8 @@ def commit_ref(k_cache, v_cache, lens, k_step, v_step, accept_len, k):
             err[b] = 1
             continue
         for i in range(a):
-            kc[b, :, L + i, :] = k_step[b, i, :, :]
-            vc[b, :, :, L + i] = v_step[b, i, :, :]
+            pos = L + i
+            kc[b, :, pos, :] = k_step[b, i, :, :]
+            vc[b, :, pos // 64, :, pos % 64] = v_step[b, i, :, :]
         ln[b] = L + a
     return kc, vc, ln, err

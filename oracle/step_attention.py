@@ -64,11 +64,13 @@ def step_mask_ref(k: int, n_groups: int, L: int) -> np.ndarray:
 
 def _gather_kv(k_step, v_step, k_cache, v_cache, b, kv, L):
     """Concatenated [prefix ; step] keys and values (float64), (L+R) x D.
-    v_cache is stored transposed, [B][Hkv][D][S_max]."""
+    v_cache holds pages of 64 positions, each stored transposed:
+    value of position p = v_cache[b, kv, p // 64, :, p % 64]."""
     K = np.concatenate([np.asarray(k_cache[b, kv, :L, :], dtype=np.float64),
                         np.asarray(k_step[b, :, kv, :], dtype=np.float64)], axis=0)
-    V = np.concatenate([np.asarray(v_cache[b, kv, :, :L], dtype=np.float64).T,
-                        np.asarray(v_step[b, :, kv, :], dtype=np.float64)], axis=0)
+    pages = np.asarray(v_cache[b, kv], dtype=np.float64)          # [S/64][D][64]
+    prefix_v = pages.transpose(0, 2, 1).reshape(-1, pages.shape[1])[:L]
+    V = np.concatenate([prefix_v, np.asarray(v_step[b, :, kv, :], dtype=np.float64)], axis=0)
     return K, V
 
 
@@ -82,7 +84,7 @@ def attention_ref(q, k_step, v_step, k_cache, v_cache, lens, k, n_groups, sm_sca
     """Dense masked softmax attention of the step block, float64.
 
     q [B][R][Hq][D]; k_step/v_step [B][R][Hkv][D]; k_cache [B][Hkv][S][D];
-    v_cache [B][Hkv][D][S]; lens [B].  Query head h reads KV head h // (Hq/Hkv).
+    v_cache [B][Hkv][S/64][D][64] (pages of 64 positions, transposed); lens [B].  Query head h reads KV head h // (Hq/Hkv).
     Returns out [B][R][Hq][D] and lse [B][Hq][R] (natural log of the softmax
     denominator of sm_scale*q.k over visible keys).  With ``pairs`` (a list of
     (b, h)), only those heads are computed; other entries are NaN."""

@@ -93,7 +93,7 @@ class TinyDecoder:
     # -- one TiDAR step against the cache
     def forward_step(self, tokens, positions, caches, lens, k, n_groups):
         """tokens/positions of the R step rows; caches[l] = (k_cache, v_cache)
-        of shape [1][H][S][hd] / [1][H][hd][S].  Returns logits [R][V] and the
+        of shape [1][H][S][hd] / [1][H][S/64][hd][64].  Returns logits [R][V] and the
         per-layer step keys/values [1][R][H][hd]."""
         R = len(tokens)
         h = self.w["emb"][np.asarray(tokens)]
@@ -148,10 +148,11 @@ def tidar_greedy(model: TinyDecoder, prompt, n_new, k, draft_fn=None):
     _, kv = model.forward_full(prompt[:-1])
     for l in range(cfg.n_layers):
         kc = np.zeros((1, H, S, hd))
-        vc = np.zeros((1, H, hd, S))
         kk, vv = kv[l]
         kc[0, :, :P - 1, :] = kk.transpose(1, 0, 2)
-        vc[0, :, :, :P - 1] = vv.transpose(1, 2, 0)
+        vn = np.zeros((H, S, hd))
+        vn[:, :P - 1, :] = vv.transpose(1, 0, 2)
+        vc = vn.reshape(1, H, S // 64, 64, hd).transpose(0, 1, 2, 4, 3).copy()  # pages of 64, transposed
         caches.append((kc, vc))
     lens = np.array([P - 1], dtype=np.int32)
 

@@ -51,6 +51,7 @@ def test_attention_workspace_validation(T):
     assert _ws(T, *ok)[0] == 0
     bad = {
         "dtype": ((7,) + ok[1:], -2), "head dim": (ok[:4] + (96,) + ok[5:], -2),
+        "S_max % 64": (ok[:5] + (4104,) + ok[6:], -1),
         "k too large": (ok[:7] + (17, 17, 0), -2), "k zero": (ok[:7] + (0, 0, 0), -1),
         "n_groups": (ok[:8] + (3, 0), -1), "S_max % 8": (ok[:5] + (4161,) + ok[6:], -1),
         "max_len > S_max": (ok[:6] + (4168,) + ok[7:], -1), "kv_chunk % 64": (ok[:9] + (100,), -1),
@@ -75,7 +76,10 @@ def test_attention_workspace_size(T):
 def test_attention_call_rejects_before_launch(T):
     f = T.lib().tidar_step_attention
     p = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: every call below fails validation
-    args = [0, 2, 8, 2, 128, 256, 100, 4, 4, 0.1, 0] + [p] * 6 + [p, None, p, 1 << 20, None]
+    # this shape splits its keys, so it needs a workspace: 16 bytes is rejected before any launch
+    st, need = _ws(T, 0, 2, 8, 2, 128, 4096, 4000, 4, 4, 0)
+    assert st == 0 and need > 16
+    args = [0, 2, 8, 2, 128, 4096, 4000, 4, 4, 0.1, 0] + [p] * 6 + [p, None, p, 1 << 30, None]
     bad_ws = list(args); bad_ws[20] = 16
     assert f(*bad_ws) == -3
     bad_scale = list(args); bad_scale[9] = 0.0

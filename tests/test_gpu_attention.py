@@ -21,7 +21,7 @@ from _gpu_util import DEV, attn_f32, attn_to_dev, bits, check_attention  # noqa:
 
 
 def _shape(B, Hq, Hkv, D, k, n_groups, lens, dtype="bf16", S_max=None, scale=None, k_prescale=1.0):
-    S_max = S_max or ((max(lens) + 64 + 7) // 8 * 8)
+    S_max = S_max or ((max(lens) + 64 + 63) // 64 * 64)
     return W.AttnShape(B=B, Hq=Hq, Hkv=Hkv, D=D, k=k, n_groups=n_groups, lens=tuple(lens), S_max=S_max,
                        dtype=dtype, sm_scale=scale or 1.0 / math.sqrt(D), k_prescale=k_prescale)
 

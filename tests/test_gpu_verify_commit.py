@@ -71,9 +71,9 @@ def test_verify_ties_everywhere():
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_commit_matches_oracle_over_steps(dtype):
     rng = np.random.default_rng(1)
-    B, Hkv, D, S, k = 5, 4, 128, 96, 8
+    B, Hkv, D, S, k = 5, 4, 128, 128, 8
     R = k + k * k
-    shape = W.AttnShape(B=B, Hq=Hkv, Hkv=Hkv, D=D, k=k, n_groups=k, lens=(0, 7, 50, 80, 90), S_max=S, dtype=dtype)
+    shape = W.AttnShape(B=B, Hq=Hkv, Hkv=Hkv, D=D, k=k, n_groups=k, lens=(0, 7, 60, 110, 124), S_max=S, dtype=dtype)
     d = W.kv_cache(shape, seed=2, tail="random")
     kc, vc, ln = d["k_cache"], d["v_cache"], d["lens"]
     t_kc, t_vc, t_ln = to_dev(kc, dtype == "bf16"), to_dev(vc, dtype == "bf16"), to_dev(ln)
@@ -94,14 +94,15 @@ def test_commit_matches_oracle_over_steps(dtype):
 
 
 def test_commit_overflow_flag():
-    B, Hkv, D, S, k = 2, 1, 64, 16, 4
+    B, Hkv, D, S, k = 2, 1, 64, 64, 4
     kc = torch.zeros((B, Hkv, S, D), dtype=torch.bfloat16, device=DEV)
-    vc = torch.zeros((B, Hkv, D, S), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros((B, Hkv, S // 64, D, 64), dtype=torch.bfloat16, device=DEV)
     ks = torch.ones((B, k + k * k, Hkv, D), dtype=torch.bfloat16, device=DEV)
-    lens = torch.tensor([14, 12], dtype=torch.int32, device=DEV)
+    lens = torch.tensor([62, 60], dtype=torch.int32, device=DEV)
     a = torch.tensor([3, 4], dtype=torch.int32, device=DEV)
     ef = torch.empty(B, dtype=torch.int32, device=DEV)
     tidar.kv_commit(kc, vc, lens, ks, ks, a, k, ef)
     assert ef.cpu().tolist() == [1, 0]
-    assert lens.cpu().tolist() == [14, 16]
-    assert float(kc[0].float().abs().sum()) == 0.0 and float(kc[1, 0, 12:16].float().sum()) == 4 * D
+    assert lens.cpu().tolist() == [62, 64]
+    assert float(kc[0].float().abs().sum()) == 0.0 and float(kc[1, 0, 60:64].float().sum()) == 4 * D
+    assert float(vc[1, 0, 0, :, 60:64].float().sum()) == 4 * D and float(vc[1].float().sum()) == 4 * D

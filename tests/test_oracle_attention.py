@@ -26,7 +26,7 @@ import workloads as W
 
 
 def _inputs(B, Hq, Hkv, D, k, n_groups, lens, seed=0, S_max=None, scale=None):
-    S_max = S_max or (max(lens) + 8)
+    S_max = S_max or ((max(lens) + 8 + 63) // 64 * 64)
     shape = W.AttnShape(B=B, Hq=Hq, Hkv=Hkv, D=D, k=k, n_groups=n_groups, lens=tuple(lens),
                         S_max=S_max, dtype="f32", sm_scale=scale or 1.0 / math.sqrt(D))
     d = W.attention_inputs(shape, seed=seed, tail="nan")
@@ -74,8 +74,10 @@ def test_worked_examples(golden_dir):
         q = np.array(case["q"]).reshape(1, 2, 1, D)
         ks = np.array(case["k_step"]).reshape(1, 2, 1, D)
         vs = np.array(case["v_step"]).reshape(1, 2, 1, D)
-        kc = np.array(case["k_prefix"]).reshape(1, 1, 1, D)
-        vc = np.array(case["v_prefix"]).T.reshape(1, 1, D, 1)
+        kc = np.zeros((1, 1, 64, D))
+        kc[0, 0, 0] = case["k_prefix"][0]
+        vc = np.zeros((1, 1, 1, D, 64))  # one value page, stored transposed
+        vc[0, 0, 0, :, 0] = case["v_prefix"][0]
         out, lse = oracle.attention_ref(q, ks, vs, kc, vc, [1], 1, 1, case["sm_scale"])
         np.testing.assert_allclose(out[0, :, 0, :], np.array(case["out"]), rtol=0, atol=1e-14)
         np.testing.assert_allclose(lse[0, 0], np.array(case["lse"]), rtol=0, atol=1e-14)
@@ -101,7 +103,7 @@ def test_zero_drafts_is_causal_attention(B, Hq, Hkv, D, k, lens):
     for b in range(B):
         L = lens[b]
         keys = np.concatenate([d["k_cache"][b, :, :L, :].transpose(1, 0, 2), d["k_step"][b]], axis=0)
-        vals = np.concatenate([d["v_cache"][b, :, :, :L].transpose(2, 0, 1), d["v_step"][b]], axis=0)
+        vals = np.concatenate([W.v_natural(d["v_cache"][b])[:, :L, :].transpose(1, 0, 2), d["v_step"][b]], axis=0)
         qfull = np.concatenate([rng.standard_normal((L, Hq, D)), d["q"][b]], axis=0)
         ref = _sdpa(qfull, keys, vals, shape.sm_scale, causal=True, gqa=True)[L:]
         np.testing.assert_allclose(out[b], ref, rtol=1e-12, atol=1e-12)
@@ -113,7 +115,7 @@ def test_full_step_candidates_and_slots(Hq, Hkv, k, L):
     shape, d = _inputs(1, Hq, Hkv, D, k, k, (L,))
     out, _ = _run(shape, d)
     keys_pre = d["k_cache"][0, :, :L, :].transpose(1, 0, 2)
-    vals_pre = d["v_cache"][0, :, :, :L].transpose(2, 0, 1)
+    vals_pre = W.v_natural(d["v_cache"][0])[:, :L, :].transpose(1, 0, 2)
     ks, vs, q = d["k_step"][0], d["v_step"][0], d["q"][0]
     # candidate rows == causal rows of a brute-force pass over [prefix ; candidates]
     rng = np.random.default_rng(3)

@@ -63,23 +63,11 @@ def test_boost_mode_gives_varied_lengths():
     assert len(set(a.tolist())) >= 2
 
 
-def _brute_cache(k_cache, v_cache, lens, k_step, v_step, accepted):
-    """Concatenate settled rows and every accepted row, per (b, h)."""
-    B, H, S, D = k_cache.shape
-    Ks, Vs = [], []
-    for b in range(B):
-        Ks.append([np.concatenate([k_cache[b, h, :lens[b]]] + [k_step[b, :a, h] for a in accepted[b]])
-                   for h in range(H)])
-        Vs.append([np.concatenate([v_cache[b, h, :, :lens[b]].T] + [v_step[b, :a, h] for a in accepted[b]])
-                   for h in range(H)])
-    return Ks, Vs
-
-
 def test_commit_equals_concatenation_over_steps():
     rng = np.random.default_rng(5)
-    B, H, S, D, k, R = 3, 2, 40, 8, 4, 20
+    B, H, S, D, k, R = 3, 2, 64, 8, 4, 20
     kc = rng.standard_normal((B, H, S, D))
-    vc = rng.standard_normal((B, H, D, S))
+    vc = rng.standard_normal((B, H, S // 64, D, 64))
     lens0 = np.array([0, 5, 17], dtype=np.int32)
     lens = lens0.copy()
     k_start, v_start = kc.copy(), vc.copy()
@@ -97,23 +85,25 @@ def test_commit_equals_concatenation_over_steps():
     for b in range(B):
         for h in range(H):
             want_k = np.concatenate([k_start[b, h, :lens0[b]]] + [ks[b, :a[b], h] for ks, _, a in step_rows])
-            want_v = np.concatenate([v_start[b, h, :, :lens0[b]].T] + [vs[b, :a[b], h] for _, vs, a in step_rows])
+            v0, v1 = W.v_natural(v_start[b, h]), W.v_natural(vc[b, h])
+            want_v = np.concatenate([v0[:lens0[b]]] + [vs[b, :a[b], h] for _, vs, a in step_rows])
             assert np.array_equal(kc[b, h, :lens[b]], want_k)
-            assert np.array_equal(vc[b, h, :, :lens[b]].T, want_v)
+            assert np.array_equal(v1[:lens[b]], want_v)
             # rows past the new length are untouched
             assert np.array_equal(kc[b, h, lens[b]:], k_start[b, h, lens[b]:])
-            assert np.array_equal(vc[b, h, :, lens[b]:], v_start[b, h, :, lens[b]:])
+            assert np.array_equal(v1[lens[b]:], v0[lens[b]:])
 
 
 def test_commit_flags():
-    B, H, S, D, k = 3, 1, 10, 4, 4
+    B, H, S, D, k = 3, 1, 64, 4, 4
     kc = np.zeros((B, H, S, D), dtype=np.uint16)
-    vc = np.zeros((B, H, D, S), dtype=np.uint16)
+    vc = np.zeros((B, H, S // 64, D, 64), dtype=np.uint16)
     ks = np.ones((B, 20, H, D), dtype=np.uint16)
     vs = np.ones((B, 20, H, D), dtype=np.uint16)
-    lens = np.array([8, 8, 2], dtype=np.int32)
-    a = np.array([2, 3, 5], dtype=np.int32)  # fits, overflows (11 > 10), a > k
+    lens = np.array([62, 62, 2], dtype=np.int32)
+    a = np.array([2, 3, 5], dtype=np.int32)  # fits, overflows (65 > 64), a > k
     kc2, vc2, lens2, err = oracle.commit_ref(kc, vc, lens, ks, vs, a, k)
     assert err.tolist() == [0, 1, 2]
-    assert lens2.tolist() == [10, 8, 2]
-    assert kc2[0, 0, 8:10].sum() == 2 * D and kc2[1].sum() == 0 and kc2[2].sum() == 0
+    assert lens2.tolist() == [64, 62, 2]
+    assert kc2[0, 0, 62:64].sum() == 2 * D and kc2[1].sum() == 0 and kc2[2].sum() == 0
+    assert vc2[0, 0, 0, :, 62:64].sum() == 2 * D and vc2[0, 0, 0, :, :62].sum() == 0

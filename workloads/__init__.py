@@ -14,7 +14,8 @@ name           shape                        note
 q              [B][R][Hq][D]                query rows of the step block
 k_step/v_step  [B][R][Hkv][D]               keys/values of the step block
 k_cache        [B][Hkv][S_max][D]           settled keys, rows < lens[b] valid
-v_cache        [B][Hkv][D][S_max]           settled values, stored transposed
+v_cache        [B][Hkv][S_max/64][D][64]    settled values in pages of 64 positions,
+                                            each page stored transposed
 lens           [B] int32                    settled prefix length per sequence
 ar_logits      [B][k+1][V] float32          row 0 carried, rows 1..k candidates
 draft_logits   [B][k][k][V] float32         group g, slot s
@@ -42,6 +43,21 @@ _T_AR, _T_DRAFT, _T_CAND, _T_ACC, _T_BOOST = 11, 12, 13, 14, 15
 _T_TINY_W, _T_PROMPT, _T_INJECT = 21, 22, 23
 
 MASK_TOKEN_TINY = 1024  # extra embedding row of the tiny decoder; outside its LM head
+VPAGE = 64  # positions per value-cache page
+
+
+def v_paged(v: np.ndarray) -> np.ndarray:
+    """[..., S, D] values -> [..., S/64, D, 64] pages (layout only)."""
+    *lead, S, D = v.shape
+    assert S % VPAGE == 0
+    p = v.reshape(*lead, S // VPAGE, VPAGE, D)
+    return np.ascontiguousarray(np.swapaxes(p, -1, -2))
+
+
+def v_natural(vp: np.ndarray) -> np.ndarray:
+    """[..., S/64, D, 64] pages -> [..., S, D] values (layout only)."""
+    *lead, P, D, W = vp.shape
+    return np.ascontiguousarray(np.swapaxes(vp, -1, -2)).reshape(*lead, P * W, D)
 
 
 def generator(seed: int, config_id: int, step: int, tensor_id: int) -> np.random.Generator:
@@ -182,14 +198,15 @@ def kv_cache(shape: AttnShape, seed: int, config_id: int = 0, tail: str = "nan")
     """Settled caches filled up to lens[b]; rows at or past lens[b] hold ``tail``
     ("nan" poisons any read past the settled length, "zero", or "random")."""
     s = shape
+    assert s.S_max % VPAGE == 0, "cache capacity must be a whole number of 64-position pages"
     kc = _normal(generator(seed, config_id, 0, _T_KC), (s.B, s.Hkv, s.S_max, s.D), s.k_prescale)
-    vc = _normal(generator(seed, config_id, 0, _T_VC), (s.B, s.Hkv, s.D, s.S_max))
+    vc = _normal(generator(seed, config_id, 0, _T_VC), (s.B, s.Hkv, s.S_max, s.D))
     if tail != "random":
         fill = np.float32(np.nan) if tail == "nan" else np.float32(0.0)
         for b, L in enumerate(s.lens):
             kc[b, :, L:, :] = fill
-            vc[b, :, :, L:] = fill
-    return {"k_cache": _as_dtype(kc, s.dtype), "v_cache": _as_dtype(vc, s.dtype),
+            vc[b, :, L:, :] = fill
+    return {"k_cache": _as_dtype(kc, s.dtype), "v_cache": _as_dtype(v_paged(vc), s.dtype),
             "lens": np.asarray(s.lens, dtype=np.int32)}
 
 
