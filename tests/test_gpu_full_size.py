@@ -1,0 +1,65 @@
+"""GPU parity at the full sizes of the 1.5B-shaped, 8B-shaped and long-context
+8B-shaped steps, in the launch configuration bench.py times (the library's
+own split plan).  Attention on sampled (sequence, head) pairs the oracle
+computes one by one; verify and commit bit-exact on the whole batch."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+tidar = pytest.importorskip("diffusion_drafted_self_amd")
+from _gpu_util import DEV, attn_f32, attn_to_dev, bits, check_attention, to_dev  # noqa: E402
+
+NAMES = ["step_1p5b", "step_8b", "step_8b_long"]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name", NAMES)
+def test_full_size_attention_sampled(name):
+    wl = W.WORKLOADS[name]()
+    s = wl.attn
+    print(f"{name}: {wl.description}", flush=True)
+    d = W.attention_inputs(s, seed=7, config_id=wl.config_id, tail="nan")  # NaN past lens: never read
+    t = attn_to_dev(d, "bf16")
+    out, lse = tidar.step_attention(t["q"], t["k_step"], t["v_step"], t["k_cache"], t["v_cache"], t["lens"], s.k,
+                                    s.n_groups, s.sm_scale, max_len=s.max_len)
+    rng = np.random.default_rng(1)
+    pairs = [(0, 0), (s.B - 1, s.Hq - 1)] + [(int(rng.integers(s.B)), int(rng.integers(s.Hq))) for _ in range(4)]
+    f = attn_f32(d, "bf16")
+    ref, ref_lse = oracle.attention_ref(f["q"], f["k_step"], f["v_step"], f["k_cache"], f["v_cache"], d["lens"], s.k,
+                                        s.n_groups, s.sm_scale, pairs=pairs)
+    check_attention(out, lse, ref, ref_lse, "bf16", pairs=pairs, what=name)
+    assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name", NAMES)
+def test_full_size_verify(name):
+    wl = W.WORKLOADS[name]()
+    s = wl.attn
+    v = W.verify_inputs(s.B, s.k, wl.V, seed=7, config_id=wl.config_id, accept=wl.accept)
+    a, n = tidar.verify_greedy(to_dev(v["ar_logits"]), to_dev(v["draft_logits"]), to_dev(v["cand"]))
+    ra, rn = oracle.verify_ref(v["ar_logits"], v["draft_logits"], v["cand"])
+    assert a.cpu().numpy().tolist() == ra.tolist()
+    assert n.cpu().numpy().tolist() == rn.tolist()
+    if v["planted"] is not None:
+        assert ra.tolist() == v["planted"].tolist()
+
+
+@pytest.mark.timeout(300)
+def test_full_size_commit_8b():
+    wl = W.step_8b()
+    s = wl.attn
+    d = W.attention_inputs(s, seed=8, config_id=wl.config_id, tail="random")
+    a = W.accept_lengths("uniform", s.B, s.k, seed=8, config_id=wl.config_id)
+    kc, vc, ln = to_dev(d["k_cache"], True), to_dev(d["v_cache"], True), to_dev(d["lens"])
+    ef = torch.full((s.B,), -1, dtype=torch.int32, device=DEV)
+    tidar.kv_commit(kc, vc, ln, to_dev(d["k_step"], True), to_dev(d["v_step"], True), to_dev(a), s.k, ef)
+    rk, rv, rl, re = oracle.commit_ref(d["k_cache"], d["v_cache"], d["lens"], d["k_step"], d["v_step"], a, s.k)
+    assert ef.cpu().numpy().tolist() == re.tolist()
+    assert ln.cpu().numpy().tolist() == rl.tolist()
+    assert np.array_equal(bits(kc), rk) and np.array_equal(bits(vc), rv)

@@ -332,3 +332,27 @@ def corrupt_drafts(truth: Sequence[int], vocab: int, p: float, seed: int, step: 
     for t in truth:
         out.append(int(g.integers(0, vocab)) if g.random() < p else int(t))
     return out
+
+
+# ----------------------------------------------------------------------------- device-side draws
+def step_rows_device(shape: AttnShape, seed: int, step: int, device, config_id: int = 0) -> dict:
+    """q, k_step, v_step for one step drawn directly on the GPU with torch's
+    seeded Philox generator (bf16, rounded from float32 draws); used by the
+    long serving loop, where host-side draws of every step would dominate.
+    Callers hand host copies of these same tensors to the oracle."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence([seed, config_id, step, 99]).generate_state(1)[0]))
+    s = shape
+    dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+
+    def draw(shp, scale=1.0):
+        x = torch.randn(shp, generator=g, device=device, dtype=torch.float32)
+        if scale != 1.0:
+            x = x * scale
+        return x.to(dt)
+
+    return {"q": draw((s.B, s.R, s.Hq, s.D)),
+            "k_step": draw((s.B, s.R, s.Hkv, s.D), s.k_prescale),
+            "v_step": draw((s.B, s.R, s.Hkv, s.D))}
