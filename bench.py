@@ -19,6 +19,9 @@ Prints ONE JSON line.  Options:
   --no-cpu-baseline skip the oracle timing (for profiler runs)
   --calibrate-copy  run only a plain device copy of known size (for scaling
                     the FETCH_SIZE / WRITE_SIZE counters)
+  --summarize DIR   turn rocprofv3 outputs under DIR (kt/, pmc_FETCH_SIZE/,
+                    pmc_WRITE_SIZE/, pmc_copy_FETCH_SIZE/, pmc_copy_WRITE_SIZE/)
+                    into the summaries kept under profiles/
 """
 from __future__ import annotations
 
@@ -51,6 +54,7 @@ def parse():
     p.add_argument("--calibrate-copy", action="store_true")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--kv-chunk", type=int, default=0, help="key positions per attention chunk (0: library plan)")
+    p.add_argument("--summarize", metavar="DIR", help="write profiles/ summaries from rocprofv3 outputs in DIR")
     p.add_argument("--workload", default="step_8b", choices=["step_8b", "step_1p5b", "step_8b_long"],
                    help="synthetic workload (the reported line is the 8B-shaped step)")
     return p.parse_args()
@@ -115,6 +119,72 @@ def calibrate_copy():
     print(json.dumps({"calibrate_copy_bytes_each_way": COPY_CALIB_BYTES, "launches": 5}))
 
 
+def _csv_rows(pattern):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(pattern)):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def summarize(dirname):
+    """Summaries of a profiling session (see the module docstring for the
+    commands); written under profiles/."""
+    import statistics
+    cmd_kt = ("rocprofv3 --kernel-trace --stats -d DIR/kt -o kt --output-format csv -- "
+              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline")
+    stats = _csv_rows(os.path.join(dirname, "kt", "*kernel_stats.csv"))
+    lines = ["# Kernel trace: one TiDAR step on the 8B-shaped workload", "",
+             f"Command (from the repository root, MI355X): `{cmd_kt}`", "",
+             "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        if "tidar" not in r["Name"] and "copyBuffer" not in r["Name"]:
+            continue
+        name = r["Name"].replace("(anonymous namespace)::", "").replace("tidar::", "")
+        lines.append(f"| `{name[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    lines += ["", "`copyBuffer` is the 64-byte restore of the settled lengths after each timed step (harness).", ""]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "attention_step_8b_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines))
+
+    def per_dispatch(counter, kernel_key):
+        vals = [float(r["Counter_Value"]) for r in _csv_rows(os.path.join(dirname, f"pmc_{counter}", "*counter_collection.csv"))
+                if kernel_key in r["Kernel_Name"]]
+        return statistics.mean(vals) if vals else None, len(vals)
+
+    def copy_factor(counter):
+        vals = [float(r["Counter_Value"]) for r in
+                _csv_rows(os.path.join(dirname, f"pmc_copy_{counter}", "*counter_collection.csv"))
+                if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) >= 65536]
+        return (COPY_CALIB_BYTES / 1024.0) / statistics.mean(vals)
+
+    f_fetch, f_write = copy_factor("FETCH_SIZE"), copy_factor("WRITE_SIZE")
+    fetch, nf = per_dispatch("FETCH_SIZE", "attn_split_bf16")
+    write, nw = per_dispatch("WRITE_SIZE", "attn_split_bf16")
+    hbm = fetch * 1024 * f_fetch + write * 1024 * f_write
+    out = ["# HBM traffic of the step-attention kernel, 8B-shaped workload (rocprofv3 counters)",
+           "# Commands (from the repository root, MI355X), one counter per run:",
+           "#   rocprofv3 --pmc FETCH_SIZE -d DIR/pmc_FETCH_SIZE -o p --output-format csv -- "
+           "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+           "#   rocprofv3 --pmc WRITE_SIZE -d DIR/pmc_WRITE_SIZE -o p --output-format csv -- "
+           "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+           "#   the same two counters on: python3 bench.py --calibrate-copy  (1 GiB device copy)",
+           "# Counter values are KiB per dispatch; each is scaled by (known bytes / counter) of the copy.",
+           f"fetch_kib_per_launch = {fetch:.1f}",
+           f"write_kib_per_launch = {write:.1f}",
+           f"dispatches = {nf}",
+           f"copy_scale_fetch = {f_fetch:.4f}",
+           f"copy_scale_write = {f_write:.4f}",
+           f"hbm_bytes_per_launch = {hbm:.0f}",
+           f"kernel_source_sha = {attention_source_sha()}", ""]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(out))
+    print("\n".join(lines))
+    print("\n".join(out))
+
+
 def cpu_baseline(wl, d, v, a_planted):
     """The oracle (as it stands) on the same workload: three full steps."""
     import numpy as np
@@ -162,6 +232,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.summarize:
+        summarize(args.summarize)
         return
 
     import numpy as np
