@@ -2,7 +2,7 @@
 
 The library is the only native artefact: the kernels (attention, verify,
 commit) and the C ABI of include/tidar.h.  Every HIP source is compiled with
-packed fp32 instructions disabled."""
+packed fp32 instructions disabled and MFMA results kept in arch VGPRs."""
 from __future__ import annotations
 
 import os
@@ -38,7 +38,11 @@ def build(verbose: bool = False) -> str:
     os.makedirs(objdir, exist_ok=True)
     flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
              "-I", INCLUDE, "-I", CSRC,
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             # MFMA results in arch VGPRs: the attention loop feeds its score
+             # accumulators straight to the VALU softmax, so results parked in
+             # AGPRs would cost a copy per element
+             "-mllvm", "-amdgpu-mfma-vgpr-form"]
     procs, objs = [], []
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")

@@ -11,14 +11,17 @@
 // paragraph on masking; abstract on fugumt.com).
 //
 // Kernels
-//   attn_split_bf16_kernel<D, NW>  one workgroup = NW waves x 32 query rows
-//       of one (b, kvh) against one key chunk.  Per 64-key tile: K and V^T
-//       stream into two LDS stages by direct loads, S^T = K.Q^T and O^T += V^T.P^T run on
-//       v_mfma_f32_32x32x16_bf16, the online softmax runs in registers
-//       (exp2 with the scale folded in, lazy rescale), and the mask is
-//       evaluated from zone indices only on tiles that hold step keys.
+//   attn_pipe_bf16_kernel<D, NT>  one workgroup per CU: four waves, one per
+//       SIMD, each owning up to NT tiles of 16 query rows of one (b, kvh),
+//       against one key chunk.  Per 64-key tile, K and V^T arrive in LDS
+//       rings by direct loads issued two and three tiles ahead; scores
+//       S^T = K.Q^T and O^T += V^T.P^T run on v_mfma_f32_16x16x32_bf16, each
+//       K / V^T operand read once from LDS and reused by the NT row tiles.
+//       The loop body holds the softmax of tile t, the scores of tile t+1
+//       and the P.V product of tile t-1, three independent streams in one
+//       basic block, so the exp2 work of the VALU runs under the MFMAs.
 //       Single-chunk sequences are normalised and written directly; others
-//       leave the chunk's unnormalised output, running max and sum.
+//       leave the chunk's unnormalised output, reference max and sum.
 //   attn_split_f32_kernel<D>  the f32 instance (VALU FMA; fp32 MFMA peak
 //       equals VALU fp32 peak on this part), same partial format.
 //   attn_merge_kernel<Out, D>  log-sum-exp merge of the chunks, one wave per
@@ -30,13 +33,9 @@ namespace tidar {
 
 namespace {
 
-constexpr int TK = 64;  // keys per tile
-
-// S^T tile row i <-> key sigma(i) of the 32-key block.  With this order the
-// 16 fp32 scores a lane holds after S^T = K.Q^T are, in register order, the
-// keys 16h + 8*(lane/32) + 0..7 (h = 0, 1): exactly the B-operand layout of
-// the P^T factor of O^T += V^T.P^T, so P needs no cross-lane shuffle.
-__device__ __forceinline__ int sigma(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+constexpr int TK = 64;    // keys per tile
+constexpr int NWV = 4;    // waves per bf16 workgroup, one per SIMD
+constexpr int RING = 4;   // LDS slots for K tiles, and as many for V^T tiles
 
 // The value cache holds pages of VPAGE positions, each stored transposed
 // ([S_max/VPAGE][D][VPAGE] per (b, kvh)), so one 64-key V^T tile is one
@@ -53,8 +52,10 @@ __device__ __forceinline__ size_t vpos(int d, int c, int D) {  // element (d, po
 // (each lane moves 16 B; lane t lands at byte 16t of the 1 KB block), so a
 // 16 B piece's position inside its row is permuted by an XOR swizzle chosen
 // by the source address each lane reads: logical piece p of K row `row` sits
-// at physical piece p ^ kswz(row), logical piece q of V^T row d at q ^ (d&7).
-// With these, the 32 lanes reading one MFMA operand column hit distinct banks.
+// at physical piece p ^ kswz(row), logical piece q of V^T row d at
+// q ^ vswz(d).  With these, the 16 lanes reading one MFMA operand column hit
+// distinct banks whether the LDS serves 8 or 16 lanes of a 16 B read per
+// cycle.
 template <int D>
 struct Tile {
   static constexpr int KROW = D * 2;        // bytes per K row
@@ -62,25 +63,37 @@ struct Tile {
   static constexpr int K_BYTES = TK * KROW;
   static constexpr int VROW = TK * 2;       // bytes per V^T row (8 pieces)
   static constexpr int V_BYTES = D * VROW;
-  static constexpr int NK = K_BYTES / 1024; // 1 KB load instructions per tile
-  static constexpr int NV = V_BYTES / 1024;
-  static constexpr int NI = NK + NV;
+  static constexpr int NKW = K_BYTES / 1024 / NWV;  // direct loads per wave per K tile
+  static constexpr int NVW = V_BYTES / 1024 / NWV;  // ... per V^T tile
+  static constexpr int NDB = D / 16;  // 16-row head-dim blocks of O^T
+  static constexpr int NDC = D / 32;  // 32-deep head-dim steps of S^T
 };
 
-// V^T rows: 16 consecutive rows get distinct (row parity, piece) pairs and 8
-// consecutive rows distinct pieces, so the read is conflict-free whether the
-// LDS serves 8 or 16 lanes of a 16 B read per cycle.
-__device__ __forceinline__ int vswz(int d) { return (d & 7) ^ ((d >> 3) & 1); }
+// Score block kb4 (16 keys) of a tile: MFMA row i (= lane & 15 of the A
+// operand) is tile key 32*(kb4>>1) + 8*(i>>2) + 4*(kb4&1) + (i&3).  With this
+// order the 4 scores a lane holds from blocks 2c and 2c+1 are keys
+// 32c + 8*(lane>>4) + 0..7: exactly the B-operand layout of P^T for the
+// 32-key step c of O^T += V^T.P^T, so P needs no cross-lane movement.
+__device__ __forceinline__ int krow_of(int kb4, int i) {
+  return 32 * (kb4 >> 1) + 8 * (i >> 2) + 4 * (kb4 & 1) + (i & 3);
+}
 
+// Within one operand read the rows vary in bits 0, 1, 3 and 4; the swizzle
+// maps those bits (with the row parity where a row is 128 B) to distinct
+// 16 B slots.
 template <int D>
 __device__ __forceinline__ int kswz(int row) {
-  if constexpr (Tile<D>::KPPR == 16) return sigma(row & 15);
-  else return (row & 3) | ((row >> 1) & 4);
+  if constexpr (Tile<D>::KPPR == 16) return (row & 3) | ((row >> 1) & 12);
+  else return ((row >> 1) & 1) | ((row >> 2) & 2) | (((row ^ (row >> 4)) & 1) << 2);
 }
+// V^T rows: 16 consecutive rows get distinct (row parity, piece) pairs and 8
+// consecutive rows distinct pieces.
+__device__ __forceinline__ int vswz(int d) { return (d & 7) ^ ((d >> 3) & 1); }
 
 // LDS pointers stay in address space 3 end to end (no generic casts)
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0]+[15:14], expcnt[6:4], lgkmcnt[11:8])
 template <int N>
@@ -90,6 +103,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+// Workgroup barrier that is also a compiler memory barrier: LDS reads and
+// writes stay on their side of it.  Waiting for this wave's own memory
+// operations is left to the caller (the ring waits for some direct loads
+// only).
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Direct global->LDS load of 16 B per lane: lane t's bytes land at
 // lds_dst + 16*t.  Issued as inline asm with a scalar base and a 32-bit
@@ -107,63 +129,59 @@ __device__ __forceinline__ void dma_b128(const char* base, unsigned off, lds_cha
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(sb), "s"(m0) : "memory", "m0");
 }
 
-// Per-lane byte offsets of this wave's direct loads inside a tile: load
-// i = wave + ii*NW of the tile (K loads first, then V^T loads), each moving
-// one 1 KB block of the swizzled LDS layout.  Tile-invariant, so computed
-// once per workgroup.
-template <int D, int NW>
+// Per-lane byte offsets of this wave's direct loads inside a tile: wave w
+// moves the 1 KB blocks w*NKW .. w*NKW+NKW-1 of the K tile and
+// w*NVW .. w*NVW+NVW-1 of the V^T tile.  Tile-invariant.
+template <int D>
 struct DmaPlan {
-  static constexpr int N = (Tile<D>::NI + NW - 1) / NW;
-  unsigned off[N];
+  unsigned k[Tile<D>::NKW];
+  unsigned v[Tile<D>::NVW];
 };
 
-template <int D, int NW>
-__device__ __forceinline__ void dma_plan(DmaPlan<D, NW>& pl, int wave, int lane) {
+template <int D>
+__device__ __forceinline__ void dma_plan(DmaPlan<D>& pl, int wave, int lane) {
   using T = Tile<D>;
 #pragma unroll
-  for (int ii = 0; ii < DmaPlan<D, NW>::N; ++ii) {
-    const int i = wave + ii * NW;
-    unsigned off = 0;
-    if (i < T::NK) {
-      const int row = i * (64 / T::KPPR) + lane / T::KPPR;
-      const int p = (lane % T::KPPR) ^ kswz<D>(row);
-      off = row * T::KROW + p * 16;
-    } else if (i < T::NI) {
-      const int d = (i - T::NK) * 8 + (lane >> 3);
-      const int q = (lane & 7) ^ vswz(d);
-      off = d * T::VROW + q * 16;
-    }
-    pl.off[ii] = off;
+  for (int ii = 0; ii < T::NKW; ++ii) {
+    const int row = (wave * T::NKW + ii) * (1024 / T::KROW) + lane / T::KPPR;
+    const int p = (lane % T::KPPR) ^ kswz<D>(row);
+    pl.k[ii] = row * T::KROW + p * 16;
+  }
+#pragma unroll
+  for (int ii = 0; ii < T::NVW; ++ii) {
+    const int d = (wave * T::NVW + ii) * 8 + (lane >> 3);
+    const int q = (lane & 7) ^ vswz(d);
+    pl.v[ii] = d * T::VROW + q * 16;
   }
 }
 
-// Issue this wave's share of the direct loads of one prefix tile (keys
-// t0..t0+TK-1, all settled).  The K tile is 64 contiguous cache rows, the
-// V^T tile one contiguous value page.
-template <int D, int NW>
-__device__ __forceinline__ void issue_tile(lds_char* sK, lds_char* sV, const bf16* kc_base, const bf16* vc_base,
-                                           const DmaPlan<D, NW>& pl, int t0, int wave) {
+// This wave's share of the direct loads of K tile / V^T tile (keys t0..t0+TK-1,
+// all settled): 64 contiguous cache rows, one contiguous value page.
+template <int D>
+__device__ __forceinline__ void issue_k(lds_char* sK, const bf16* kc_base, const DmaPlan<D>& pl, int t0, int wave) {
   using T = Tile<D>;
   const char* kt = (const char*)(kc_base + (size_t)t0 * D);
+#pragma unroll
+  for (int ii = 0; ii < T::NKW; ++ii) dma_b128(kt, pl.k[ii], sK + (wave * T::NKW + ii) * 1024);
+}
+template <int D>
+__device__ __forceinline__ void issue_v(lds_char* sV, const bf16* vc_base, const DmaPlan<D>& pl, int t0, int wave) {
+  using T = Tile<D>;
   const char* vt = (const char*)(vc_base + (size_t)(t0 / VPAGE) * D * VPAGE);
 #pragma unroll
-  for (int ii = 0; ii < DmaPlan<D, NW>::N; ++ii) {
-    const int i = wave + ii * NW;
-    if (i < T::NK) dma_b128(kt, pl.off[ii], sK + i * 1024);
-    else if (i < T::NI) dma_b128(vt, pl.off[ii], sV + (i - T::NK) * 1024);
-  }
+  for (int ii = 0; ii < T::NVW; ++ii) dma_b128(vt, pl.v[ii], sV + (wave * T::NVW + ii) * 1024);
 }
 
 // Stage a tile that reaches past the settled prefix (the step block, or
 // keys past the end) into the same swizzled layout.  Settled keys come from
 // the caches in 16 B pieces; step rows are read 16 B at a time and their
 // values scattered into V^T columns; everything else is zero.
-template <int D, int NW>
+template <int D>
 __device__ __forceinline__ void stage_tail_tile(lds_char* sK, lds_char* sV, const bf16* kc_base, const bf16* vc_base,
                                                 const bf16* ks_base, const bf16* vs_base, size_t step_stride,
                                                 int t0, int L, int Ltot, int tid) {
   using T = Tile<D>;
-  for (int id = tid; id < TK * T::KPPR; id += NW * 64) {
+  for (int id = tid; id < TK * T::KPPR; id += NWV * 64) {
     const int row = id / T::KPPR, p = id % T::KPPR;
     const int c = t0 + row;
     bf16x8 val = {};
@@ -172,7 +190,7 @@ __device__ __forceinline__ void stage_tail_tile(lds_char* sK, lds_char* sV, cons
     *(lds_bf16x8*)(sK + row * T::KROW + ((p ^ kswz<D>(row)) * 16)) = val;
   }
   // settled part of V^T (pieces of 8 positions), zero elsewhere
-  for (int id = tid; id < D * 8; id += NW * 64) {
+  for (int id = tid; id < D * 8; id += NWV * 64) {
     const int d = id >> 3, q = id & 7;
     const int c0 = t0 + q * 8;
     bf16x8 val = {};
@@ -185,10 +203,10 @@ __device__ __forceinline__ void stage_tail_tile(lds_char* sK, lds_char* sV, cons
     *(lds_bf16x8*)(sV + d * T::VROW + ((q ^ vswz(d)) * 16)) = val;
   }
   wait_all();
-  __builtin_amdgcn_s_barrier();
+  barrier();
   // step rows: one 16 B load of 8 head-dim elements, scattered into 8 V^T rows
   const int j0 = max(t0, L), j1 = min(t0 + TK, Ltot);
-  for (int id = tid; id < (j1 - j0) * (D / 8); id += NW * 64) {
+  for (int id = tid; id < (j1 - j0) * (D / 8); id += NWV * 64) {
     const int c = j0 + id / (D / 8), dc = id % (D / 8);
     const bf16x8 val = *(const bf16x8*)(vs_base + (size_t)(c - L) * step_stride + dc * 8);
     const int cl = c - t0;
@@ -200,102 +218,224 @@ __device__ __forceinline__ void stage_tail_tile(lds_char* sK, lds_char* sV, cons
   }
 }
 
-// One 64-key tile: S^T = K.Q^T, mask (tail tiles only), online softmax,
-// O^T += V^T.P^T.  LDS operand reads run a few MFMAs ahead of their use
-// (a small ring of registers), so the LDS latency hides behind the MFMAs.
-template <int D, bool MASK>
-__device__ __forceinline__ void compute_tile(const lds_char* sK, const lds_char* sV, int t0, int L, int ke, int r, int k,
-                                             float scale_log2, const bf16x8 (&qf)[D / 16], floatx16 (&o)[D / 32],
-                                             float& m_run, float& l_run, int lane) {
+// Running softmax state of one wave: per row tile, the reference max m (log2
+// units, shared by the four lanes holding a row) and this lane's part of the
+// sum l.  Scores are turned into p = exp2(scale_log2*s - m) against the
+// current m without looking for the tile's max: as long as every p stays
+// below 2^64 the fp32 sums and the bf16 P keep full relative precision (a
+// reference below the true max only scales them), so the tile's sum of p
+// decides.  When it exceeds 2^64 (always on a row's first tile, where m is
+// kNoMax) the wave takes the exact path: true tile max across the four
+// lanes of each row, rescale of O and l, p recomputed.
+constexpr float kSumLimit = 18446744073709551616.0f;  // 2^64
+
+// p = exp2(scale_log2*s - m) against the current reference; returns true
+// when some row tile of this lane needs the exact path.
+template <int NT>
+__device__ __forceinline__ bool sm_tile(const floatx4 (&s)[NT][4], bf16x8 (&pk)[NT][2], float (&ps)[NT],
+                                        const float (&m)[NT], float scale_log2) {
+  bool big = false;
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    float sum = 0.f;
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[rt][kb4][v], scale_log2, -m[rt]));
+        sum += p;
+        pk[rt][kb4 >> 1][4 * (kb4 & 1) + v] = (bf16)p;
+      }
+    ps[rt] = sum;
+    big |= sum > kSumLimit;
+  }
+  return big;
+}
+
+// Exact path: move each row's reference to the true running max, rescale
+// O and l, recompute p.
+template <int D, int NT>
+__device__ __forceinline__ void sm_exact(const floatx4 (&s)[NT][4], bf16x8 (&pk)[NT][2], float (&m)[NT], float (&l)[NT],
+                                      floatx4 (&o)[NT][D / 16], float scale_log2) {
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[rt][kb4][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m[rt], mx * scale_log2);
+    const float alpha = __builtin_amdgcn_exp2f(m[rt] - m_new);
+    m[rt] = m_new;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[rt][db][v] *= alpha;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[rt][kb4][v], scale_log2, -m_new));
+        sum += p;
+        pk[rt][kb4 >> 1][4 * (kb4 & 1) + v] = (bf16)p;
+      }
+    l[rt] = l[rt] * alpha + sum;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int D, int NT>
+__device__ __forceinline__ void softmax_commit(bool big, const floatx4 (&s)[NT][4], bf16x8 (&pk)[NT][2],
+                                               const float (&ps)[NT], float (&m)[NT], float (&l)[NT],
+                                               floatx4 (&o)[NT][D / 16], float scale_log2) {
+  if (__any(big)) {
+    sm_exact<D, NT>(s, pk, m, l, o, scale_log2);
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) l[rt] += ps[rt];
+  }
+}
+
+template <int NT>
+constexpr int operand_depth() { return NT == 1 ? 4 : (NT == 2 ? 3 : 2); }
+
+// One pipelined loop body: the scores of the next tile (S steps, one per
+// (head-dim step, 16-key block)), the P.V product of the previous tile (PV
+// steps, one per (32-key step, 16-row head-dim block)) and the softmax of
+// the current tile, issued as a fixed sequence of steps.  Each step runs NT
+// MFMAs on one LDS operand, reads the operand of the step DEPTH ahead and
+// takes its slice of the softmax elements; a scheduling fence after every
+// step keeps the exp2 work spread under the MFMAs and bounds the operands in
+// flight.  Returns true when some lane's softmax needs the exact path.
+template <int D, int NT, bool DO_S, bool DO_PV>
+__device__ __forceinline__ bool pipe_body(const lds_char* sKn, const lds_char* sVp, const bf16x8 (&qf)[NT][D / 32],
+                                          floatx4 (&s_next)[NT][4], const floatx4 (&s_cur)[NT][4],
+                                          bf16x8 (&p_cur)[NT][2], const bf16x8 (&p_prev)[NT][2],
+                                          floatx4 (&o)[NT][D / 16], float (&ps)[NT], const float (&m)[NT],
+                                          float sl2, int lane) {
   using T = Tile<D>;
-  const int half = lane >> 5, l32 = lane & 31;
-  // K operand of S^T item i (i = 2c + kb2): row 32*kb2 + sigma(l32), logical piece 2c + half
-  const lds_char* kr0 = sK + sigma(l32) * T::KROW;
-  const int ksw = kswz<D>(sigma(l32));  // same for rows +32
-  auto kread = [&](int i) -> bf16x8 {
-    const int kb2 = i & 1, c = i >> 1;
-    return *(const lds_bf16x8*)(kr0 + kb2 * 32 * T::KROW + (((2 * c + half) ^ ksw) * 16));
+  constexpr int NS = DO_S ? T::NDC * 4 : 0;
+  constexpr int NP = DO_PV ? 2 * T::NDB : 0;
+  constexpr int NSTEP = NS + NP;
+  constexpr int NE = NT * 16;  // softmax elements of this lane
+  constexpr int DEPTH = operand_depth<NT>();
+  const int i16 = lane & 15, hi = lane >> 4;
+  const lds_char* kr = sKn + krow_of(0, i16) * T::KROW;
+  const int ksw = kswz<D>(krow_of(0, i16));
+  const lds_char* vr = sVp + i16 * T::VROW;
+  const int vsw = vswz(i16);
+  auto frag = [&](int i) -> bf16x8 {
+    if (i < NS) {
+      const int c = i / 4, kb4 = i % 4;
+      return *(const lds_bf16x8*)(kr + krow_of(kb4, 0) * T::KROW + (((4 * c + hi) ^ ksw) * 16));
+    }
+    const int j = i - NS, kc = j / T::NDB, db = j % T::NDB;
+    return *(const lds_bf16x8*)(vr + db * 16 * T::VROW + (((4 * kc + hi) ^ vsw) * 16));
   };
-  // V operand of PV item j (j = 4*kc + db... for D/32 blocks): row 32*db + l32, logical piece 2*kc + half
-  constexpr int NDB = D / 32;
-  const lds_char* vr0 = sV + l32 * T::VROW;
-  const int vsw = vswz(l32);  // rows 32*db + l32 share the low bits of l32
-  auto vread = [&](int j) -> bf16x8 {
-    const int db = j % NDB, kc = j / NDB;
-    return *(const lds_bf16x8*)(vr0 + db * 32 * T::VROW + (((2 * kc + half) ^ vsw) * 16));
+  const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+  bf16x8 fr[DEPTH + 1];
+#pragma unroll
+  for (int i = 0; i < DEPTH && i < NSTEP; ++i) fr[i] = frag(i);
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) ps[rt] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NSTEP; ++i) {
+    if (i + DEPTH < NSTEP) fr[(i + DEPTH) % (DEPTH + 1)] = frag(i + DEPTH);
+    const bf16x8 f = fr[i % (DEPTH + 1)];
+    if (i < NS) {
+      const int c = i / 4, kb4 = i % 4;
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt)
+        s_next[rt][kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, qf[rt][c], c == 0 ? z : s_next[rt][kb4], 0, 0, 0);
+    } else {
+      const int j = i - NS, kc = j / T::NDB, db = j % T::NDB;
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt)
+        o[rt][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, p_prev[rt][kc], o[rt][db], 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = i * (NE / 2) / NSTEP; e < (i + 1) * (NE / 2) / NSTEP; ++e) {  // element pairs
+      const int rt = e / 8, kb4 = (e / 2) % 4, v = 2 * (e % 2);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[rt][kb4][v], sl2, -m[rt]));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[rt][kb4][v + 1], sl2, -m[rt]));
+      ps[rt] += p0 + p1;
+      // convert here: the empty asm pins the packed pair to this step, so
+      // the compiler cannot sink the conversion past the exact-path branch
+      // and keep 32-bit p values alive instead
+      unsigned u = __builtin_bit_cast(unsigned, (bf16x2){(bf16)p0, (bf16)p1});
+      asm volatile("" : "+v"(u));
+      const bf16x2 t2 = __builtin_bit_cast(bf16x2, u);
+      p_cur[rt][kb4 >> 1][4 * (kb4 & 1) + v] = t2[0];
+      p_cur[rt][kb4 >> 1][4 * (kb4 & 1) + v + 1] = t2[1];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  bool big = false;
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) big |= ps[rt] > kSumLimit;
+  return big;
+}
+
+// Scores of one tile alone, and P.V of one tile alone, in the same fenced
+// step order (ring prologue, tiles past the prefix, last tile).
+template <int D, int NT>
+__device__ __forceinline__ void s_tile(const lds_char* sK, const bf16x8 (&qf)[NT][D / 32], floatx4 (&s)[NT][4],
+                                       int lane) {
+  using T = Tile<D>;
+  constexpr int NSTEP = T::NDC * 4;
+  constexpr int DEPTH = operand_depth<NT>();
+  const int i16 = lane & 15, hi = lane >> 4;
+  const lds_char* kr = sK + krow_of(0, i16) * T::KROW;
+  const int ksw = kswz<D>(krow_of(0, i16));
+  auto frag = [&](int i) -> bf16x8 {
+    const int c = i / 4, kb4 = i % 4;
+    return *(const lds_bf16x8*)(kr + krow_of(kb4, 0) * T::KROW + (((4 * c + hi) ^ ksw) * 16));
   };
+  const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+  bf16x8 fr[DEPTH + 1];
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i) fr[i] = frag(i);
+#pragma unroll
+  for (int i = 0; i < NSTEP; ++i) {
+    if (i + DEPTH < NSTEP) fr[(i + DEPTH) % (DEPTH + 1)] = frag(i + DEPTH);
+    const int c = i / 4, kb4 = i % 4;
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt)
+      s[rt][kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[i % (DEPTH + 1)], qf[rt][c], c == 0 ? z : s[rt][kb4],
+                                                           0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
 
-  constexpr int NS = 2 * (D / 16);  // S^T MFMAs
-  constexpr int RA = 3;             // read-ahead depth
-  floatx16 s[2];
+template <int D, int NT>
+__device__ __forceinline__ void pv_tile(const lds_char* sV, const bf16x8 (&pk)[NT][2], floatx4 (&o)[NT][D / 16],
+                                        int lane) {
+  using T = Tile<D>;
+  constexpr int NSTEP = 2 * T::NDB;
+  constexpr int DEPTH = operand_depth<NT>();
+  const int i16 = lane & 15, hi = lane >> 4;
+  const lds_char* vr = sV + i16 * T::VROW;
+  const int vsw = vswz(i16);
+  auto frag = [&](int j) -> bf16x8 {
+    const int kc = j / T::NDB, db = j % T::NDB;
+    return *(const lds_bf16x8*)(vr + db * 16 * T::VROW + (((4 * kc + hi) ^ vsw) * 16));
+  };
+  bf16x8 fr[DEPTH + 1];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) { s[0][v] = 0.f; s[1][v] = 0.f; }
-  bf16x8 kbuf[RA + 1];
+  for (int i = 0; i < DEPTH; ++i) fr[i] = frag(i);
 #pragma unroll
-  for (int i = 0; i < RA; ++i) kbuf[i] = kread(i);
+  for (int j = 0; j < NSTEP; ++j) {
+    if (j + DEPTH < NSTEP) fr[(j + DEPTH) % (DEPTH + 1)] = frag(j + DEPTH);
+    const int kc = j / T::NDB, db = j % T::NDB;
 #pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    if (i + RA < NS) kbuf[(i + RA) % (RA + 1)] = kread(i + RA);
-    s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbuf[i % (RA + 1)], qf[i >> 1], s[i & 1], 0, 0, 0);
-  }
-  // the first V operands load while the softmax runs
-  constexpr int NPV = NDB * 4;
-  constexpr int RV = 4;
-  bf16x8 vbuf[RV];
-#pragma unroll
-  for (int j = 0; j < RV; ++j) vbuf[j] = vread(j);
-
-  if (MASK) {
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int i = 8 * (v >> 2) + 4 * half + (v & 3);
-        const int c = t0 + 32 * kb2 + sigma(i);
-        const bool vis = c < ke && (c < L || step_visible(r, c - L, k));
-        if (!vis) s[kb2][v] = -INFINITY;
-      }
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb2][v]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  // The reference max only moves when a score exceeds it by more than 2^8:
-  // in between, p = exp2(s - m_run) <= 256 stays far inside the fp32 and
-  // bf16 ranges, and O, l keep one consistent scale, so most tiles skip the
-  // rescale of O entirely.
-  const float m_tile = mx * scale_log2;
-  const bool grow = m_tile > m_run + 8.f;
-  if (__any(grow)) {
-    const float m_new = grow ? m_tile : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
-  }
-  bf16x8 pk[4];
-  float psum = 0.f;
-#pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const float p = __builtin_amdgcn_exp2f(s[kb2][8 * h + jj] * scale_log2 - m_run);
-        psum += p;
-        pk[2 * kb2 + h][jj] = (bf16)p;
-      }
-  l_run += psum;
-#pragma unroll
-  for (int j = 0; j < NPV; ++j) {
-    const bf16x8 va = vbuf[j % RV];
-    if (j + RV < NPV) vbuf[j % RV] = vread(j + RV);
-    o[j % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[j / NDB], o[j % NDB], 0, 0, 0);
+    for (int rt = 0; rt < NT; ++rt)
+      o[rt][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[j % (DEPTH + 1)], pk[rt][kc], o[rt][db], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -304,44 +444,60 @@ __device__ __forceinline__ void compute_tile(const lds_char* sK, const lds_char*
 // attn_merge_kernel combines them (a kernel boundary is the cheap coherence
 // point across XCDs; an in-kernel device-scope fence writes back and
 // invalidates the whole L2 of the XCD).
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-void attn_split_bf16_kernel(AttnArgs a) {
+//
+// Prefix tiles j = 0..n-1 of the chunk flow through the LDS rings: K(j) is
+// requested three loop iterations before its scores are needed (slot j%4),
+// V(j) two iterations before that tile's P.V (slot j%4).  Iteration t waits
+// for K(t+1) and V(t-1), passes one barrier (after which every wave is done
+// with iteration t-1, so slots K(t-1) and V(t-2) are free), requests K(t+3)
+// and V(t+2), then runs softmax(t) | scores(t+1) | P.V(t-1).  Tiles that
+// reach past the settled prefix are staged through registers into the
+// fourth slots first, before the ring fills them.
+template <int D, int NT>
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_pipe_bf16_kernel(AttnArgs a) {
   using T = Tile<D>;
-  __shared__ __attribute__((aligned(1024))) char smK0[T::K_BYTES];
-  __shared__ __attribute__((aligned(1024))) char smV0[T::V_BYTES];
-  __shared__ __attribute__((aligned(1024))) char smK1[T::K_BYTES];
-  __shared__ __attribute__((aligned(1024))) char smV1[T::V_BYTES];
-  lds_char* sK0 = (lds_char*)smK0;
-  lds_char* sV0 = (lds_char*)smV0;
-  lds_char* sK1 = (lds_char*)smK1;
-  lds_char* sV1 = (lds_char*)smV1;
+  __shared__ __attribute__((aligned(1024))) char smem[RING * (T::K_BYTES + T::V_BYTES)];
+  __shared__ int ovf_flag;
+  lds_char* const sK0 = (lds_char*)smem;
+  lds_char* const sV0 = sK0 + RING * T::K_BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int half = lane >> 5;
+  const int hi = lane >> 4;
 
   int t = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int rb = t % a.n_rowblk;
+  const int rw = t % a.n_rowblk;
   t /= a.n_rowblk;
   const int split = t % a.n_split;
   t /= a.n_split;
   const int kvh = t % a.Hkv;
   const int b = t / a.Hkv;
 
-  const int m = rb * (NW * 32) + wave * 32 + (lane & 31);  // this lane's query row
-  const bool row_ok = m < a.M;
-  const int r = row_ok ? m / a.G : 0;
-  const int jh = row_ok ? m % a.G : 0;
-  const int h = kvh * a.G + jh;
-  bf16* orow = (bf16*)a.out + ((size_t)(b * a.R + r) * a.Hq + h) * D;
+  // this wave's row tiles: [w0, w1) of the n16 tiles of 16 rows of (b, kvh)
+  const int T0 = rw * a.n16 / a.n_rowblk, T1 = (rw + 1) * a.n16 / a.n_rowblk;
+  const int w0 = T0 + wave * (T1 - T0) / NWV, w1 = T0 + (wave + 1) * (T1 - T0) / NWV;
+  int mrow[NT];
+  bool row_ok[NT];
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    mrow[rt] = 16 * (w0 + rt) + (lane & 15);
+    row_ok[rt] = w0 + rt < w1 && mrow[rt] < a.M;
+  }
 
   const int L = a.lens[b];
   if (L < 0 || L > a.max_len) {  // contract violation: NaN rows, written once
-    if (split == 0 && row_ok) {
-      for (int e = half; e < D; e += 2) orow[e] = (bf16)NAN;
-      if (a.lse && half == 0) a.lse[((size_t)b * a.Hq + h) * a.R + r] = NAN;
+    if (split == 0) {
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+        if (!row_ok[rt]) continue;
+        const int r = mrow[rt] / a.G, h = kvh * a.G + mrow[rt] % a.G;
+        bf16* orow = (bf16*)a.out + ((size_t)(b * a.R + r) * a.Hq + h) * D;
+        for (int db = 0; db < D / 16; ++db)
+          for (int v = 0; v < 4; ++v) orow[16 * db + 4 * hi + v] = (bf16)NAN;
+        if (a.lse && hi == 0) a.lse[((size_t)b * a.Hq + h) * a.R + r] = NAN;
+      }
     }
     return;
   }
@@ -351,22 +507,6 @@ void attn_split_bf16_kernel(AttnArgs a) {
   const int ke = min(kb + a.chunk, Ltot);
   const int n_valid = (Ltot + a.chunk - 1) / a.chunk;
 
-  bf16x8 qf[D / 16];
-  {
-    const bf16* qrow = (const bf16*)a.q + ((size_t)(b * a.R + r) * a.Hq + h) * D;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      bf16x8 z = {};
-      qf[c] = row_ok ? *(const bf16x8*)(qrow + 16 * c + 8 * half) : z;
-    }
-  }
-  floatx16 o[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
-  float m_run = kNoMax, l_run = 0.f;
-
   const size_t pair = (size_t)b * a.Hkv + kvh;
   const bf16* kc_base = (const bf16*)a.k_cache + pair * a.S_max * D;
   const bf16* vc_base = (const bf16*)a.v_cache + pair * D * a.S_max;
@@ -374,69 +514,187 @@ void attn_split_bf16_kernel(AttnArgs a) {
   const bf16* ks_base = (const bf16*)a.k_step + (size_t)b * a.R * step_stride + kvh * D;
   const bf16* vs_base = (const bf16*)a.v_step + (size_t)b * a.R * step_stride + kvh * D;
 
-  // Prefix tiles [kb, fast_end) stream through two LDS stages by direct
-  // loads.  One barrier per tile: after it, every wave's loads of tile t have
-  // landed and every wave is done with tile t-1, whose stage then receives
-  // the loads of tile t+1 while tile t is computed.
   const int fast_end = min(ke, (L / TK) * TK);
-  const int n_fast = fast_end > kb ? (fast_end - kb) / TK : 0;
-  DmaPlan<D, NW> plan;
-  dma_plan<D, NW>(plan, wave, lane);
-  if (n_fast > 0) issue_tile<D, NW>(sK0, sV0, kc_base, vc_base, plan, kb, wave);
-  for (int it = 0; it < n_fast; it += 2) {
-    wait_vmcnt<0>();
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_barrier();
-    if (it + 1 < n_fast) issue_tile<D, NW>(sK1, sV1, kc_base, vc_base, plan, kb + (it + 1) * TK, wave);
-    compute_tile<D, false>(sK0, sV0, kb + it * TK, L, ke, r, a.k, a.scale_log2, qf, o, m_run, l_run, lane);
-    if (it + 1 >= n_fast) break;
-    wait_vmcnt<0>();
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_barrier();
-    if (it + 2 < n_fast) issue_tile<D, NW>(sK0, sV0, kc_base, vc_base, plan, kb + (it + 2) * TK, wave);
-    compute_tile<D, false>(sK1, sV1, kb + (it + 1) * TK, L, ke, r, a.k, a.scale_log2, qf, o, m_run, l_run, lane);
+  const int n = fast_end > kb ? (fast_end - kb) / TK : 0;  // prefix tiles through the rings
+  if (tid == 0) ovf_flag = 0;  // published by the first barrier below
+  DmaPlan<D> plan;
+  dma_plan<D>(plan, wave, lane);
+  auto kslot = [&](int j) { return sK0 + (j & (RING - 1)) * T::K_BYTES; };
+  auto vslot = [&](int j) { return sV0 + (j & (RING - 1)) * T::V_BYTES; };
+  // ring prologue: K(0); K(1), V(0); K(2), V(1)
+  if (n > 0) issue_k<D>(kslot(0), kc_base, plan, kb, wave);
+  if (n > 1) issue_k<D>(kslot(1), kc_base, plan, kb + TK, wave);
+  if (n > 0) issue_v<D>(vslot(0), vc_base, plan, kb, wave);
+  if (n > 2) issue_k<D>(kslot(2), kc_base, plan, kb + 2 * TK, wave);
+  if (n > 1) issue_v<D>(vslot(1), vc_base, plan, kb + TK, wave);
+
+  bf16x8 qf[NT][D / 32];
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    const int r = mrow[rt] / a.G, h = kvh * a.G + mrow[rt] % a.G;
+    const bf16* qrow = (const bf16*)a.q + ((size_t)(b * a.R + r) * a.Hq + h) * D;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      bf16x8 z = {};
+      qf[rt][c] = row_ok[rt] ? *(const bf16x8*)(qrow + 32 * c + 8 * hi) : z;
+    }
   }
-  // tiles reaching past the prefix: staged through registers, masked by zone
-  for (int t0 = max(kb, fast_end); t0 < ke; t0 += TK) {
+  floatx4 o[NT][D / 16];
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) o[rt][db] = (floatx4){0.f, 0.f, 0.f, 0.f};
+  float m_run[NT], l_run[NT], ps[NT];
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) { m_run[rt] = kNoMax; l_run[rt] = 0.f; }
+  const float sl2 = a.scale_log2;
+  floatx4 sA[NT][4], sB[NT][4];
+  bf16x8 pA[NT][2], pB[NT][2];
+
+  // Tiles reaching past the prefix: staged through registers into the
+  // fourth slots, masked by zone, softmax with the exact path.
+  auto tail_tiles = [&]() {
+    for (int t0 = max(kb, fast_end); t0 < ke; t0 += TK) {
+      lds_char* sK = kslot(RING - 1);
+      lds_char* sV = vslot(RING - 1);
+      barrier();
+      stage_tail_tile<D>(sK, sV, kc_base, vc_base, ks_base, vs_base, step_stride, t0, L, Ltot, tid);
+      wait_all();
+      barrier();
+      s_tile<D, NT>(sK, qf, sA, lane);
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+        const StepZone z = step_zone(mrow[rt] / a.G, a.k);
+#pragma unroll
+        for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int c = t0 + 32 * (kb4 >> 1) + 8 * hi + 4 * (kb4 & 1) + v;
+            // branch-free select: no divergent control flow around the
+            // vector element update
+            const bool vis = (c < ke) & z.sees(c - L);
+            sA[rt][kb4][v] = vis ? sA[rt][kb4][v] : -INFINITY;
+          }
+      }
+      const bool big = sm_tile<NT>(sA, pA, ps, m_run, sl2);
+      softmax_commit<D, NT>(big, sA, pA, ps, m_run, l_run, o, sl2);
+      pv_tile<D, NT>(sV, pA, o, lane);
+      wait_lgkmcnt0();
+    }
+  };
+  tail_tiles();
+
+  if (n > 0) {
+    // Tile 0 is scored and its softmax taken with the exact path, so every
+    // row's reference is a true max of fully visible keys before the
+    // pipelined loop.  Inside the loop a reference is never moved: a tile
+    // whose sum of p passes 2^64 (scores 64 above the reference, in log2
+    // units) raises the workgroup's overflow flag, and the chunk is then
+    // recomputed tile by tile with the exact path.
+    if (n > 2) wait_vmcnt<2 * T::NKW + 2 * T::NVW>();
+    else if (n > 1) wait_vmcnt<T::NKW + 2 * T::NVW>();
+    else wait_vmcnt<T::NVW>();
+    barrier();
+    s_tile<D, NT>(kslot(0), qf, sA, lane);
+    {
+      const bool big = sm_tile<NT>(sA, pA, ps, m_run, sl2);
+      softmax_commit<D, NT>(big, sA, pA, ps, m_run, l_run, o, sl2);
+    }
+
+    // Iteration t: wait until only V(t), K(t+2), V(t+1) may be in flight.
+    auto sync = [&](int it) {
+      if (it + 2 < n) wait_vmcnt<T::NKW + 2 * T::NVW>();
+      else if (it + 1 < n) wait_vmcnt<2 * T::NVW>();
+      else wait_vmcnt<T::NVW>();
+      wait_lgkmcnt0();
+      barrier();
+      if (it + 3 < n) issue_k<D>(kslot(it + 3), kc_base, plan, kb + (it + 3) * TK, wave);
+      if (it + 2 < n) issue_v<D>(vslot(it + 2), vc_base, plan, kb + (it + 2) * TK, wave);
+    };
+    bool overflow = false;
+    auto commit_sum = [&](bool big) {
+      overflow |= __any(big);
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) l_run[rt] += ps[rt];
+    };
+    if (n > 1) {  // t = 0: scores(1)
+      sync(0);
+      s_tile<D, NT>(kslot(1), qf, sB, lane);
+    }
+    // iteration t: softmax(t) | scores(t+1) | P.V(t-1); the scores after
+    // the last tile come from a stale slot and are never used
+    int it = 1;
+    for (; it + 1 < n; it += 2) {
+      sync(it);
+      commit_sum(pipe_body<D, NT, true, true>(kslot(it + 1), vslot(it - 1), qf, sA, sB, pB, pA, o, ps, m_run, sl2,
+                                              lane));
+      sync(it + 1);
+      commit_sum(pipe_body<D, NT, true, true>(kslot(it + 2), vslot(it), qf, sB, sA, pA, pB, o, ps, m_run, sl2,
+                                              lane));
+    }
+    if (it < n) {  // odd last tile: softmax(n-1) in sB
+      sync(it);
+      commit_sum(pipe_body<D, NT, false, true>(kslot(it), vslot(it - 1), qf, sA, sB, pB, pA, o, ps, m_run, sl2,
+                                               lane));
+    }
+    if (overflow) ovf_flag = 1;
     wait_all();
-    __builtin_amdgcn_s_barrier();
-    stage_tail_tile<D, NW>(sK0, sV0, kc_base, vc_base, ks_base, vs_base, step_stride, t0, L, Ltot, tid);
-    wait_all();
-    __builtin_amdgcn_s_barrier();
-    compute_tile<D, true>(sK0, sV0, t0, L, ke, r, a.k, a.scale_log2, qf, o, m_run, l_run, lane);
+    barrier();
+    pv_tile<D, NT>(vslot(n - 1), ((n - 1) & 1) ? pB : pA, o, lane);
+
+    if (ovf_flag) {  // the same for every wave after the barrier
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+        m_run[rt] = kNoMax;
+        l_run[rt] = 0.f;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) o[rt][db] = (floatx4){0.f, 0.f, 0.f, 0.f};
+      }
+      for (int j = 0; j < n; ++j) {
+        barrier();
+        issue_k<D>(kslot(0), kc_base, plan, kb + j * TK, wave);
+        issue_v<D>(vslot(0), vc_base, plan, kb + j * TK, wave);
+        wait_vmcnt<0>();
+        barrier();
+        s_tile<D, NT>(kslot(0), qf, sA, lane);
+        const bool big = sm_tile<NT>(sA, pA, ps, m_run, sl2);
+        softmax_commit<D, NT>(big, sA, pA, ps, m_run, l_run, o, sl2);
+        pv_tile<D, NT>(vslot(0), pA, o, lane);
+        wait_lgkmcnt0();
+      }
+      tail_tiles();
+    }
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!row_ok) return;
-  if (n_valid > 1) {  // one chunk of several: publish it for the merge kernel
-    const size_t prow = (pair * a.n_split + split) * a.M + m;
-    float* op = a.o_part + prow * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int rt = 0; rt < NT; ++rt) {
+    float lt = l_run[rt];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    if (!row_ok[rt]) continue;
+    const int m = mrow[rt];
+    const int r = m / a.G, h = kvh * a.G + m % a.G;
+    if (n_valid > 1) {  // one chunk of several: publish it for the merge kernel
+      const size_t prow = (pair * a.n_split + split) * a.M + m;
+      float* op = a.o_part + prow * D;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        floatx4 w;
+      for (int db = 0; db < D / 16; ++db) *(floatx4*)(op + 16 * db + 4 * hi) = o[rt][db];
+      if (hi == 0) a.ml_part[prow] = make_float2(m_run[rt], lt);
+      continue;
+    }
+    bf16* orow = (bf16*)a.out + ((size_t)(b * a.R + r) * a.Hq + h) * D;
+    const float inv = 1.f / lt;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = o[db][4 * g4 + e];
-        *(floatx4*)(op + 32 * db + 8 * g4 + 4 * half) = w;
-      }
-    if (half == 0) a.ml_part[prow] = make_float2(m_run, l_tot);
-    return;
-  }
-  const float inv = 1.f / l_tot;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
+    for (int db = 0; db < D / 16; ++db) {
       typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
       bf16x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (bf16)(o[db][4 * g4 + e] * inv);
-      *(bf16x4*)(orow + 32 * db + 8 * g4 + 4 * half) = w;
+      for (int v = 0; v < 4; ++v) w[v] = (bf16)(o[rt][db][v] * inv);
+      *(bf16x4*)(orow + 16 * db + 4 * hi) = w;
     }
-  if (a.lse && half == 0) a.lse[((size_t)b * a.Hq + h) * a.R + r] = (m_run + log2f(l_tot)) * kLn2;
+    if (a.lse && hi == 0) a.lse[((size_t)b * a.Hq + h) * a.R + r] = (m_run[rt] + log2f(lt)) * kLn2;
+  }
 }
-
 
 // f32 instance: one wave per (b, kvh, chunk, query row).  Lanes first take
 // keys (scores into LDS), then head-dim elements (P.V).  chunk <= 1024.
@@ -554,10 +812,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   if (lse && lane == 0) *lse = (mx + log2f(den)) * kLn2;
 }
 
-template <int D, int NW>
-hipError_t launch_bf16_split(const AttnArgs& a, hipStream_t s) {
+template <int D, int NT>
+hipError_t launch_bf16_pipe(const AttnArgs& a, hipStream_t s) {
   const int nblk = a.B * a.Hkv * a.n_split * a.n_rowblk;
-  hipLaunchKernelGGL((attn_split_bf16_kernel<D, NW>), dim3(nblk), dim3(NW * 64), 0, s, a);
+  hipLaunchKernelGGL((attn_pipe_bf16_kernel<D, NT>), dim3(nblk), dim3(NWV * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -574,18 +832,16 @@ hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
   hipError_t e = hipErrorInvalidValue;
   if (a.D == 128) {
-    switch (a.waves) {
-      case 1: e = launch_bf16_split<128, 1>(a, s); break;
-      case 2: e = launch_bf16_split<128, 2>(a, s); break;
-      case 3: e = launch_bf16_split<128, 3>(a, s); break;
-      case 4: e = launch_bf16_split<128, 4>(a, s); break;
+    switch (a.nt) {
+      case 1: e = launch_bf16_pipe<128, 1>(a, s); break;
+      case 2: e = launch_bf16_pipe<128, 2>(a, s); break;
+      case 3: e = launch_bf16_pipe<128, 3>(a, s); break;
     }
   } else if (a.D == 64) {
-    switch (a.waves) {
-      case 1: e = launch_bf16_split<64, 1>(a, s); break;
-      case 2: e = launch_bf16_split<64, 2>(a, s); break;
-      case 3: e = launch_bf16_split<64, 3>(a, s); break;
-      case 4: e = launch_bf16_split<64, 4>(a, s); break;
+    switch (a.nt) {
+      case 1: e = launch_bf16_pipe<64, 1>(a, s); break;
+      case 2: e = launch_bf16_pipe<64, 2>(a, s); break;
+      case 3: e = launch_bf16_pipe<64, 3>(a, s); break;
     }
   }
   if (e != hipSuccess || a.n_split == 1) return e;

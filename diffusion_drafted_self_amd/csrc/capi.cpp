@@ -18,23 +18,31 @@ constexpr int kTileKeys = 64;           // keys per attention tile
 constexpr int kValuePage = 64;          // positions per value-cache page
 constexpr int kMaxChunkF32 = 1024;      // LDS score buffer of the f32 kernel
 constexpr int kVerifyChunk = 4096;      // logits per argmax workgroup
-constexpr long kTargetWorkgroups = 512;      // two per CU on 256 CUs
-constexpr long kSingleChunkWorkgroups = 192; // three quarters of the CUs busy without splitting keys
+constexpr int kCUs = 256;               // compute units of the part
+constexpr int kMaxRowTilesPerWave = 3;  // 16-row tiles a bf16 wave can hold in registers
 
 bool aligned(const void* p, uintptr_t a) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 long cdiv(long a, long b) { return (a + b - 1) / b; }
 
 struct AttnPlan {
-  int R, G, M, waves, n_rowblk, chunk, n_split;
-  size_t cnt_bytes, o_bytes, ml_bytes, total;
+  int R, G, M, n16, nt, n_rowblk, chunk, n_split;
+  size_t o_bytes, ml_bytes, total;
 };
 
-// Split plan of the step attention.  Rows of one (b, kvh): M = R*G in
-// 32-row MFMA tiles; a workgroup takes `waves` tiles, picked to leave the
-// fewest padding waves.  Keys: `chunk` positions per workgroup, chosen so
-// the grid holds about kTargetWorkgroups workgroups but chunks stay >= 256
-// keys (each chunk's partial output costs M*(D+2)*4 bytes of traffic).
+// Split plan of the step attention.
+//
+// bf16: the M = R*G query rows of one (b, kvh) form n16 tiles of 16 rows; a
+// workgroup (four waves, one per SIMD, one workgroup per CU) takes a
+// contiguous share of them for one key chunk, each wave at most nt <= 3
+// tiles.  Candidates (row workgroups per (b, kvh), key chunks) are scored in
+// units of one 64-key tile for one 16-row tile (~512 MFMA cycles): the
+// slowest wave's tiles per round of kCUs workgroups, the HBM floor of the
+// stream, a fixed cost per round, and for several chunks the partial
+// outputs (M*(D+2)*4 bytes per chunk, written and read back) plus the merge
+// launch.
+//
+// f32: one wave per query row and chunk, chunks of at most kMaxChunkF32.
 int plan_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_len, int k,
                    int n_groups, int kv_chunk, AttnPlan* p) {
   if (dtype != TIDAR_BF16 && dtype != TIDAR_F32) return TIDAR_EUNSUPPORTED;
@@ -49,48 +57,59 @@ int plan_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_
   p->R = k + n_groups * k;
   p->G = Hq / Hkv;
   p->M = p->R * p->G;
+  p->n16 = (int)cdiv(p->M, 16);
   const long keys = (long)max_len + p->R;
+  const long pairs = std::max<long>(1, (long)B * Hkv);
 
-  // waves per workgroup: the largest of 4, 3, 2, 1 whose padding wastes at
-  // most 1/16 of the MFMA tiles (else the least padding)
-  const int n_tiles = (int)cdiv(p->M, 32);
-  int best_w = 1, best_pad = 1 << 30;
-  for (int w = 4; w >= 1; --w) {
-    const int pad = (int)cdiv(n_tiles, w) * w - n_tiles;
-    if (pad * 16 <= n_tiles) { best_w = w; best_pad = pad; break; }
-    if (pad < best_pad) { best_pad = pad; best_w = w; }
-  }
-  p->waves = best_w;
-  p->n_rowblk = (int)cdiv(n_tiles, best_w);
-
-  // key chunks: one chunk per (b, kvh, row block) whenever that already
-  // gives most CUs a workgroup -- every extra chunk costs a partial output
-  // of M*(D+2)*4 bytes written and read back -- else enough chunks to reach
-  // about kTargetWorkgroups workgroups, each at least 256 keys
-  long chunk = kv_chunk;
-  if (chunk == 0) {
-    if (dtype == TIDAR_F32) {
-      chunk = std::min<long>(kMaxChunkF32, (long)round_up(keys, kTileKeys));
-    } else {
-      const long base = std::max<long>(1, (long)B * Hkv * p->n_rowblk);
-      long n_split = base >= kSingleChunkWorkgroups ? 1 : cdiv(kTargetWorkgroups, base);
-      n_split = std::max<long>(1, std::min<long>(n_split, cdiv(keys, 256)));
-      chunk = (long)round_up(cdiv(keys, n_split), kTileKeys);
+  if (dtype == TIDAR_F32) {
+    p->chunk = kv_chunk ? kv_chunk : (int)std::min<long>(kMaxChunkF32, (long)round_up(keys, kTileKeys));
+    p->nt = 1;
+    p->n_rowblk = 1;
+  } else {
+    const long n_key_tiles = cdiv(keys, kTileKeys);
+    const double hbm_units = (double)pairs * keys * D * 4 / 1.3e6;  // K+V bytes at ~6 TB/s, 0.22 us units
+    double best = 1e300;
+    long best_chunk = 0;
+    int best_wr = 1, best_nt = 1;
+    long best_wgs = 0;
+    const long ns_max = kv_chunk ? 1 : std::min<long>(n_key_tiles, 64);
+    for (long ns_try = 1; ns_try <= ns_max; ++ns_try) {
+      const long chunk = kv_chunk ? kv_chunk : (long)round_up(cdiv(keys, ns_try), kTileKeys);
+      const long ns = cdiv(keys, chunk);
+      if (ns != ns_try && !kv_chunk) continue;  // the same chunk as a smaller count
+      const long kt = cdiv(chunk, kTileKeys) + 1;  // + the step tile staged through registers
+      for (int wr = 1; wr <= p->n16; ++wr) {
+        const int per_wave = (int)cdiv(cdiv(p->n16, wr), 4);
+        if (per_wave > kMaxRowTilesPerWave) continue;
+        const long wgs = pairs * wr * ns;
+        const long rounds = cdiv(wgs, kCUs);
+        double cost = std::max((double)rounds * per_wave * kt, hbm_units) + 10.0 * rounds;
+        if (ns > 1) cost += 14.0 + (double)pairs * ns * p->M * (D * 4 + 8) * 2 / 1.1e6;
+        const bool better = cost < best * 0.999 || (cost <= best * 1.001 && wgs > best_wgs && wgs <= rounds * kCUs);
+        if (better) {
+          best = cost;
+          best_chunk = chunk;
+          best_wr = wr;
+          best_nt = per_wave;
+          best_wgs = wgs;
+        }
+      }
     }
+    p->chunk = (int)best_chunk;
+    p->nt = best_nt;
+    p->n_rowblk = best_wr;
   }
-  p->chunk = (int)chunk;
-  p->n_split = (int)cdiv(keys, chunk);
+  p->n_split = (int)cdiv(keys, p->chunk);
 
-  const long blocks = (long)B * Hkv * p->n_split * (dtype == TIDAR_F32 ? p->M : p->n_rowblk);
+  const long blocks = pairs * p->n_split * (dtype == TIDAR_F32 ? p->M : p->n_rowblk);
   if (blocks > 0x7fffffffL) return TIDAR_EUNSUPPORTED;
 
   // workspace: [partial outputs][partial (max, sum)]; none is needed when
   // every sequence fits one chunk (bf16 path)
   const size_t parts = (dtype == TIDAR_F32 || p->n_split > 1) ? (size_t)B * Hkv * p->n_split * p->M : 0;
-  p->cnt_bytes = 0;
   p->o_bytes = round_up(parts * D * sizeof(float), 256);
   p->ml_bytes = round_up(parts * sizeof(float2), 256);
-  p->total = p->cnt_bytes + p->o_bytes + p->ml_bytes;
+  p->total = p->o_bytes + p->ml_bytes;
   return TIDAR_OK;
 }
 
@@ -165,8 +184,8 @@ int tidar_step_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, in
   a.out = out;
   a.lse = lse;
   char* ws = static_cast<char*>(workspace);
-  a.o_part = reinterpret_cast<float*>(ws + p.cnt_bytes);
-  a.ml_part = reinterpret_cast<float2*>(ws + p.cnt_bytes + p.o_bytes);
+  a.o_part = reinterpret_cast<float*>(ws);
+  a.ml_part = reinterpret_cast<float2*>(ws + p.o_bytes);
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
@@ -179,7 +198,8 @@ int tidar_step_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, in
   a.M = p.M;
   a.chunk = p.chunk;
   a.n_split = p.n_split;
-  a.waves = p.waves;
+  a.n16 = p.n16;
+  a.nt = p.nt;
   a.n_rowblk = p.n_rowblk;
   a.scale_log2 = sm_scale * 1.44269504088896340736f;
   a.single_chunk_direct = dtype == TIDAR_BF16;

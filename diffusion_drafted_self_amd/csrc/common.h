@@ -30,6 +30,19 @@ __device__ __forceinline__ bool step_visible(int r, int j, int k) {
   return (j - k) / k == g;
 }
 
+// The same zones per query row, for tests of many step rows j against one
+// row r: step rows [0, cand_last] and [slot_lo, slot_hi) are visible
+// (settled positions, j < 0, always are).
+struct StepZone {
+  int cand_last, slot_lo, slot_hi;
+  __device__ __forceinline__ bool sees(int j) const { return (j <= cand_last) | ((j >= slot_lo) & (j < slot_hi)); }
+};
+__device__ __forceinline__ StepZone step_zone(int r, int k) {
+  if (r < k) return {r, 0, 0};
+  const int g = (r - k) / k;
+  return {g, k + g * k, k + (g + 1) * k};
+}
+
 // Block index remap for a 8-XCD part: the hardware hands consecutive
 // workgroup ids round-robin to the XCDs, so ids i, i+8, i+16, ... share an
 // XCD (and its L2).  The returned logical id makes runs of consecutive

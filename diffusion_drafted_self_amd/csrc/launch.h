@@ -24,7 +24,7 @@ struct AttnArgs {
   float2* ml_part; // [B][Hkv][n_split][M]     (running max in log2 units, sum)
   int B, Hq, Hkv, G, D, S_max, max_len, k, R, M;
   int chunk, n_split;
-  int waves, n_rowblk;  // bf16 path: waves per workgroup, row blocks per (b, kvh)
+  int n16, nt, n_rowblk;  // bf16 path: 16-row tiles of (b, kvh), tiles per wave, workgroups per (b, kvh)
   float scale_log2;     // sm_scale * log2(e)
   int single_chunk_direct;  // the split kernel writes sequences that fit one chunk (bf16 path)
 };
