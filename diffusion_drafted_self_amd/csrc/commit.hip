@@ -5,60 +5,88 @@
 // autorégressive", nodesdaily.com, paragraph on the three zones; "KV Cache"
 // section of "TiDAR: Think in Diffusion, Talk in Autoregression",
 // mauroscia.it).  One workgroup per sequence appends the a accepted
-// candidate rows (step rows 0..a-1) at positions lens..lens+a-1 -- keys as
-// 16 B row copies, values transposed into their 64-position value page -- then
+// candidate rows (step rows 0..a-1) at positions lens..lens+a-1 -- keys into
+// their rows, values transposed into their 64-position value page -- then
 // advances lens in place.  Rejected candidates and slot rows are evicted by
 // never being written.  The work is a few KB per sequence: latency-bound.
 #include "common.h"
 #include "launch.h"
 
+#include <algorithm>
+
 namespace tidar {
 
 namespace {
 
-__global__ __launch_bounds__(256) void kv_commit_kernel(CommitArgs a) {
+// One workgroup per sequence.  The k candidate rows of keys and values are
+// loaded in 16 B pieces before the accept length and settled length are
+// known (step rows 0..k-1 always exist), so the kernel waits for memory
+// once; then every thread stores its key piece into the cache row and
+// scatters its value piece (PER consecutive head-dim elements of one
+// position) into PER value-page rows.  The settled length moves after a
+// barrier that only orders it behind every thread's read of the old value.
+template <typename E, int D>
+__global__ __launch_bounds__(1024) void kv_commit_kernel(CommitArgs a) {
+  constexpr int PER = 16 / sizeof(E);  // elements per 16 B piece
+  constexpr int PPR = D / PER;         // pieces per row
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int kSlots = 2;            // pieces per thread and tensor held at once
   const int b = blockIdx.x;
-  const int tid = threadIdx.x;
   const int acc = a.accept_len[b];
   const int L = a.lens[b];
+  const int n_piece = a.Hkv * a.k * PPR;  // per tensor: (candidate row, head, piece)
+  const size_t row_stride = (size_t)a.Hkv * D;
+  const E* ks = (const E*)a.k_step + (size_t)b * a.R * row_stride;
+  const E* vs = (const E*)a.v_step + (size_t)b * a.R * row_stride;
+
+  for (int p0 = threadIdx.x; p0 < n_piece; p0 += kSlots * blockDim.x) {
+    u32x4 kp[kSlots], vp[kSlots];
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+      const int p = p0 + u * blockDim.x;
+      if (p < n_piece) {  // p = (i * Hkv + h) * PPR + c: row i's head h, piece c
+        kp[u] = *(const u32x4*)(ks + (size_t)p * PER);
+        vp[u] = *(const u32x4*)(vs + (size_t)p * PER);
+      }
+    }
+    const int flag = (acc < 0 || acc > a.k) ? 2 : ((L < 0 || L + acc > a.S_max) ? 1 : 0);
+    if (flag) break;
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+      const int p = p0 + u * blockDim.x;
+      if (p >= n_piece) continue;
+      const int c = p % PPR, ih = p / PPR;
+      const int h = ih % a.Hkv, i = ih / a.Hkv;
+      if (i >= acc) continue;
+      const int pos = L + i;
+      E* dk = (E*)a.k_cache + (((size_t)b * a.Hkv + h) * a.S_max + pos) * D + c * PER;
+      *(u32x4*)dk = kp[u];
+      E* dv = (E*)a.v_cache + ((size_t)b * a.Hkv + h) * a.S_max * D + (size_t)(pos / 64) * D * 64 + pos % 64;
+      const E* ve = (const E*)&vp[u];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) dv[(size_t)(c * PER + j) * 64] = ve[j];
+    }
+  }
   const int flag = (acc < 0 || acc > a.k) ? 2 : ((L < 0 || L + acc > a.S_max) ? 1 : 0);
-  if (tid == 0 && a.err_flags) a.err_flags[b] = flag;
-  if (flag) return;
-
-  const int esz = a.elem_bytes;
-  const int cpr = a.D * esz / 16;  // 16 B chunks per key row
-  const char* ks = (const char*)a.k_step;
-  char* kc = (char*)a.k_cache;
-  const int nk = a.Hkv * acc * cpr;
-  for (int id = tid; id < nk; id += 256) {
-    const int h = id / (acc * cpr);
-    const int rem = id % (acc * cpr);
-    const int i = rem / cpr, c = rem % cpr;
-    const size_t src = (((size_t)b * a.R + i) * a.Hkv + h) * a.D * esz + 16 * c;
-    const size_t dst = (((size_t)b * a.Hkv + h) * a.S_max + L + i) * a.D * esz + 16 * c;
-    *(uint4*)(kc + dst) = *(const uint4*)(ks + src);
-  }
-
-  const int nv = a.Hkv * a.D * acc;
-  for (int id = tid; id < nv; id += 256) {
-    const int h = id / (a.D * acc);
-    const int rem = id % (a.D * acc);
-    const int d = rem / acc, i = rem % acc;
-    const size_t src = (((size_t)b * a.R + i) * a.Hkv + h) * a.D + d;
-    const int pos = L + i;
-    const size_t dst = ((size_t)b * a.Hkv + h) * a.S_max * a.D + (size_t)(pos / 64) * a.D * 64 + d * 64 + pos % 64;
-    if (esz == 2) ((uint16_t*)a.v_cache)[dst] = ((const uint16_t*)a.v_step)[src];
-    else ((uint32_t*)a.v_cache)[dst] = ((const uint32_t*)a.v_step)[src];
-  }
-  __syncthreads();  // every thread has read lens[b] before it moves
-  if (tid == 0) a.lens[b] = L + acc;
+  if (threadIdx.x == 0 && a.err_flags) a.err_flags[b] = flag;
+  __builtin_amdgcn_s_barrier();  // every thread has read lens[b]
+  if (threadIdx.x == 0 && !flag) a.lens[b] = L + acc;
 }
 
 }  // namespace
 
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
-  hipLaunchKernelGGL(kv_commit_kernel, dim3(a.B), dim3(256), 0, s, a);
+  const int pieces = a.Hkv * a.k * a.D * a.elem_bytes / 16;
+  const int threads = std::min(1024, std::max(64, ((pieces + 63) / 64) * 64));
+  if (a.elem_bytes == 2) {
+    if (a.D == 128) hipLaunchKernelGGL((kv_commit_kernel<uint16_t, 128>), dim3(a.B), dim3(threads), 0, s, a);
+    else hipLaunchKernelGGL((kv_commit_kernel<uint16_t, 64>), dim3(a.B), dim3(threads), 0, s, a);
+    // (bf16 elements move as raw 16-bit words)
+  } else {
+    if (a.D == 128) hipLaunchKernelGGL((kv_commit_kernel<uint32_t, 128>), dim3(a.B), dim3(threads), 0, s, a);
+    else hipLaunchKernelGGL((kv_commit_kernel<uint32_t, 64>), dim3(a.B), dim3(threads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -9,12 +9,14 @@
 //   argmax_partial_kernel<false>  (chunk, AR row): 16 B loads, per-thread
 //       (value, index) with strict '>' (indices ascend inside a thread, so
 //       the lowest index wins ties), wave shuffles, then LDS across waves.
-//   verify_select_kernel   one wave per sequence: reduces each AR row's
-//       chunk results in order i = 0..k and stops at the first mismatch:
-//       accept length, bonus token, draft group.
+//   verify_select_kernel   one workgroup per sequence, one wave per AR row:
+//       each wave reduces its row's chunk results, then the first mismatch
+//       is taken by a ballot: accept length, bonus token, draft group.
 //   argmax_partial_kernel<true>   the selected group's draft rows 1..k-1.
-//   draft_finalize_kernel  one wave per sequence: the next drafts.
+//   draft_finalize_kernel  one workgroup per sequence, one wave per draft
+//       row: the next drafts.
 // Ties compare as (value, lower index); -0.0 == +0.0 by IEEE compare.
+#include <algorithm>
 #include <climits>
 
 #include "common.h"
@@ -54,7 +56,7 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(VerifyArgs a) {
   } else {
     const int b = row / (a.k - 1);
     const int mm = 1 + row % (a.k - 1);
-    const int g = a.group[b];
+    const int g = min(max(a.group[b], 0), a.k - 1);  // written by verify_select_kernel; clamped regardless
     src = a.draft_logits + (((size_t)b * a.k + g) * a.k + mm) * a.V;
     dst = a.part_draft + (size_t)row * a.n_chunks + chunk;
   }
@@ -93,7 +95,13 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(VerifyArgs a) {
   }
 }
 
-// Reduce the chunk results of one row; every lane returns the row argmax.
+// One wave per row: the wave reduces that row's chunk results (one round
+// of loads, one shuffle tree); the rows of a sequence run in parallel and
+// meet in LDS.  A workgroup has at most kMaxWaves waves; with more rows a
+// wave takes rows w, w + kMaxWaves, ...
+constexpr int kMaxRows = 17;   // k + 1 for the largest k
+constexpr int kMaxWaves = 16;  // 1024 threads
+
 __device__ __forceinline__ int reduce_row(const float2* part, int n_chunks) {
   const int lane = threadIdx.x & 63;
   float bv = -INFINITY;
@@ -110,43 +118,57 @@ __device__ __forceinline__ int reduce_row(const float2* part, int n_chunks) {
   return bi;
 }
 
-__global__ __launch_bounds__(64) void verify_select_kernel(VerifyArgs a) {
+// block: min(k+1, kMaxWaves) waves over the k+1 AR rows of sequence blockIdx.x
+__global__ __launch_bounds__(64 * kMaxWaves) void verify_select_kernel(VerifyArgs a) {
+  __shared__ int t_row[kMaxRows];
   const int b = blockIdx.x;
-  int acc = 0, bonus = 0;
-  for (int i = 0; i <= a.k; ++i) {
-    const int t = reduce_row(a.part_ar + ((size_t)b * (a.k + 1) + i) * a.n_chunks, a.n_chunks);
-    if (i < a.k && a.cand[(size_t)b * a.k + i] == t) {
-      ++acc;
-    } else {
-      bonus = t;
-      break;
-    }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int row = wave; row <= a.k; row += nw) {
+    const int t = reduce_row(a.part_ar + ((size_t)b * (a.k + 1) + row) * a.n_chunks, a.n_chunks);
+    if (lane == 0) t_row[row] = t;
   }
-  if (threadIdx.x == 0) {
-    a.accept_len[b] = acc;
-    a.next_cand[(size_t)b * a.k] = bonus;
-    a.group[b] = (acc > 0 ? acc : 1) - 1;
+  __syncthreads();
+  const int row = wave;
+  if (row == 0) {
+    // the accepted length is the first i < k with cand[i] != t_i (k if none)
+    const bool miss = lane < a.k && a.cand[(size_t)b * a.k + lane] != t_row[lane];
+    const unsigned long long mm = __ballot(miss || lane == a.k);
+    const int acc = __ffsll((long long)mm) - 1;
+    if (lane == 0) {
+      a.accept_len[b] = acc;
+      a.next_cand[(size_t)b * a.k] = t_row[acc];
+      a.group[b] = (acc > 0 ? acc : 1) - 1;
+    }
   }
 }
 
-__global__ __launch_bounds__(64) void draft_finalize_kernel(VerifyArgs a) {
+// block: min(k-1, kMaxWaves) waves over the k-1 draft rows of sequence blockIdx.x
+__global__ __launch_bounds__(64 * kMaxWaves) void draft_finalize_kernel(VerifyArgs a) {
   const int b = blockIdx.x;
-  for (int mm = 1; mm < a.k; ++mm) {
-    const int t = reduce_row(a.part_draft + ((size_t)b * (a.k - 1) + (mm - 1)) * a.n_chunks, a.n_chunks);
-    if (threadIdx.x == 0) a.next_cand[(size_t)b * a.k + mm] = t;
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int row = wave; row < a.k - 1; row += nw) {
+    const int t = reduce_row(a.part_draft + ((size_t)b * (a.k - 1) + row) * a.n_chunks, a.n_chunks);
+    if ((threadIdx.x & 63) == 0) a.next_cand[(size_t)b * a.k + 1 + row] = t;
   }
 }
 
 }  // namespace
 
+// Each launch is checked before the next: the draft kernels index rows by
+// the group the selection writes.
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
+  if (a.k + 1 > kMaxRows) return hipErrorInvalidValue;
   hipLaunchKernelGGL(argmax_partial_kernel<false>, dim3(a.n_chunks, a.B * (a.k + 1)), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(verify_select_kernel, dim3(a.B), dim3(64), 0, s, a);
-  if (a.k > 1) {
-    hipLaunchKernelGGL(argmax_partial_kernel<true>, dim3(a.n_chunks, a.B * (a.k - 1)), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(draft_finalize_kernel, dim3(a.B), dim3(64), 0, s, a);
-  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(verify_select_kernel, dim3(a.B), dim3(64 * std::min(a.k + 1, kMaxWaves)), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.k == 1) return e;
+  hipLaunchKernelGGL(argmax_partial_kernel<true>, dim3(a.n_chunks, a.B * (a.k - 1)), dim3(256), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(draft_finalize_kernel, dim3(a.B), dim3(64 * std::min(a.k - 1, kMaxWaves)), 0, s, a);
   return hipGetLastError();
 }
 
