@@ -11,12 +11,13 @@
 // paragraph on masking; abstract on fugumt.com).
 //
 // Kernels
-//   attn_pipe_bf16_kernel<D, NT>  one workgroup per CU: four waves, one per
-//       SIMD, each owning up to NT tiles of 16 query rows of one (b, kvh),
-//       against one key chunk.  Per 64-key tile, K and V^T arrive in LDS
+//   attn_pipe_bf16_kernel<D, NF, NS>  one workgroup per CU: four waves, one
+//       per SIMD, each owning NF tiles of 16 query rows of one (b, kvh) and
+//       one 16-key block of each of NS tiles they share, against one key
+//       chunk.  Per 64-key tile, K and V^T arrive in LDS
 //       rings by direct loads issued two and three tiles ahead; scores
 //       S^T = K.Q^T and O^T += V^T.P^T run on v_mfma_f32_16x16x32_bf16, each
-//       K / V^T operand read once from LDS and reused by the NT row tiles.
+//       K / V^T operand read once from LDS and reused by the row tiles.
 //       The loop body holds the softmax of tile t, the scores of tile t+1
 //       and the P.V product of tile t-1, three independent streams in one
 //       basic block, so the exp2 work of the VALU runs under the MFMAs.
@@ -53,9 +54,8 @@ __device__ __forceinline__ size_t vpos(int d, int c, int D) {  // element (d, po
 // 16 B piece's position inside its row is permuted by an XOR swizzle chosen
 // by the source address each lane reads: logical piece p of K row `row` sits
 // at physical piece p ^ kswz(row), logical piece q of V^T row d at
-// q ^ vswz(d).  With these, the 16 lanes reading one MFMA operand column hit
-// distinct banks whether the LDS serves 8 or 16 lanes of a 16 B read per
-// cycle.
+// q ^ vswz(d).  With these the MFMA operand reads are free of bank
+// conflicts.
 template <int D>
 struct Tile {
   static constexpr int KROW = D * 2;        // bytes per K row
@@ -86,14 +86,18 @@ __device__ __forceinline__ int kswz(int row) {
   if constexpr (Tile<D>::KPPR == 16) return (row & 3) | ((row >> 1) & 12);
   else return ((row >> 1) & 1) | ((row >> 2) & 2) | (((row ^ (row >> 4)) & 1) << 2);
 }
-// V^T rows: 16 consecutive rows get distinct (row parity, piece) pairs and 8
-// consecutive rows distinct pieces.
-__device__ __forceinline__ int vswz(int d) { return (d & 7) ^ ((d >> 3) & 1); }
+// V^T rows: the piece index XOR the row's low three bits.  With the operand
+// read of O^T += V^T.P^T (16 consecutive rows, four consecutive pieces per
+// row across the four lane groups) this is free of bank conflicts on this
+// part, measured with the LDS bank-conflict counter; the variant that also
+// folded in bit 3 of the row conflicted on 40% of the active cycles.
+__device__ __forceinline__ int vswz(int d) { return d & 7; }
 
 // LDS pointers stay in address space 3 end to end (no generic casts)
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0]+[15:14], expcnt[6:4], lgkmcnt[11:8])
 template <int N>
@@ -204,12 +208,16 @@ __device__ __forceinline__ void stage_tail_tile(lds_char* sK, lds_char* sV, cons
   }
   wait_all();
   barrier();
-  // step rows: one 16 B load of 8 head-dim elements, scattered into 8 V^T rows
+  // step rows: one 16 B load of 8 head-dim elements, scattered into 8 V^T
+  // rows.  Consecutive lanes take consecutive keys, so each 2-byte store of
+  // a wave fills one V^T row across 64 columns (lanes on the same column
+  // would all hit one bank).
   const int j0 = max(t0, L), j1 = min(t0 + TK, Ltot);
-  for (int id = tid; id < (j1 - j0) * (D / 8); id += NWV * 64) {
-    const int c = j0 + id / (D / 8), dc = id % (D / 8);
+  for (int id = tid; id < TK * (D / 8); id += NWV * 64) {
+    const int cl = id % TK, dc = id / TK;
+    const int c = t0 + cl;
+    if (c < j0 || c >= j1) continue;
     const bf16x8 val = *(const bf16x8*)(vs_base + (size_t)(c - L) * step_stride + dc * 8);
-    const int cl = c - t0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int d = dc * 8 + e;
@@ -218,225 +226,329 @@ __device__ __forceinline__ void stage_tail_tile(lds_char* sK, lds_char* sV, cons
   }
 }
 
-// Running softmax state of one wave: per row tile, the reference max m (log2
-// units, shared by the four lanes holding a row) and this lane's part of the
-// sum l.  Scores are turned into p = exp2(scale_log2*s - m) against the
-// current m without looking for the tile's max: as long as every p stays
-// below 2^64 the fp32 sums and the bf16 P keep full relative precision (a
-// reference below the true max only scales them), so the tile's sum of p
-// decides.  When it exceeds 2^64 (always on a row's first tile, where m is
-// kNoMax) the wave takes the exact path: true tile max across the four
-// lanes of each row, rescale of O and l, p recomputed.
+// Row tiles of one wave.  A workgroup takes T tiles of 16 query rows of one
+// (b, kvh): each of its four waves owns NF "full" tiles, and the remaining
+// NS = T - 4*NF "shared" tiles are split by keys: wave w computes, for every
+// 64-key tile, only score block w (16 keys) of each shared tile, keeps its
+// own softmax state for that part, and the four parts are merged in LDS at
+// the end.  Every wave then does the same work, NF + NS/4 tiles, whatever T
+// is (T = 9: 2.25 tiles per wave instead of waves of 3 and 2 waiting for
+// each other at every barrier).
+//
+// Running softmax state per tile (per part for a shared tile): the
+// reference max m (log2 units, the same in the four lanes that hold a row)
+// and this lane's part of the sum l.  Scores become p = exp2(scale_log2*s -
+// m) against the current m without looking for the tile's max: while every
+// p stays below 2^64 the fp32 sums and the bf16 P keep full relative
+// precision (a reference below the true max only scales them), so a tile's
+// sum of p decides.  Above 2^64 (always on the first tile, where m is
+// kNoMax) the exact path runs: the true tile max across the four lanes of
+// each row, rescale of O and l, p recomputed.
 constexpr float kSumLimit = 18446744073709551616.0f;  // 2^64
 
-// p = exp2(scale_log2*s - m) against the current reference; returns true
-// when some row tile of this lane needs the exact path.
-template <int NT>
-__device__ __forceinline__ bool sm_tile(const floatx4 (&s)[NT][4], bf16x8 (&pk)[NT][2], float (&ps)[NT],
-                                        const float (&m)[NT], float scale_log2) {
+template <int N>
+constexpr int at_least_1() { return N > 0 ? N : 1; }
+
+template <int D, int NF, int NS>
+struct Acc {  // accumulators of one wave
+  floatx4 o[at_least_1<NF>()][D / 16];
+  floatx4 os[at_least_1<NS>()][D / 16];
+  float m[at_least_1<NF>()], l[at_least_1<NF>()];
+  float ms[at_least_1<NS>()], ls[at_least_1<NS>()];
+};
+template <int NF, int NS>
+struct Scores {
+  floatx4 s[at_least_1<NF>()][4];
+  floatx4 ss[at_least_1<NS>()];  // block w of each shared tile
+};
+template <int NF, int NS>
+struct Probs {
+  bf16x8 p[at_least_1<NF>()][2];  // P^T operands of the two 32-key steps
+  bf16x4 ps[at_least_1<NS>()];    // P^T operand of the 16 keys of block w
+  float sum[at_least_1<NF>()], sums[at_least_1<NS>()];
+};
+template <int D, int NF, int NS>
+struct QFrags {
+  bf16x8 f[at_least_1<NF>()][D / 32];
+  bf16x8 s[at_least_1<NS>()][D / 32];
+};
+
+// Operands of score block w and of the 16 keys of block w in P.V, read from
+// LDS for the shared tiles (the full tiles read theirs inside the steps).
+template <int D>
+__device__ __forceinline__ bf16x8 kfrag(const lds_char* sK, int kb4, int c, int lane) {
+  using T = Tile<D>;
+  const int i16 = lane & 15, hi = lane >> 4;
+  const int ksw = kswz<D>(krow_of(0, i16));  // the same for every block of the tile
+  return *(const lds_bf16x8*)(sK + krow_of(kb4, i16) * T::KROW + (((4 * c + hi) ^ ksw) * 16));
+}
+template <int D>
+__device__ __forceinline__ bf16x8 vfrag(const lds_char* sV, int db, int kc, int lane) {
+  using T = Tile<D>;
+  const int i16 = lane & 15, hi = lane >> 4;
+  return *(const lds_bf16x8*)(sV + (16 * db + i16) * T::VROW + (((4 * kc + hi) ^ vswz(i16)) * 16));
+}
+// keys 32*(w>>1) + 8*(lane>>4) + 4*(w&1) + 0..3 of V^T row 16*db + (lane&15):
+// with these the A operand of v_mfma_f32_16x16x16_bf16 holds, in its k order,
+// the keys whose p this lane holds from score block w
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+template <int D>
+__device__ __forceinline__ bf16x4 vfrag16(const lds_char* sV, int db, int w, int lane) {
+  using T = Tile<D>;
+  const int i16 = lane & 15, hi = lane >> 4;
+  return *(const lds_bf16x4*)(sV + (16 * db + i16) * T::VROW + (((4 * (w >> 1) + hi) ^ vswz(i16)) * 16) + 8 * (w & 1));
+}
+
+template <int NF, int NS>
+__device__ __forceinline__ void pair_to_p(Probs<NF, NS>& pr, bool shared, int t, int kb4, int v, float p0, float p1) {
+  // convert here: the empty asm pins the packed pair to this point, so the
+  // compiler cannot sink the conversion past the exact-path branch and keep
+  // 32-bit p values alive instead
+  unsigned u = __builtin_bit_cast(unsigned, (bf16x2){(bf16)p0, (bf16)p1});
+  asm volatile("" : "+v"(u));
+  const bf16x2 t2 = __builtin_bit_cast(bf16x2, u);
+  if (!shared) {
+    pr.p[t][kb4 >> 1][4 * (kb4 & 1) + v] = t2[0];
+    pr.p[t][kb4 >> 1][4 * (kb4 & 1) + v + 1] = t2[1];
+  } else {
+    pr.ps[t][v] = t2[0];
+    pr.ps[t][v + 1] = t2[1];
+  }
+}
+
+// Softmax element pair e of a wave (full tiles' pairs first, then the
+// shared parts'): p = exp2(scale_log2*s - m) against the held reference.
+template <int NF, int NS>
+__device__ __forceinline__ void sm_pair(int e, const Scores<NF, NS>& sc, Probs<NF, NS>& pr, const float* m,
+                                        const float* ms, float sl2) {
+  if (e < NF * 8) {
+    const int t = e / 8, kb4 = (e / 2) % 4, v = 2 * (e % 2);
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(sc.s[t][kb4][v], sl2, -m[t]));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(sc.s[t][kb4][v + 1], sl2, -m[t]));
+    pr.sum[t] += p0 + p1;
+    pair_to_p(pr, false, t, kb4, v, p0, p1);
+  } else {
+    const int t = (e - NF * 8) / 2, v = 2 * ((e - NF * 8) % 2);
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(sc.ss[t][v], sl2, -ms[t]));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(sc.ss[t][v + 1], sl2, -ms[t]));
+    pr.sums[t] += p0 + p1;
+    pair_to_p(pr, true, t, 0, v, p0, p1);
+  }
+}
+
+template <int NF, int NS>
+__device__ __forceinline__ void sums_zero(Probs<NF, NS>& pr) {
+#pragma unroll
+  for (int t = 0; t < NF; ++t) pr.sum[t] = 0.f;
+#pragma unroll
+  for (int t = 0; t < NS; ++t) pr.sums[t] = 0.f;
+}
+template <int NF, int NS>
+__device__ __forceinline__ bool sums_big(const Probs<NF, NS>& pr) {
   bool big = false;
 #pragma unroll
-  for (int rt = 0; rt < NT; ++rt) {
-    float sum = 0.f;
+  for (int t = 0; t < NF; ++t) big |= pr.sum[t] > kSumLimit;
 #pragma unroll
-    for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[rt][kb4][v], scale_log2, -m[rt]));
-        sum += p;
-        pk[rt][kb4 >> 1][4 * (kb4 & 1) + v] = (bf16)p;
-      }
-    ps[rt] = sum;
-    big |= sum > kSumLimit;
-  }
+  for (int t = 0; t < NS; ++t) big |= pr.sums[t] > kSumLimit;
   return big;
 }
-
-// Exact path: move each row's reference to the true running max, rescale
-// O and l, recompute p.
-template <int D, int NT>
-__device__ __forceinline__ void sm_exact(const floatx4 (&s)[NT][4], bf16x8 (&pk)[NT][2], float (&m)[NT], float (&l)[NT],
-                                      floatx4 (&o)[NT][D / 16], float scale_log2) {
+template <int D, int NF, int NS>
+__device__ __forceinline__ void sums_commit(const Probs<NF, NS>& pr, Acc<D, NF, NS>& ac) {
 #pragma unroll
-  for (int rt = 0; rt < NT; ++rt) {
-    float mx = -INFINITY;
+  for (int t = 0; t < NF; ++t) ac.l[t] += pr.sum[t];
 #pragma unroll
-    for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[rt][kb4][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m[rt], mx * scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m[rt] - m_new);
-    m[rt] = m_new;
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) o[rt][db][v] *= alpha;
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    float sum = 0.f;
-#pragma unroll
-    for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[rt][kb4][v], scale_log2, -m_new));
-        sum += p;
-        pk[rt][kb4 >> 1][4 * (kb4 & 1) + v] = (bf16)p;
-      }
-    l[rt] = l[rt] * alpha + sum;
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  for (int t = 0; t < NS; ++t) ac.ls[t] += pr.sums[t];
 }
 
-template <int D, int NT>
-__device__ __forceinline__ void softmax_commit(bool big, const floatx4 (&s)[NT][4], bf16x8 (&pk)[NT][2],
-                                               const float (&ps)[NT], float (&m)[NT], float (&l)[NT],
-                                               floatx4 (&o)[NT][D / 16], float scale_log2) {
-  if (__any(big)) {
-    sm_exact<D, NT>(s, pk, m, l, o, scale_log2);
-  } else {
+// Softmax of a whole tile against the held references (not pipelined).
+template <int D, int NF, int NS>
+__device__ __forceinline__ bool sm_tile(const Scores<NF, NS>& sc, Probs<NF, NS>& pr, const Acc<D, NF, NS>& ac,
+                                        float sl2) {
+  sums_zero(pr);
 #pragma unroll
-    for (int rt = 0; rt < NT; ++rt) l[rt] += ps[rt];
+  for (int e = 0; e < NF * 8 + NS * 2; ++e) sm_pair<NF, NS>(e, sc, pr, ac.m, ac.ms, sl2);
+  return sums_big(pr);
+}
+
+// Exact path for one row tile (or shared part): move each row's reference
+// to the true running max, rescale O and l, recompute p.
+template <int D, int NV>
+__device__ __forceinline__ float exact_ref(const float* s, float& m, float& l, floatx4 (&o)[D / 16], float sl2) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) mx = fmaxf(mx, s[v]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m, mx * sl2);
+  const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+  m = m_new;
+  l *= alpha;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) o[db][v] *= alpha;
+    __builtin_amdgcn_sched_barrier(0);
   }
+  return m_new;
+}
+
+template <int D, int NF, int NS>
+__device__ __forceinline__ void sm_exact(const Scores<NF, NS>& sc, Probs<NF, NS>& pr, Acc<D, NF, NS>& ac, float sl2) {
+#pragma unroll
+  for (int t = 0; t < NF; ++t) {
+    float sv[16];
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sv[4 * kb4 + v] = sc.s[t][kb4][v];
+    exact_ref<D, 16>(sv, ac.m[t], ac.l[t], ac.o[t], sl2);
+  }
+#pragma unroll
+  for (int t = 0; t < NS; ++t) {
+    float sv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sv[v] = sc.ss[t][v];
+    exact_ref<D, 4>(sv, ac.ms[t], ac.ls[t], ac.os[t], sl2);
+  }
+  sm_tile<D, NF, NS>(sc, pr, ac, sl2);
+  sums_commit(pr, ac);
+}
+
+template <int D, int NF, int NS>
+__device__ __forceinline__ void softmax_commit(bool big, const Scores<NF, NS>& sc, Probs<NF, NS>& pr,
+                                               Acc<D, NF, NS>& ac, float sl2) {
+  if (__any(big)) sm_exact<D, NF, NS>(sc, pr, ac, sl2);
+  else sums_commit(pr, ac);
 }
 
 template <int NT>
-constexpr int operand_depth() { return NT == 1 ? 4 : (NT == 2 ? 3 : 2); }
+constexpr int operand_depth() { return NT <= 1 ? 8 : (NT == 2 ? 6 : 4); }
 
 // One pipelined loop body: the scores of the next tile (S steps, one per
 // (head-dim step, 16-key block)), the P.V product of the previous tile (PV
 // steps, one per (32-key step, 16-row head-dim block)) and the softmax of
-// the current tile, issued as a fixed sequence of steps.  Each step runs NT
-// MFMAs on one LDS operand, reads the operand of the step DEPTH ahead and
-// takes its slice of the softmax elements; a scheduling fence after every
-// step keeps the exp2 work spread under the MFMAs and bounds the operands in
+// the current tile, issued as a fixed sequence of steps.  Each step runs
+// the full tiles' MFMAs on one LDS operand, reads the operand of the step
+// DEPTH ahead and takes its slice of the softmax elements; the shared
+// tiles' block-w MFMAs ride on the first steps of each kind (their
+// operands are read at the start).  A scheduling fence after every step
+// keeps the exp2 work spread under the MFMAs and bounds the operands in
 // flight.  Returns true when some lane's softmax needs the exact path.
-template <int D, int NT, bool DO_S, bool DO_PV>
-__device__ __forceinline__ bool pipe_body(const lds_char* sKn, const lds_char* sVp, const bf16x8 (&qf)[NT][D / 32],
-                                          floatx4 (&s_next)[NT][4], const floatx4 (&s_cur)[NT][4],
-                                          bf16x8 (&p_cur)[NT][2], const bf16x8 (&p_prev)[NT][2],
-                                          floatx4 (&o)[NT][D / 16], float (&ps)[NT], const float (&m)[NT],
-                                          float sl2, int lane) {
+template <int D, int NF, int NS, bool DO_S, bool DO_PV>
+__device__ __forceinline__ bool pipe_body(const lds_char* sKn, const lds_char* sVp, const QFrags<D, NF, NS>& q,
+                                          Scores<NF, NS>& s_next, const Scores<NF, NS>& s_cur,
+                                          Probs<NF, NS>& p_cur, const Probs<NF, NS>& p_prev,
+                                          Acc<D, NF, NS>& ac, float sl2, int lane, int w) {
   using T = Tile<D>;
-  constexpr int NS = DO_S ? T::NDC * 4 : 0;
-  constexpr int NP = DO_PV ? 2 * T::NDB : 0;
-  constexpr int NSTEP = NS + NP;
-  constexpr int NE = NT * 16;  // softmax elements of this lane
-  constexpr int DEPTH = operand_depth<NT>();
-  const int i16 = lane & 15, hi = lane >> 4;
-  const lds_char* kr = sKn + krow_of(0, i16) * T::KROW;
-  const int ksw = kswz<D>(krow_of(0, i16));
-  const lds_char* vr = sVp + i16 * T::VROW;
-  const int vsw = vswz(i16);
+  constexpr int NSS = DO_S ? T::NDC * 4 : 0;
+  constexpr int NPS = DO_PV ? 2 * T::NDB : 0;
+  constexpr int NSTEP = NSS + NPS;
+  constexpr int NE = NF * 8 + NS * 2;  // softmax element pairs of this lane
+  constexpr int DEPTH = operand_depth<NF>();
   auto frag = [&](int i) -> bf16x8 {
-    if (i < NS) {
-      const int c = i / 4, kb4 = i % 4;
-      return *(const lds_bf16x8*)(kr + krow_of(kb4, 0) * T::KROW + (((4 * c + hi) ^ ksw) * 16));
-    }
-    const int j = i - NS, kc = j / T::NDB, db = j % T::NDB;
-    return *(const lds_bf16x8*)(vr + db * 16 * T::VROW + (((4 * kc + hi) ^ vsw) * 16));
+    if (i < NSS) return kfrag<D>(sKn, i % 4, i / 4, lane);
+    const int j = i - NSS;
+    return vfrag<D>(sVp, j % T::NDB, j / T::NDB, lane);
   };
   const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+  bf16x8 ksh[T::NDC];   // shared tiles: K of block w, per head-dim step
+  bf16x4 vsh[T::NDB];   // shared tiles: V^T of block w's keys, per head-dim block
+  if (NS > 0) {
+#pragma unroll
+    for (int c = 0; c < T::NDC; ++c)
+      if (DO_S) ksh[c] = kfrag<D>(sKn, w, c, lane);
+#pragma unroll
+    for (int db = 0; db < T::NDB; ++db)
+      if (DO_PV) vsh[db] = vfrag16<D>(sVp, db, w, lane);
+  }
   bf16x8 fr[DEPTH + 1];
+  if (NF > 0) {
 #pragma unroll
-  for (int i = 0; i < DEPTH && i < NSTEP; ++i) fr[i] = frag(i);
-#pragma unroll
-  for (int rt = 0; rt < NT; ++rt) ps[rt] = 0.f;
+    for (int i = 0; i < DEPTH && i < NSTEP; ++i) fr[i] = frag(i);
+  }
+  sums_zero(p_cur);
 #pragma unroll
   for (int i = 0; i < NSTEP; ++i) {
-    if (i + DEPTH < NSTEP) fr[(i + DEPTH) % (DEPTH + 1)] = frag(i + DEPTH);
-    const bf16x8 f = fr[i % (DEPTH + 1)];
-    if (i < NS) {
+    if (NF > 0 && i + DEPTH < NSTEP) fr[(i + DEPTH) % (DEPTH + 1)] = frag(i + DEPTH);
+    if (i < NSS) {
       const int c = i / 4, kb4 = i % 4;
 #pragma unroll
-      for (int rt = 0; rt < NT; ++rt)
-        s_next[rt][kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, qf[rt][c], c == 0 ? z : s_next[rt][kb4], 0, 0, 0);
+      for (int t = 0; t < NF; ++t)
+        s_next.s[t][kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[i % (DEPTH + 1)], q.f[t][c],
+                                                                   c == 0 ? z : s_next.s[t][kb4], 0, 0, 0);
+      if (kb4 == 0) {
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+          s_next.ss[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ksh[c], q.s[t][c], c == 0 ? z : s_next.ss[t], 0, 0, 0);
+      }
     } else {
-      const int j = i - NS, kc = j / T::NDB, db = j % T::NDB;
+      const int j = i - NSS, kc = j / T::NDB, db = j % T::NDB;
 #pragma unroll
-      for (int rt = 0; rt < NT; ++rt)
-        o[rt][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, p_prev[rt][kc], o[rt][db], 0, 0, 0);
+      for (int t = 0; t < NF; ++t)
+        ac.o[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[i % (DEPTH + 1)], p_prev.p[t][kc], ac.o[t][db], 0, 0, 0);
+      if (kc == 0) {
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+          ac.os[t][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vsh[db], p_prev.ps[t], ac.os[t][db], 0, 0, 0);
+      }
     }
 #pragma unroll
-    for (int e = i * (NE / 2) / NSTEP; e < (i + 1) * (NE / 2) / NSTEP; ++e) {  // element pairs
-      const int rt = e / 8, kb4 = (e / 2) % 4, v = 2 * (e % 2);
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[rt][kb4][v], sl2, -m[rt]));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[rt][kb4][v + 1], sl2, -m[rt]));
-      ps[rt] += p0 + p1;
-      // convert here: the empty asm pins the packed pair to this step, so
-      // the compiler cannot sink the conversion past the exact-path branch
-      // and keep 32-bit p values alive instead
-      unsigned u = __builtin_bit_cast(unsigned, (bf16x2){(bf16)p0, (bf16)p1});
-      asm volatile("" : "+v"(u));
-      const bf16x2 t2 = __builtin_bit_cast(bf16x2, u);
-      p_cur[rt][kb4 >> 1][4 * (kb4 & 1) + v] = t2[0];
-      p_cur[rt][kb4 >> 1][4 * (kb4 & 1) + v + 1] = t2[1];
-    }
+    for (int e = i * NE / NSTEP; e < (i + 1) * NE / NSTEP; ++e) sm_pair<NF, NS>(e, s_cur, p_cur, ac.m, ac.ms, sl2);
     __builtin_amdgcn_sched_barrier(0);
   }
-  bool big = false;
-#pragma unroll
-  for (int rt = 0; rt < NT; ++rt) big |= ps[rt] > kSumLimit;
-  return big;
+  return sums_big(p_cur);
 }
 
-// Scores of one tile alone, and P.V of one tile alone, in the same fenced
-// step order (ring prologue, tiles past the prefix, last tile).
-template <int D, int NT>
-__device__ __forceinline__ void s_tile(const lds_char* sK, const bf16x8 (&qf)[NT][D / 32], floatx4 (&s)[NT][4],
-                                       int lane) {
+// Scores of one tile alone, and P.V of one tile alone (ring prologue, tiles
+// past the prefix, last tile, exact recompute).
+template <int D, int NF, int NS>
+__device__ __forceinline__ void s_tile(const lds_char* sK, const QFrags<D, NF, NS>& q, Scores<NF, NS>& s, int lane,
+                                       int w) {
   using T = Tile<D>;
-  constexpr int NSTEP = T::NDC * 4;
-  constexpr int DEPTH = operand_depth<NT>();
-  const int i16 = lane & 15, hi = lane >> 4;
-  const lds_char* kr = sK + krow_of(0, i16) * T::KROW;
-  const int ksw = kswz<D>(krow_of(0, i16));
-  auto frag = [&](int i) -> bf16x8 {
-    const int c = i / 4, kb4 = i % 4;
-    return *(const lds_bf16x8*)(kr + krow_of(kb4, 0) * T::KROW + (((4 * c + hi) ^ ksw) * 16));
-  };
   const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-  bf16x8 fr[DEPTH + 1];
 #pragma unroll
-  for (int i = 0; i < DEPTH; ++i) fr[i] = frag(i);
+  for (int c = 0; c < T::NDC; ++c) {
 #pragma unroll
-  for (int i = 0; i < NSTEP; ++i) {
-    if (i + DEPTH < NSTEP) fr[(i + DEPTH) % (DEPTH + 1)] = frag(i + DEPTH);
-    const int c = i / 4, kb4 = i % 4;
+    for (int kb4 = 0; kb4 < 4; ++kb4) {
+      if (NF > 0) {
+        const bf16x8 kf = kfrag<D>(sK, kb4, c, lane);
 #pragma unroll
-    for (int rt = 0; rt < NT; ++rt)
-      s[rt][kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[i % (DEPTH + 1)], qf[rt][c], c == 0 ? z : s[rt][kb4],
-                                                           0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+        for (int t = 0; t < NF; ++t)
+          s.s[t][kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, q.f[t][c], c == 0 ? z : s.s[t][kb4], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (NS > 0) {
+      const bf16x8 kf = kfrag<D>(sK, w, c, lane);
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+        s.ss[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, q.s[t][c], c == 0 ? z : s.ss[t], 0, 0, 0);
+    }
   }
 }
 
-template <int D, int NT>
-__device__ __forceinline__ void pv_tile(const lds_char* sV, const bf16x8 (&pk)[NT][2], floatx4 (&o)[NT][D / 16],
-                                        int lane) {
+template <int D, int NF, int NS>
+__device__ __forceinline__ void pv_tile(const lds_char* sV, const Probs<NF, NS>& pr, Acc<D, NF, NS>& ac, int lane,
+                                        int w) {
   using T = Tile<D>;
-  constexpr int NSTEP = 2 * T::NDB;
-  constexpr int DEPTH = operand_depth<NT>();
-  const int i16 = lane & 15, hi = lane >> 4;
-  const lds_char* vr = sV + i16 * T::VROW;
-  const int vsw = vswz(i16);
-  auto frag = [&](int j) -> bf16x8 {
-    const int kc = j / T::NDB, db = j % T::NDB;
-    return *(const lds_bf16x8*)(vr + db * 16 * T::VROW + (((4 * kc + hi) ^ vsw) * 16));
-  };
-  bf16x8 fr[DEPTH + 1];
 #pragma unroll
-  for (int i = 0; i < DEPTH; ++i) fr[i] = frag(i);
+  for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-  for (int j = 0; j < NSTEP; ++j) {
-    if (j + DEPTH < NSTEP) fr[(j + DEPTH) % (DEPTH + 1)] = frag(j + DEPTH);
-    const int kc = j / T::NDB, db = j % T::NDB;
+    for (int db = 0; db < T::NDB; ++db) {
+      if (NF > 0) {
+        const bf16x8 vf = vfrag<D>(sV, db, kc, lane);
 #pragma unroll
-    for (int rt = 0; rt < NT; ++rt)
-      o[rt][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[j % (DEPTH + 1)], pk[rt][kc], o[rt][db], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+        for (int t = 0; t < NF; ++t)
+          ac.o[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pr.p[t][kc], ac.o[t][db], 0, 0, 0);
+      }
+      if (NS > 0 && kc == 0) {
+        const bf16x4 vf = vfrag16<D>(sV, db, w, lane);
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+          ac.os[t][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pr.ps[t], ac.os[t][db], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // Step attention, bf16.  A sequence whose keys fit one chunk is normalised
@@ -446,17 +558,18 @@ __device__ __forceinline__ void pv_tile(const lds_char* sV, const bf16x8 (&pk)[N
 // invalidates the whole L2 of the XCD).
 //
 // Prefix tiles j = 0..n-1 of the chunk flow through the LDS rings: K(j) is
-// requested three loop iterations before its scores are needed (slot j%4),
-// V(j) two iterations before that tile's P.V (slot j%4).  Iteration t waits
-// for K(t+1) and V(t-1), passes one barrier (after which every wave is done
-// with iteration t-1, so slots K(t-1) and V(t-2) are free), requests K(t+3)
-// and V(t+2), then runs softmax(t) | scores(t+1) | P.V(t-1).  Tiles that
-// reach past the settled prefix are staged through registers into the
-// fourth slots first, before the ring fills them.
-template <int D, int NT>
+// requested two loop iterations before the iteration that scores it (slot
+// j%4), V(j) three before its P.V (slot j%4).  Iteration t waits for K(t+1) and V(t-1),
+// passes one barrier (after which every wave is done with iteration t-1, so
+// slots K(t-1) and V(t-2) are free), requests K(t+3) and V(t+2), then runs
+// softmax(t) | scores(t+1) | P.V(t-1).  Tiles that reach past the settled
+// prefix are staged through registers into the last slots first, before
+// the ring fills them.
+template <int D, int NF, int NS>
 __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_pipe_bf16_kernel(AttnArgs a) {
   using T = Tile<D>;
+  constexpr int NSa = at_least_1<NS>();
   __shared__ __attribute__((aligned(1024))) char smem[RING * (T::K_BYTES + T::V_BYTES)];
   __shared__ int ovf_flag;
   lds_char* const sK0 = (lds_char*)smem;
@@ -475,29 +588,47 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
   const int kvh = t % a.Hkv;
   const int b = t / a.Hkv;
 
-  // this wave's row tiles: [w0, w1) of the n16 tiles of 16 rows of (b, kvh)
+  // this workgroup's tiles [T0, T1): wave w owns T0 + w*NF + f (f < NF);
+  // the shared tiles T0 + 4*NF + s (s < NS) are split by key block
   const int T0 = rw * a.n16 / a.n_rowblk, T1 = (rw + 1) * a.n16 / a.n_rowblk;
-  const int w0 = T0 + wave * (T1 - T0) / NWV, w1 = T0 + (wave + 1) * (T1 - T0) / NWV;
-  int mrow[NT];
-  bool row_ok[NT];
+  int mrow[at_least_1<NF>()], mrow_s[NSa];
+  bool ok[at_least_1<NF>()], ok_s[NSa];
 #pragma unroll
-  for (int rt = 0; rt < NT; ++rt) {
-    mrow[rt] = 16 * (w0 + rt) + (lane & 15);
-    row_ok[rt] = w0 + rt < w1 && mrow[rt] < a.M;
+  for (int f = 0; f < NF; ++f) {
+    const int ti = T0 + wave * NF + f;
+    mrow[f] = 16 * ti + (lane & 15);
+    ok[f] = ti < T1 && mrow[f] < a.M;
   }
+#pragma unroll
+  for (int s2 = 0; s2 < NS; ++s2) {
+    const int ti = T0 + 4 * NF + s2;
+    mrow_s[s2] = 16 * ti + (lane & 15);
+    ok_s[s2] = ti < T1 && mrow_s[s2] < a.M;
+  }
+  auto out_row = [&](int m) {
+    const int r = m / a.G, h = kvh * a.G + m % a.G;
+    return (bf16*)a.out + ((size_t)(b * a.R + r) * a.Hq + h) * D;
+  };
+  auto lse_at = [&](int m) {
+    const int r = m / a.G, h = kvh * a.G + m % a.G;
+    return a.lse + ((size_t)b * a.Hq + h) * a.R + r;
+  };
 
   const int L = a.lens[b];
   if (L < 0 || L > a.max_len) {  // contract violation: NaN rows, written once
     if (split == 0) {
-#pragma unroll
-      for (int rt = 0; rt < NT; ++rt) {
-        if (!row_ok[rt]) continue;
-        const int r = mrow[rt] / a.G, h = kvh * a.G + mrow[rt] % a.G;
-        bf16* orow = (bf16*)a.out + ((size_t)(b * a.R + r) * a.Hq + h) * D;
+      auto nan_row = [&](int m) {
+        bf16* orow = out_row(m);
         for (int db = 0; db < D / 16; ++db)
           for (int v = 0; v < 4; ++v) orow[16 * db + 4 * hi + v] = (bf16)NAN;
-        if (a.lse && hi == 0) a.lse[((size_t)b * a.Hq + h) * a.R + r] = NAN;
-      }
+        if (a.lse && hi == 0) *lse_at(m) = NAN;
+      };
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        if (ok[f]) nan_row(mrow[f]);
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2)
+        if (ok_s[s2] && wave == 0) nan_row(mrow_s[s2]);
     }
     return;
   }
@@ -521,38 +652,50 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
   dma_plan<D>(plan, wave, lane);
   auto kslot = [&](int j) { return sK0 + (j & (RING - 1)) * T::K_BYTES; };
   auto vslot = [&](int j) { return sV0 + (j & (RING - 1)) * T::V_BYTES; };
-  // ring prologue: K(0); K(1), V(0); K(2), V(1)
+  // ring prologue, as iterations -3..-1 would issue it: K(0); K(1), V(0); K(2), V(1)
   if (n > 0) issue_k<D>(kslot(0), kc_base, plan, kb, wave);
   if (n > 1) issue_k<D>(kslot(1), kc_base, plan, kb + TK, wave);
   if (n > 0) issue_v<D>(vslot(0), vc_base, plan, kb, wave);
   if (n > 2) issue_k<D>(kslot(2), kc_base, plan, kb + 2 * TK, wave);
   if (n > 1) issue_v<D>(vslot(1), vc_base, plan, kb + TK, wave);
 
-  bf16x8 qf[NT][D / 32];
-#pragma unroll
-  for (int rt = 0; rt < NT; ++rt) {
-    const int r = mrow[rt] / a.G, h = kvh * a.G + mrow[rt] % a.G;
+  QFrags<D, NF, NS> q;
+  auto load_q = [&](int m, bool ok_row, bf16x8 (&dst)[D / 32]) {
+    const int r = m / a.G, h = kvh * a.G + m % a.G;
     const bf16* qrow = (const bf16*)a.q + ((size_t)(b * a.R + r) * a.Hq + h) * D;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
-      bf16x8 z = {};
-      qf[rt][c] = row_ok[rt] ? *(const bf16x8*)(qrow + 32 * c + 8 * hi) : z;
+      bf16x8 zq = {};
+      dst[c] = ok_row ? *(const bf16x8*)(qrow + 32 * c + 8 * hi) : zq;
     }
-  }
-  floatx4 o[NT][D / 16];
+  };
 #pragma unroll
-  for (int rt = 0; rt < NT; ++rt)
+  for (int f = 0; f < NF; ++f) load_q(mrow[f], ok[f], q.f[f]);
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) o[rt][db] = (floatx4){0.f, 0.f, 0.f, 0.f};
-  float m_run[NT], l_run[NT], ps[NT];
-#pragma unroll
-  for (int rt = 0; rt < NT; ++rt) { m_run[rt] = kNoMax; l_run[rt] = 0.f; }
-  const float sl2 = a.scale_log2;
-  floatx4 sA[NT][4], sB[NT][4];
-  bf16x8 pA[NT][2], pB[NT][2];
+  for (int s2 = 0; s2 < NS; ++s2) load_q(mrow_s[s2], ok_s[s2], q.s[s2]);
 
-  // Tiles reaching past the prefix: staged through registers into the
-  // fourth slots, masked by zone, softmax with the exact path.
+  Acc<D, NF, NS> ac;
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    ac.m[f] = kNoMax;
+    ac.l[f] = 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) ac.o[f][db] = (floatx4){0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int s2 = 0; s2 < NS; ++s2) {
+    ac.ms[s2] = kNoMax;
+    ac.ls[s2] = 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) ac.os[s2][db] = (floatx4){0.f, 0.f, 0.f, 0.f};
+  }
+  const float sl2 = a.scale_log2;
+  Scores<NF, NS> sA, sB;
+  Probs<NF, NS> pA, pB;
+
+  // Tiles reaching past the prefix: staged through registers into the last
+  // slots (free until the loop's first requests), masked by zone, softmax
+  // with the exact path.
   auto tail_tiles = [&]() {
     for (int t0 = max(kb, fast_end); t0 < ke; t0 += TK) {
       lds_char* sK = kslot(RING - 1);
@@ -561,24 +704,34 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
       stage_tail_tile<D>(sK, sV, kc_base, vc_base, ks_base, vs_base, step_stride, t0, L, Ltot, tid);
       wait_all();
       barrier();
-      s_tile<D, NT>(sK, qf, sA, lane);
+      s_tile<D, NF, NS>(sK, q, sA, lane, wave);
+      // branch-free selects: no divergent control flow around the vector
+      // element updates
 #pragma unroll
-      for (int rt = 0; rt < NT; ++rt) {
-        const StepZone z = step_zone(mrow[rt] / a.G, a.k);
+      for (int f = 0; f < NF; ++f) {
+        const StepZone z = step_zone(mrow[f] / a.G, a.k);
 #pragma unroll
         for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int c = t0 + 32 * (kb4 >> 1) + 8 * hi + 4 * (kb4 & 1) + v;
-            // branch-free select: no divergent control flow around the
-            // vector element update
+            const int c = t0 + krow_of(kb4, 4 * hi + v);
             const bool vis = (c < ke) & z.sees(c - L);
-            sA[rt][kb4][v] = vis ? sA[rt][kb4][v] : -INFINITY;
+            sA.s[f][kb4][v] = vis ? sA.s[f][kb4][v] : -INFINITY;
           }
       }
-      const bool big = sm_tile<NT>(sA, pA, ps, m_run, sl2);
-      softmax_commit<D, NT>(big, sA, pA, ps, m_run, l_run, o, sl2);
-      pv_tile<D, NT>(sV, pA, o, lane);
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) {
+        const StepZone z = step_zone(mrow_s[s2] / a.G, a.k);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int c = t0 + krow_of(wave, 4 * hi + v);
+          const bool vis = (c < ke) & z.sees(c - L);
+          sA.ss[s2][v] = vis ? sA.ss[s2][v] : -INFINITY;
+        }
+      }
+      const bool big = sm_tile<D, NF, NS>(sA, pA, ac, sl2);
+      softmax_commit<D, NF, NS>(big, sA, pA, ac, sl2);
+      pv_tile<D, NF, NS>(sV, pA, ac, lane, wave);
       wait_lgkmcnt0();
     }
   };
@@ -595,10 +748,10 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
     else if (n > 1) wait_vmcnt<T::NKW + 2 * T::NVW>();
     else wait_vmcnt<T::NVW>();
     barrier();
-    s_tile<D, NT>(kslot(0), qf, sA, lane);
+    s_tile<D, NF, NS>(kslot(0), q, sA, lane, wave);
     {
-      const bool big = sm_tile<NT>(sA, pA, ps, m_run, sl2);
-      softmax_commit<D, NT>(big, sA, pA, ps, m_run, l_run, o, sl2);
+      const bool big = sm_tile<D, NF, NS>(sA, pA, ac, sl2);
+      softmax_commit<D, NF, NS>(big, sA, pA, ac, sl2);
     }
 
     // Iteration t: wait until only V(t), K(t+2), V(t+1) may be in flight.
@@ -612,43 +765,49 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
       if (it + 2 < n) issue_v<D>(vslot(it + 2), vc_base, plan, kb + (it + 2) * TK, wave);
     };
     bool overflow = false;
-    auto commit_sum = [&](bool big) {
+    auto commit_sum = [&](bool big, const Probs<NF, NS>& pr) {
       overflow |= __any(big);
-#pragma unroll
-      for (int rt = 0; rt < NT; ++rt) l_run[rt] += ps[rt];
+      sums_commit(pr, ac);
     };
     if (n > 1) {  // t = 0: scores(1)
       sync(0);
-      s_tile<D, NT>(kslot(1), qf, sB, lane);
+      s_tile<D, NF, NS>(kslot(1), q, sB, lane, wave);
     }
     // iteration t: softmax(t) | scores(t+1) | P.V(t-1); the scores after
     // the last tile come from a stale slot and are never used
     int it = 1;
     for (; it + 1 < n; it += 2) {
       sync(it);
-      commit_sum(pipe_body<D, NT, true, true>(kslot(it + 1), vslot(it - 1), qf, sA, sB, pB, pA, o, ps, m_run, sl2,
-                                              lane));
+      commit_sum(pipe_body<D, NF, NS, true, true>(kslot(it + 1), vslot(it - 1), q, sA, sB, pB, pA, ac, sl2, lane, wave),
+                 pB);
       sync(it + 1);
-      commit_sum(pipe_body<D, NT, true, true>(kslot(it + 2), vslot(it), qf, sB, sA, pA, pB, o, ps, m_run, sl2,
-                                              lane));
+      commit_sum(pipe_body<D, NF, NS, true, true>(kslot(it + 2), vslot(it), q, sB, sA, pA, pB, ac, sl2, lane, wave),
+                 pA);
     }
     if (it < n) {  // odd last tile: softmax(n-1) in sB
       sync(it);
-      commit_sum(pipe_body<D, NT, false, true>(kslot(it), vslot(it - 1), qf, sA, sB, pB, pA, o, ps, m_run, sl2,
-                                               lane));
+      commit_sum(pipe_body<D, NF, NS, false, true>(kslot(it), vslot(it - 1), q, sA, sB, pB, pA, ac, sl2, lane, wave),
+                 pB);
     }
     if (overflow) ovf_flag = 1;
     wait_all();
     barrier();
-    pv_tile<D, NT>(vslot(n - 1), ((n - 1) & 1) ? pB : pA, o, lane);
+    pv_tile<D, NF, NS>(vslot(n - 1), ((n - 1) & 1) ? pB : pA, ac, lane, wave);
 
     if (ovf_flag) {  // the same for every wave after the barrier
 #pragma unroll
-      for (int rt = 0; rt < NT; ++rt) {
-        m_run[rt] = kNoMax;
-        l_run[rt] = 0.f;
+      for (int f = 0; f < NF; ++f) {
+        ac.m[f] = kNoMax;
+        ac.l[f] = 0.f;
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db) o[rt][db] = (floatx4){0.f, 0.f, 0.f, 0.f};
+        for (int db = 0; db < D / 16; ++db) ac.o[f][db] = (floatx4){0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) {
+        ac.ms[s2] = kNoMax;
+        ac.ls[s2] = 0.f;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) ac.os[s2][db] = (floatx4){0.f, 0.f, 0.f, 0.f};
       }
       for (int j = 0; j < n; ++j) {
         barrier();
@@ -656,43 +815,125 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
         issue_v<D>(vslot(0), vc_base, plan, kb + j * TK, wave);
         wait_vmcnt<0>();
         barrier();
-        s_tile<D, NT>(kslot(0), qf, sA, lane);
-        const bool big = sm_tile<NT>(sA, pA, ps, m_run, sl2);
-        softmax_commit<D, NT>(big, sA, pA, ps, m_run, l_run, o, sl2);
-        pv_tile<D, NT>(vslot(0), pA, o, lane);
+        s_tile<D, NF, NS>(kslot(0), q, sA, lane, wave);
+        const bool big = sm_tile<D, NF, NS>(sA, pA, ac, sl2);
+        softmax_commit<D, NF, NS>(big, sA, pA, ac, sl2);
+        pv_tile<D, NF, NS>(vslot(0), pA, ac, lane, wave);
         wait_lgkmcnt0();
       }
       tail_tiles();
     }
   }
 
-#pragma unroll
-  for (int rt = 0; rt < NT; ++rt) {
-    float lt = l_run[rt];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
-    if (!row_ok[rt]) continue;
-    const int m = mrow[rt];
-    const int r = m / a.G, h = kvh * a.G + m % a.G;
-    if (n_valid > 1) {  // one chunk of several: publish it for the merge kernel
+  // Output of a finished row tile: normalised bf16 rows and the LSE, or the
+  // unnormalised partial of this chunk for the merge kernel.
+  auto emit = [&](int m, bool ok_row, const floatx4 (&o)[D / 16], float m_ref, float l_tot) {
+    if (!ok_row) return;
+    if (n_valid > 1) {
       const size_t prow = (pair * a.n_split + split) * a.M + m;
       float* op = a.o_part + prow * D;
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db) *(floatx4*)(op + 16 * db + 4 * hi) = o[rt][db];
-      if (hi == 0) a.ml_part[prow] = make_float2(m_run[rt], lt);
-      continue;
+      for (int db = 0; db < D / 16; ++db) *(floatx4*)(op + 16 * db + 4 * hi) = o[db];
+      if (hi == 0) a.ml_part[prow] = make_float2(m_ref, l_tot);
+      return;
     }
-    bf16* orow = (bf16*)a.out + ((size_t)(b * a.R + r) * a.Hq + h) * D;
-    const float inv = 1.f / lt;
+    bf16* orow = out_row(m);
+    const float inv = 1.f / l_tot;
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      bf16x4 w;
+      typedef __bf16 bf16x4o __attribute__((ext_vector_type(4)));
+      bf16x4o wv;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) w[v] = (bf16)(o[rt][db][v] * inv);
-      *(bf16x4*)(orow + 16 * db + 4 * hi) = w;
+      for (int v = 0; v < 4; ++v) wv[v] = (bf16)(o[db][v] * inv);
+      *(bf16x4o*)(orow + 16 * db + 4 * hi) = wv;
     }
-    if (a.lse && hi == 0) a.lse[((size_t)b * a.Hq + h) * a.R + r] = (m_run[rt] + log2f(lt)) * kLn2;
+    if (a.lse && hi == 0) *lse_at(m) = (m_ref + log2f(l_tot)) * kLn2;
+  };
+
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    float lt = ac.l[f];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    emit(mrow[f], ok[f], ac.o[f], ac.m[f], lt);
+  }
+
+  if (NS > 0) {
+    // Merge the four key-block parts of each shared tile through LDS (the
+    // ring is free now): part w of tile s is O (16 rows x D, this wave's
+    // register layout), its reference and its sum.  Wave w then combines
+    // head-dim blocks w, w+4, ... of every shared tile and writes them.
+    float* mo = (float*)smem;                       // [NS][4 parts][D/16][64 lanes][4]
+    float* mml = mo + NS * 4 * (D / 16) * 64 * 4;  // [NS][4 parts][16 rows][2]
+    wait_all();
+    barrier();
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2) {
+      float lt = ac.ls[s2];
+      lt += __shfl_xor(lt, 16);
+      lt += __shfl_xor(lt, 32);
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+        *(floatx4*)(mo + (((s2 * 4 + wave) * (D / 16) + db) * 64 + lane) * 4) = ac.os[s2][db];
+      if (hi == 0) {
+        mml[((s2 * 4 + wave) * 16 + (lane & 15)) * 2] = ac.ms[s2];
+        mml[((s2 * 4 + wave) * 16 + (lane & 15)) * 2 + 1] = lt;
+      }
+    }
+    wait_all();
+    barrier();
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2) {
+      const int r16 = lane & 15;
+      float mp[4], lp[4], mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        mp[w] = mml[((s2 * 4 + w) * 16 + r16) * 2];
+        lp[w] = mml[((s2 * 4 + w) * 16 + r16) * 2 + 1];
+        mx = fmaxf(mx, mp[w]);
+      }
+      float wt[4], l_tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        wt[w] = __builtin_amdgcn_exp2f(mp[w] - mx);
+        l_tot += wt[w] * lp[w];
+      }
+      floatx4 om[D / 16];
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        om[db] = (floatx4){0.f, 0.f, 0.f, 0.f};
+        if (db % 4 != wave) continue;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const floatx4 x = *(const floatx4*)(mo + (((s2 * 4 + w) * (D / 16) + db) * 64 + lane) * 4);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) om[db][v] = fmaf(wt[w], x[v], om[db][v]);
+        }
+      }
+      if (!ok_s[s2]) continue;
+      const int m = mrow_s[s2];
+      if (n_valid > 1) {
+        const size_t prow = (pair * a.n_split + split) * a.M + m;
+        float* op = a.o_part + prow * D;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db)
+          if (db % 4 == wave) *(floatx4*)(op + 16 * db + 4 * hi) = om[db];
+        if (wave == 0 && hi == 0) a.ml_part[prow] = make_float2(mx, l_tot);
+        continue;
+      }
+      bf16* orow = out_row(m);
+      const float inv = 1.f / l_tot;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        if (db % 4 != wave) continue;
+        typedef __bf16 bf16x4o __attribute__((ext_vector_type(4)));
+        bf16x4o wv;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) wv[v] = (bf16)(om[db][v] * inv);
+        *(bf16x4o*)(orow + 16 * db + 4 * hi) = wv;
+      }
+      if (a.lse && wave == 0 && hi == 0) *lse_at(m) = (mx + log2f(l_tot)) * kLn2;
+    }
   }
 }
 
@@ -812,11 +1053,30 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   if (lse && lane == 0) *lse = (mx + log2f(den)) * kLn2;
 }
 
-template <int D, int NT>
+template <int D, int NF, int NS>
 hipError_t launch_bf16_pipe(const AttnArgs& a, hipStream_t s) {
   const int nblk = a.B * a.Hkv * a.n_split * a.n_rowblk;
-  hipLaunchKernelGGL((attn_pipe_bf16_kernel<D, NT>), dim3(nblk), dim3(NWV * 64), 0, s, a);
+  hipLaunchKernelGGL((attn_pipe_bf16_kernel<D, NF, NS>), dim3(nblk), dim3(NWV * 64), 0, s, a);
   return hipGetLastError();
+}
+
+// (full tiles per wave, shared tiles per workgroup) shapes that are built
+template <int D>
+hipError_t launch_bf16_shape(const AttnArgs& a, hipStream_t s) {
+  switch (a.nf * 4 + a.ns) {
+    case 1: return launch_bf16_pipe<D, 0, 1>(a, s);
+    case 2: return launch_bf16_pipe<D, 0, 2>(a, s);
+    case 3: return launch_bf16_pipe<D, 0, 3>(a, s);
+    case 4: return launch_bf16_pipe<D, 1, 0>(a, s);
+    case 5: return launch_bf16_pipe<D, 1, 1>(a, s);
+    case 6: return launch_bf16_pipe<D, 1, 2>(a, s);
+    case 7: return launch_bf16_pipe<D, 1, 3>(a, s);
+    case 8: return launch_bf16_pipe<D, 2, 0>(a, s);
+    case 9: return launch_bf16_pipe<D, 2, 1>(a, s);
+    case 10: return launch_bf16_pipe<D, 2, 2>(a, s);
+    case 12: return launch_bf16_pipe<D, 3, 0>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <typename OutT, int D>
@@ -831,19 +1091,8 @@ hipError_t launch_merge(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
   hipError_t e = hipErrorInvalidValue;
-  if (a.D == 128) {
-    switch (a.nt) {
-      case 1: e = launch_bf16_pipe<128, 1>(a, s); break;
-      case 2: e = launch_bf16_pipe<128, 2>(a, s); break;
-      case 3: e = launch_bf16_pipe<128, 3>(a, s); break;
-    }
-  } else if (a.D == 64) {
-    switch (a.nt) {
-      case 1: e = launch_bf16_pipe<64, 1>(a, s); break;
-      case 2: e = launch_bf16_pipe<64, 2>(a, s); break;
-      case 3: e = launch_bf16_pipe<64, 3>(a, s); break;
-    }
-  }
+  if (a.D == 128) e = launch_bf16_shape<128>(a, s);
+  else if (a.D == 64) e = launch_bf16_shape<64>(a, s);
   if (e != hipSuccess || a.n_split == 1) return e;
   return a.D == 128 ? launch_merge<bf16, 128>(a, s) : launch_merge<bf16, 64>(a, s);
 }

@@ -19,30 +19,42 @@ constexpr int kValuePage = 64;          // positions per value-cache page
 constexpr int kMaxChunkF32 = 1024;      // LDS score buffer of the f32 kernel
 constexpr int kVerifyChunk = 4096;      // logits per argmax workgroup
 constexpr int kCUs = 256;               // compute units of the part
-constexpr int kMaxRowTilesPerWave = 3;  // 16-row tiles a bf16 wave can hold in registers
 
 bool aligned(const void* p, uintptr_t a) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 long cdiv(long a, long b) { return (a + b - 1) / b; }
 
 struct AttnPlan {
-  int R, G, M, n16, nt, n_rowblk, chunk, n_split;
+  int R, G, M, n16, nf, ns, n_rowblk, chunk, n_split;
   size_t o_bytes, ml_bytes, total;
 };
 
 // Split plan of the step attention.
 //
-// bf16: the M = R*G query rows of one (b, kvh) form n16 tiles of 16 rows; a
+// bf16: the M = R*G query rows of one (b, kvh) form n16 tiles of 16 rows.  A
 // workgroup (four waves, one per SIMD, one workgroup per CU) takes a
-// contiguous share of them for one key chunk, each wave at most nt <= 3
-// tiles.  Candidates (row workgroups per (b, kvh), key chunks) are scored in
-// units of one 64-key tile for one 16-row tile (~512 MFMA cycles): the
-// slowest wave's tiles per round of kCUs workgroups, the HBM floor of the
-// stream, a fixed cost per round, and for several chunks the partial
-// outputs (M*(D+2)*4 bytes per chunk, written and read back) plus the merge
-// launch.
+// contiguous share of T of them for one key chunk: each wave owns nf full
+// tiles and the ns = T - 4*nf remaining tiles are shared by the four waves
+// one 16-key block each, so every wave carries nf + ns/4 tiles; or all T
+// tiles are full ones (ceil(T/4) per wave, the last waves partly idle).
+// Built shapes: nf <= 3, ns <= 3, no shared tile next to three full ones or
+// three shared next to two full ones (registers).  Candidates (row
+// workgroups per (b, kvh), tile layout, key chunks) are scored in clocks:
+// per 64-key tile a loop step costs body_clk(nf, ns) (fitted to whole-kernel
+// timings on this part: ~700 of synchronisation and direct-load issue, ~400
+// per full tile, ~300 per shared tile); per round of kCUs workgroups a fixed
+// ~20k (prologue, tiles past the prefix, output);
+// the HBM floor of the stream; and for several chunks the partial outputs
+// (M*(D+2)*4 bytes per chunk, written and read back) plus the merge launch.
 //
 // f32: one wave per query row and chunk, chunks of at most kMaxChunkF32.
+double body_clk(int nf, int ns) { return 700.0 + 400.0 * nf + 300.0 * ns; }
+
+bool shape_built(int nf, int ns) {
+  if (nf < 0 || nf > 3 || ns < 0 || ns > 3 || nf + ns == 0) return false;
+  return !(nf == 3 && ns > 0) && !(nf == 2 && ns == 3);
+}
+
 int plan_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_len, int k,
                    int n_groups, int kv_chunk, AttnPlan* p) {
   if (dtype != TIDAR_BF16 && dtype != TIDAR_F32) return TIDAR_EUNSUPPORTED;
@@ -63,14 +75,16 @@ int plan_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_
 
   if (dtype == TIDAR_F32) {
     p->chunk = kv_chunk ? kv_chunk : (int)std::min<long>(kMaxChunkF32, (long)round_up(keys, kTileKeys));
-    p->nt = 1;
+    p->nf = 1;
+    p->ns = 0;
     p->n_rowblk = 1;
   } else {
     const long n_key_tiles = cdiv(keys, kTileKeys);
-    const double hbm_units = (double)pairs * keys * D * 4 / 1.3e6;  // K+V bytes at ~6 TB/s, 0.22 us units
+    constexpr double kClkPerUs = 2200.0;
+    const double hbm_clk = (double)pairs * keys * D * 4 / 6.0e6 * kClkPerUs;  // K+V bytes at ~6 TB/s
     double best = 1e300;
     long best_chunk = 0;
-    int best_wr = 1, best_nt = 1;
+    int best_wr = 1, best_nf = 1, best_ns = 0;
     long best_wgs = 0;
     const long ns_max = kv_chunk ? 1 : std::min<long>(n_key_tiles, 64);
     for (long ns_try = 1; ns_try <= ns_max; ++ns_try) {
@@ -79,30 +93,37 @@ int plan_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_
       if (ns != ns_try && !kv_chunk) continue;  // the same chunk as a smaller count
       const long kt = cdiv(chunk, kTileKeys) + 1;  // + the step tile staged through registers
       for (int wr = 1; wr <= p->n16; ++wr) {
-        const int per_wave = (int)cdiv(cdiv(p->n16, wr), 4);
-        if (per_wave > kMaxRowTilesPerWave) continue;
-        const long wgs = pairs * wr * ns;
-        const long rounds = cdiv(wgs, kCUs);
-        double cost = std::max((double)rounds * per_wave * kt, hbm_units) + 10.0 * rounds;
-        if (ns > 1) cost += 14.0 + (double)pairs * ns * p->M * (D * 4 + 8) * 2 / 1.1e6;
-        const bool better = cost < best * 0.999 || (cost <= best * 1.001 && wgs > best_wgs && wgs <= rounds * kCUs);
-        if (better) {
-          best = cost;
-          best_chunk = chunk;
-          best_wr = wr;
-          best_nt = per_wave;
-          best_wgs = wgs;
+        const int t_max = (int)cdiv(p->n16, wr);
+        const int layouts[2][2] = {{t_max / 4, t_max % 4}, {(int)cdiv(t_max, 4), 0}};
+        for (const auto& lay : layouts) {
+          const int nf = lay[0], nsh = lay[1];
+          if (!shape_built(nf, nsh)) continue;
+          const long wgs = pairs * wr * ns;
+          const long rounds = cdiv(wgs, kCUs);
+          double cost = std::max((double)rounds * body_clk(nf, nsh) * kt, hbm_clk) + 20000.0 * rounds;
+          if (ns > 1) cost += (14.0 + (double)pairs * ns * p->M * (D * 4 + 8) * 2 / 5.0e6) * kClkPerUs;
+          const bool better = cost < best * 0.999 || (cost <= best * 1.001 && wgs > best_wgs && wgs <= rounds * kCUs);
+          if (better) {
+            best = cost;
+            best_chunk = chunk;
+            best_wr = wr;
+            best_nf = nf;
+            best_ns = nsh;
+            best_wgs = wgs;
+          }
         }
       }
     }
     p->chunk = (int)best_chunk;
-    p->nt = best_nt;
+    p->nf = best_nf;
+    p->ns = best_ns;
     p->n_rowblk = best_wr;
   }
   p->n_split = (int)cdiv(keys, p->chunk);
 
   const long blocks = pairs * p->n_split * (dtype == TIDAR_F32 ? p->M : p->n_rowblk);
   if (blocks > 0x7fffffffL) return TIDAR_EUNSUPPORTED;
+  if (dtype == TIDAR_BF16 && !shape_built(p->nf, p->ns)) return TIDAR_EUNSUPPORTED;
 
   // workspace: [partial outputs][partial (max, sum)]; none is needed when
   // every sequence fits one chunk (bf16 path)
@@ -199,7 +220,8 @@ int tidar_step_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, in
   a.chunk = p.chunk;
   a.n_split = p.n_split;
   a.n16 = p.n16;
-  a.nt = p.nt;
+  a.nf = p.nf;
+  a.ns = p.ns;
   a.n_rowblk = p.n_rowblk;
   a.scale_log2 = sm_scale * 1.44269504088896340736f;
   a.single_chunk_direct = dtype == TIDAR_BF16;

@@ -24,7 +24,8 @@ struct AttnArgs {
   float2* ml_part; // [B][Hkv][n_split][M]     (running max in log2 units, sum)
   int B, Hq, Hkv, G, D, S_max, max_len, k, R, M;
   int chunk, n_split;
-  int n16, nt, n_rowblk;  // bf16 path: 16-row tiles of (b, kvh), tiles per wave, workgroups per (b, kvh)
+  int n16, nf, ns, n_rowblk;  // bf16 path: 16-row tiles of (b, kvh); per workgroup, full tiles per
+                              // wave and tiles shared by key block; workgroups per (b, kvh)
   float scale_log2;     // sm_scale * log2(e)
   int single_chunk_direct;  // the split kernel writes sequences that fit one chunk (bf16 path)
 };
