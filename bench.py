@@ -161,8 +161,8 @@ def summarize(dirname):
         return (COPY_CALIB_BYTES / 1024.0) / statistics.mean(vals)
 
     f_fetch, f_write = copy_factor("FETCH_SIZE"), copy_factor("WRITE_SIZE")
-    fetch, nf = per_dispatch("FETCH_SIZE", "attn_split_bf16")
-    write, nw = per_dispatch("WRITE_SIZE", "attn_split_bf16")
+    fetch, nf = per_dispatch("FETCH_SIZE", "attn_pipe_bf16")
+    write, nw = per_dispatch("WRITE_SIZE", "attn_pipe_bf16")
     hbm = fetch * 1024 * f_fetch + write * 1024 * f_write
     out = ["# HBM traffic of the step-attention kernel, 8B-shaped workload (rocprofv3 counters)",
            "# Commands (from the repository root, MI355X), one counter per run:",
