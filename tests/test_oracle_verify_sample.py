@@ -1,0 +1,101 @@
+"""Pins of the stochastic-verification oracle (oracle/verify_sample.py).
+
+Each pin checks the oracle against something other than itself: published
+known-answer vectors of the random generator, and distributional properties
+that the mathematics fixes (checked by Monte Carlo with chi-square bounds at
+a 1e-4 false-alarm level; all seeds are fixed, so the tests are
+deterministic), plus the low-temperature limit, which must reproduce the
+greedy oracle.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle.verify_sample as vs
+from oracle import verify_ref
+import workloads as W
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CHI2_99_99 = {2: 18.42, 3: 21.11, 4: 23.51}  # chi-square quantile 0.9999 by degrees of freedom
+
+
+def test_philox_known_answers():
+    for line in open(os.path.join(HERE, "golden", "philox4x32_10_kat.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        w = [int(x, 16) for x in line.split()]
+        out = vs.philox4x32_10(w[0:4], (w[4], w[5]))
+        assert [int(x) for x in out] == w[6:10]
+
+
+def _chi2(counts, probs):
+    n = counts.sum()
+    e = n * np.asarray(probs)
+    return float(((counts - e) ** 2 / e).sum())
+
+
+def test_uniforms_are_uniform_and_in_open_interval():
+    u = vs.row_uniforms(seed=7, step=3, b=0, j=1, V=40000)
+    assert u.min() > 0.0 and u.max() < 1.0
+    counts = np.histogram(u, bins=5, range=(0, 1))[0]
+    assert _chi2(counts, [0.2] * 5) < CHI2_99_99[4]
+
+
+def test_gumbel_draw_follows_the_weights():
+    w = np.array([0.1, 0.2, 0.3, 0.4])
+    n = 20000
+    counts = np.zeros(4)
+    for b in range(n):
+        idx, _ = vs.gumbel_draw(w, vs.row_uniforms(seed=11, step=0, b=b, j=2, V=4))
+        counts[idx] += 1
+    assert _chi2(counts, w) < CHI2_99_99[3]
+
+
+def test_first_token_is_distributed_as_the_target():
+    """Speculative sampling's defining property: drawing the candidate from q
+    and keeping or resampling it gives a token distributed exactly as p."""
+    rng = np.random.default_rng(5)
+    V, n = 5, 20000
+    lp = rng.normal(size=V) * 1.5
+    lq = rng.normal(size=V) * 1.5
+    p, q = vs.softmax(lp, 1.0), vs.softmax(lq, 1.0)
+    # candidate 0 ~ q, drawn with an independent Gumbel stream (row 9)
+    cand = np.array([[vs.gumbel_draw(q, vs.row_uniforms(3, 1, b, 9, V))[0]] for b in range(n)], np.int32)
+    ar = np.broadcast_to(lp, (n, 2, V))
+    ql = np.broadcast_to(lq, (n, 1, V))
+    a, nxt = vs.verify_sample_ref(ar, ql, None, cand, 1.0, seed=3, step=1)
+    first = np.where(a == 1, cand[:, 0], nxt[:, 0])
+    counts = np.bincount(first, minlength=V).astype(float)
+    assert _chi2(counts, p) < CHI2_99_99[4]
+    kept = float((a == 1).mean())
+    expect = float(np.minimum(p, q).sum())
+    assert abs(kept - expect) < 4.0 * np.sqrt(expect * (1 - expect) / n)
+
+
+def test_low_temperature_with_one_hot_proposals_is_the_greedy_rule():
+    """T -> 0 with proposals peaked at the candidates: a candidate is kept
+    iff it is the target argmax, the resample is the target argmax and the
+    drafts are argmaxes -- the greedy oracle's outputs."""
+    B, k, V = 6, 4, 300
+    v = W.verify_inputs(B, k, V, seed=21, accept="uniform")
+    ar, dr, cand = v["ar_logits"].astype(np.float64), v["draft_logits"].astype(np.float64), v["cand"]
+    # make every row's maximum stand clear of the rest (gap >= 1) so T = 1e-3 is one-hot
+    for arr in (ar.reshape(-1, V), dr.reshape(-1, V)):
+        top = arr.argmax(axis=1)
+        arr[np.arange(len(arr)), top] = arr.max(axis=1) + 1.0
+    ql = np.zeros((B, k, V))
+    ql[np.arange(B)[:, None], np.arange(k)[None, :], cand] = 100.0
+    a_g, n_g = verify_ref(ar, dr, cand)
+    a_s, n_s = vs.verify_sample_ref(ar, ql, dr, cand, 1e-3, seed=1, step=0)
+    assert a_s.tolist() == a_g.tolist()
+    assert n_s.tolist() == n_g.tolist()
+
+
+def test_proposal_equal_to_target_keeps_every_candidate():
+    rng = np.random.default_rng(2)
+    B, k, V = 3, 5, 50
+    ar = rng.normal(size=(B, k + 1, V))
+    cand = rng.integers(0, V, size=(B, k)).astype(np.int32)
+    a, _ = vs.verify_sample_ref(ar, ar[:, :k], rng.normal(size=(B, k, k, V)), cand, 0.7, seed=4, step=2)
+    assert a.tolist() == [k] * B
