@@ -25,7 +25,9 @@ Randomness (passed as a seed and a step number, so both sides draw the same
 numbers): Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
 numbers: as easy as 1, 2, 3", SC 2011), key = (seed low, seed high 32 bits),
 counter = (c0, purpose, b, step).  A 32-bit output x gives the uniform
-u = ((x >> 8) + 0.5) * 2^-24 in (0, 1).
+u = ((x >> 9) + 0.5) * 2^-23 in (0, 1): 23 random bits, so that every u is
+exactly representable in fp32 (with 24 bits and the half offset, the upper
+half of the grid falls between fp32 values and its top rounds to 1.0).
 * accept test of candidate i: counter (i, 0xFFFFFFFF, b, step), word 0;
 * draw for row j (0 = next_cand[0], m = next_cand[m]): Gumbel-max,
   argmax_v (log w_v + G_v) with G_v = -log(-log u_v) and u_v from counter
@@ -77,8 +79,8 @@ def _key(seed):
 
 
 def to_uniform(x):
-    """uint32 -> uniform in (0, 1) with 24 random bits (exact in fp32)."""
-    return ((np.asarray(x, dtype=np.uint64) >> np.uint64(8)).astype(np.float64) + 0.5) * 2.0 ** -24
+    """uint32 -> uniform in (0, 1) from the top 23 bits (exact in fp32)."""
+    return ((np.asarray(x, dtype=np.uint64) >> np.uint64(9)).astype(np.float64) + 0.5) * 2.0 ** -23
 
 
 def accept_uniform(seed, step, b, i):

@@ -42,6 +42,16 @@ def test_uniforms_are_uniform_and_in_open_interval():
     assert _chi2(counts, [0.2] * 5) < CHI2_99_99[4]
 
 
+def test_uniform_grid_is_exact_in_fp32_at_both_ends():
+    # the GPU forms the same uniforms in fp32: every grid value, the extremes
+    # included, must survive a round trip through float32 and stay inside (0, 1)
+    x = np.array([0, 1 << 9, 0x7FFFFFFF, 0x80000000, 0xFFFFFDFF, 0xFFFFFFFF], dtype=np.uint64)
+    u = vs.to_uniform(x)
+    assert np.array_equal(u.astype(np.float32).astype(np.float64), u)
+    assert u[0] == 2.0 ** -24 and u[-1] == 1.0 - 2.0 ** -24
+    assert (u > 0).all() and (u < 1).all()
+
+
 def test_gumbel_draw_follows_the_weights():
     w = np.array([0.1, 0.2, 0.3, 0.4])
     n = 20000
