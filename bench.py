@@ -17,6 +17,9 @@ Prints ONE JSON line.  Options:
   --gpus N          only N = 1 is supported (one GPU per process, no collectives)
   --steps K --warmup W
   --no-cpu-baseline skip the oracle timing (for profiler runs)
+  --verify sample   stochastic verification (temperature --temperature, Philox
+                    stream of --seed and the step number) in place of greedy;
+                    inputs from the sampling generator, accept lengths as drawn
   --calibrate-copy  run only a plain device copy of known size (for scaling
                     the FETCH_SIZE / WRITE_SIZE counters)
   --summarize DIR   turn rocprofv3 outputs under DIR (kt/, pmc_FETCH_SIZE/,
@@ -55,6 +58,8 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--kv-chunk", type=int, default=0, help="key positions per attention chunk (0: library plan)")
     p.add_argument("--summarize", metavar="DIR", help="write profiles/ summaries from rocprofv3 outputs in DIR")
+    p.add_argument("--verify", default="greedy", choices=["greedy", "sample"])
+    p.add_argument("--temperature", type=float, default=1.0)
     p.add_argument("--workload", default="step_8b", choices=["step_8b", "step_1p5b", "step_8b_long"],
                    help="synthetic workload (the reported line is the 8B-shaped step)")
     return p.parse_args()
@@ -85,17 +90,23 @@ def read_traffic():
         return None
 
 
-def step_bytes(shape, V, accept):
+def step_bytes(shape, V, accept, verify_kind="greedy"):
     """Algorithmic bytes of one step (each byte moved once).
-    attention: settled K+V + step K+V + Q + O; verify: (k+1) AR rows and k-1
-    draft rows of f32 logits; commit: accepted K/V rows read and written."""
+    attention: settled K+V + step K+V + Q + O; greedy verify: (k+1) AR rows
+    and k-1 draft rows of f32 logits; sampling verify: k AR and k proposal
+    rows (softmax statistics), the k drawn rows, and the proposal row of the
+    residual where a candidate was rejected; commit: accepted K/V rows read
+    and written."""
     s = shape
     esz = 2
     kv_prefix = sum(s.lens) * s.Hkv * 2 * s.D * esz
     kv_step = s.B * s.R * s.Hkv * 2 * s.D * esz
     qo = 2 * s.B * s.R * s.Hq * s.D * esz
     attn = kv_prefix + kv_step + qo
-    verify = s.B * (2 * s.k) * V * 4
+    if verify_kind == "sample":
+        verify = (s.B * 3 * s.k + sum(1 for a in accept if a < s.k)) * V * 4
+    else:
+        verify = s.B * (2 * s.k) * V * 4
     commit = int(sum(accept)) * s.Hkv * s.D * esz * 2 * 2
     flops = 4 * s.D * s.Hq * sum(s.R * L for L in s.lens)
     return attn, verify, commit, kv_prefix + kv_step, flops
@@ -185,7 +196,7 @@ def summarize(dirname):
     print("\n".join(out))
 
 
-def cpu_baseline(wl, d, v, a_planted):
+def cpu_baseline(wl, d, v, a_planted, args):
     """The oracle (as it stands) on the same workload: three full steps."""
     import numpy as np
     try:
@@ -211,23 +222,28 @@ def cpu_baseline(wl, d, v, a_planted):
         for _ in range(n_steps):
             oracle.attention_ref(f["q"], f["k_step"], f["v_step"], f["k_cache"], f["v_cache"], d["lens"], s.k,
                                  s.n_groups, s.sm_scale)
-            acc, _ = oracle.verify_ref(v["ar_logits"], v["draft_logits"], v["cand"])
+            if args.verify == "sample":
+                acc, _ = oracle.verify_sample_ref(v["ar_logits"], v["q_logits"], v["draft_logits"], v["cand"],
+                                                  args.temperature, args.seed, 0)
+            else:
+                acc, _ = oracle.verify_ref(v["ar_logits"], v["draft_logits"], v["cand"])
             oracle.commit_ref(d["k_cache"], d["v_cache"], d["lens"], d["k_step"], d["v_step"], acc, s.k)
         dt = (time.perf_counter() - t0) / n_steps
     finally:
         if ctx:
             ctx.__exit__(None, None, None)
-    attn, ver, com, _, _ = step_bytes(s, wl.V, a_planted)
+    attn, ver, com, _, _ = step_bytes(s, wl.V, a_planted, args.verify)
     return {"value": round((attn + ver + com) / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle", "seconds_per_step": round(dt, 3),
-            "sample": f"{n_steps} full {wl.name} steps (attention over all {s.B}x{s.Hq} heads, verify, commit), "
+            "sample": f"{n_steps} full {wl.name} steps (attention over all {s.B}x{s.Hq} heads, {args.verify} verify, "
+                      "commit), "
                       f"float64 NumPy, {threads} BLAS threads on {cores} host cores"}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one GPU, with no "
+        print(f"bench.py: --gpus {args.gpus} is not supported: the benchmark runs on one GPU, with no "
               "collectives (each GPU would run the same step on its own share of the batch).", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
@@ -251,8 +267,14 @@ def main():
     s = wl.attn
 
     d = W.attention_inputs(s, seed=args.seed, config_id=wl.config_id, tail="zero")
-    v = W.verify_inputs(s.B, s.k, wl.V, seed=args.seed, config_id=wl.config_id, accept=wl.accept)
-    a_planted = v["planted"]
+    if args.verify == "sample":
+        v = W.sample_inputs(s.B, s.k, wl.V, seed=args.seed, config_id=wl.config_id)
+        v_names = ("ar_logits", "q_logits", "draft_logits", "cand")
+        a_planted = None
+    else:
+        v = W.verify_inputs(s.B, s.k, wl.V, seed=args.seed, config_id=wl.config_id, accept=wl.accept)
+        v_names = ("ar_logits", "draft_logits", "cand")
+        a_planted = v["planted"]
 
     def to_dev(x, bf16):
         x = np.ascontiguousarray(x)
@@ -261,12 +283,13 @@ def main():
         return torch.from_numpy(x).to(dev)
 
     base = {n: to_dev(x, n != "lens") for n, x in d.items()}
-    base.update({n: to_dev(v[n], False) for n in ("ar_logits", "draft_logits", "cand")})
+    base.update({n: to_dev(v[n], False) for n in v_names})
     per_rep = sum(t.numel() * t.element_size() for t in base.values())
     n_rep = max(2, math.ceil(args.cold_bytes / per_rep))
     ws_a = tidar.step_attention_workspace_bytes(0, s.B, s.Hq, s.Hkv, s.D, s.S_max, s.max_len, s.k, s.n_groups,
                                                 args.kv_chunk)
-    ws_v = tidar.verify_workspace_bytes(s.B, s.k, wl.V)
+    ws_v = (tidar.verify_sample_workspace_bytes if args.verify == "sample" else tidar.verify_workspace_bytes)(
+        s.B, s.k, wl.V)
     reps = []
     for _ in range(n_rep):
         r = {n: t.clone() for n, t in base.items()}
@@ -287,9 +310,16 @@ def main():
                              s.n_groups, s.sm_scale, max_len=s.max_len, out=r["out"], lse=r["lse"],
                              workspace=r["ws_a"], kv_chunk=args.kv_chunk)
 
-    def verify_commit(r):
-        tidar.verify_greedy(r["ar_logits"], r["draft_logits"], r["cand"], accept_len=r["acc"], next_cand=r["next"],
-                            workspace=r["ws_v"])
+    def verify(r, step_no):
+        if args.verify == "sample":
+            tidar.verify_sample(r["ar_logits"], r["q_logits"], r["draft_logits"], r["cand"], args.temperature,
+                                args.seed, step_no, accept_len=r["acc"], next_cand=r["next"], workspace=r["ws_v"])
+        else:
+            tidar.verify_greedy(r["ar_logits"], r["draft_logits"], r["cand"], accept_len=r["acc"],
+                                next_cand=r["next"], workspace=r["ws_v"])
+
+    def verify_commit(r, step_no):
+        verify(r, step_no)
         tidar.kv_commit(r["k_cache"], r["v_cache"], r["lens"], r["k_step"], r["v_step"], r["acc"], s.k, r["err"])
         r["lens"].copy_(r["lens0"])
 
@@ -300,7 +330,7 @@ def main():
     for i in range(Wu):
         r = reps[i % n_rep]
         attention(r)
-        verify_commit(r)
+        verify_commit(r, i)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(K):
@@ -308,22 +338,37 @@ def main():
         ev_a[i][0].record(stream)
         attention(r)
         ev_a[i][1].record(stream)
-        verify_commit(r)
+        verify_commit(r, Wu + i)
     t_end.record(stream)
     torch.cuda.synchronize()
     step_ms = t_start.elapsed_time(t_end) / K
     attn_ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev_a)
     attn_ms_mean = sum(attn_ms) / K
 
-    # the accepted lengths the GPU produced must be the planted ones (exact by construction)
-    acc = reps[0]["acc"].cpu().numpy()
-    if a_planted is not None:
-        assert acc.tolist() == a_planted.tolist(), "verify result differs from the planted accept lengths"
-    else:
-        a_planted = acc
     assert int(reps[0]["err"].abs().sum()) == 0
-
-    attn_b, ver_b, com_b, kv_b, flops = step_bytes(s, wl.V, a_planted)
+    if args.verify == "sample":
+        # sampling is a function of (inputs, seed, step): replay the timed
+        # steps' verification to get the accept lengths their bytes depend on
+        accs = []
+        for i in range(K):
+            r = reps[(Wu + i) % n_rep]
+            verify(r, Wu + i)
+            accs.append(r["acc"].cpu().numpy())
+        acc_all = np.stack(accs)
+        assert ((acc_all >= 0) & (acc_all <= s.k)).all()
+        a_planted = acc_all.mean(axis=0)
+        b_steps = [step_bytes(s, wl.V, a, "sample") for a in acc_all]
+        attn_b, kv_b, flops = b_steps[0][0], b_steps[0][3], b_steps[0][4]
+        ver_b = sum(b[1] for b in b_steps) / K
+        com_b = sum(b[2] for b in b_steps) / K
+    else:
+        # the accepted lengths the GPU produced must be the planted ones (exact by construction)
+        acc = reps[0]["acc"].cpu().numpy()
+        if a_planted is not None:
+            assert acc.tolist() == a_planted.tolist(), "verify result differs from the planted accept lengths"
+        else:
+            a_planted = acc
+        attn_b, ver_b, com_b, kv_b, flops = step_bytes(s, wl.V, a_planted)
     flops_step = 4 * s.D * s.Hq * s.B * visible_step_pairs(s.k, s.n_groups)
     step_gbps = (attn_b + ver_b + com_b) / (step_ms * 1e-3) / 1e9
     attn_gbps = attn_b / (attn_ms_mean * 1e-3) / 1e9
@@ -343,7 +388,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "kv_chunk": args.kv_chunk or "auto", "batch": s.B, "q_heads": s.Hq, "kv_heads": s.Hkv, "head_dim": s.D,
                    "prefix": s.lens[0], "k": s.k, "draft_groups": s.n_groups, "step_rows": s.R, "vocab": wl.V,
-                   "accept": wl.accept, "cold_replicas": n_rep},
+                   "accept": wl.accept if args.verify == "greedy" else "sampled", "verify": args.verify,
+                   "cold_replicas": n_rep},
         "step_us": round(step_ms * 1e3, 2),
         "attention_us": round(attn_ms_mean * 1e3, 2),
         "attention_us_p50": round(attn_ms[K // 2] * 1e3, 2),
@@ -356,7 +402,7 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": attn_b},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, d, v, a_planted)
+        result["cpu_baseline"] = cpu_baseline(wl, d, v, a_planted, args)
     print(json.dumps(result))
 
 

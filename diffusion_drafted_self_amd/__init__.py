@@ -1,7 +1,7 @@
 """TiDAR decode-step hot path on MI355X (gfx950): thin Python binding.
 
-The three calls of ``include/tidar.h`` -- ``step_attention``,
-``verify_greedy`` and ``kv_commit`` -- under the same names, taking torch
+The calls of ``include/tidar.h`` -- ``step_attention``, ``verify_greedy``,
+``verify_sample`` and ``kv_commit`` -- under the same names, taking torch
 tensors that live on the GPU.  This module only checks shapes and dtypes,
 marshals pointers and the current HIP stream, and allocates outputs /
 workspace with torch when the caller does not pass them.  Every step of the
@@ -13,8 +13,8 @@ Tensor layouts (row-major, contiguous):
   q [B][R][Hq][D], k_step/v_step [B][R][Hkv][D],
   k_cache [B][Hkv][S_max][D], v_cache [B][Hkv][S_max/64][D][64] (values in
   pages of 64 positions, each page transposed),
-  lens [B] int32, ar_logits [B][k+1][V] f32, draft_logits [B][k][k][V] f32,
-  cand [B][k] int32.
+  lens [B] int32, ar_logits [B][k+1][V] f32, q_logits [B][k][V] f32,
+  draft_logits [B][k][k][V] f32, cand [B][k] int32.
 """
 from __future__ import annotations
 
@@ -38,6 +38,9 @@ SIGNATURES = {
     "tidar_step_attention": (_c_int, [_c_int] * 9 + [_f, _c_int] + [_p] * 9 + [_c_size, _p]),
     "tidar_verify_workspace": (_c_int, [_c_int] * 3 + [ctypes.POINTER(_c_size)]),
     "tidar_verify_greedy": (_c_int, [_c_int] * 3 + [_p] * 6 + [_c_size, _p]),
+    "tidar_verify_sample_workspace": (_c_int, [_c_int] * 3 + [ctypes.POINTER(_c_size)]),
+    "tidar_verify_sample": (_c_int, [_c_int] * 3 + [_f] + [_p] * 4 + [ctypes.c_uint64, ctypes.c_uint32]
+                            + [_p] * 3 + [_c_size, _p]),
     "tidar_kv_commit": (_c_int, [_c_int] * 7 + [_p] * 7 + [_p]),
 }
 
@@ -228,6 +231,48 @@ def verify_greedy(ar_logits, draft_logits, cand, accept_len=None, next_cand=None
     return accept_len, next_cand
 
 
+def verify_sample_workspace_bytes(B: int, k: int, V: int) -> int:
+    n = _c_size(0)
+    _check("tidar_verify_sample_workspace", lib().tidar_verify_sample_workspace(B, k, V, ctypes.byref(n)))
+    return n.value
+
+
+def verify_sample(ar_logits, q_logits, draft_logits, cand, temperature: float, seed: int, step: int,
+                  accept_len=None, next_cand=None, workspace=None):
+    """Stochastic verification at temperature > 0 with the Philox stream of
+    (seed, step).  Returns (accept_len, next_cand)."""
+    _need(ar_logits, "ar_logits", torch.float32, 3)
+    dev = ar_logits.device
+    B, k1, V = ar_logits.shape
+    k = k1 - 1
+    _need(q_logits, "q_logits", torch.float32, 3, dev)
+    if tuple(q_logits.shape) != (B, k, V):
+        raise ValueError("q_logits must be [B][k][V]")
+    _need(cand, "cand", torch.int32, 2, dev)
+    if tuple(cand.shape) != (B, k):
+        raise ValueError("cand must be [B][k]")
+    if k > 1 or draft_logits is not None:
+        _need(draft_logits, "draft_logits", torch.float32, 4, dev)
+        if tuple(draft_logits.shape) != (B, k, k, V):
+            raise ValueError("draft_logits must be [B][k][k][V]")
+    if not 0 <= int(seed) < 1 << 64 or not 0 <= int(step) < 1 << 32:
+        raise ValueError("seed must fit 64 bits and step 32 bits")
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    else:
+        _need(accept_len, "accept_len", torch.int32, 1, dev)
+    if next_cand is None:
+        next_cand = torch.empty((B, k), dtype=torch.int32, device=dev)
+    else:
+        _need(next_cand, "next_cand", torch.int32, 2, dev)
+    ws = _workspace(verify_sample_workspace_bytes(B, k, V), dev, workspace)
+    _check("tidar_verify_sample",
+           lib().tidar_verify_sample(B, k, V, float(temperature), _ptr(ar_logits), _ptr(q_logits),
+                                    _ptr(draft_logits), _ptr(cand), int(seed), int(step), _ptr(accept_len),
+                                    _ptr(next_cand), _ptr(ws), ws.numel(), _stream()))
+    return accept_len, next_cand
+
+
 # ------------------------------------------------------------------------ commit
 def kv_commit(k_cache, v_cache, lens, k_step, v_step, accept_len, k: int, err_flags=None):
     """Append the accepted candidate rows to the caches in place and advance
@@ -254,4 +299,4 @@ def kv_commit(k_cache, v_cache, lens, k_step, v_step, accept_len, k: int, err_fl
 
 
 __all__ = ["step_attention", "step_attention_workspace_bytes", "verify_greedy", "verify_workspace_bytes",
-           "kv_commit", "strerror", "lib", "TidarError", "LIB_PATH", "SIGNATURES"]
+           "verify_sample", "verify_sample_workspace_bytes", "kv_commit", "strerror", "lib", "TidarError", "LIB_PATH", "SIGNATURES"]

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 
@@ -151,6 +152,24 @@ int plan_verify(int B, int k, int V, VerifyPlan* p) {
   return TIDAR_OK;
 }
 
+struct SamplePlan {
+  int n_chunks;
+  size_t stats_bytes, resid_bytes, part_bytes, fb_bytes, total;
+};
+
+int plan_sample(int B, int k, int V, SamplePlan* p) {
+  if (k > kMaxK) return TIDAR_EUNSUPPORTED;
+  if (B < 0 || k < 1 || V < 1) return TIDAR_EINVAL;
+  if ((long)2 * B * k > 65535) return TIDAR_EUNSUPPORTED;  // grid y limit
+  p->n_chunks = (int)cdiv(V, tidar::kSampleChunk);
+  p->stats_bytes = round_up((size_t)2 * B * k * p->n_chunks * sizeof(float2), 256);
+  p->resid_bytes = round_up((size_t)B * 4 * sizeof(float), 256);
+  p->part_bytes = round_up((size_t)B * k * p->n_chunks * sizeof(float2), 256);
+  p->fb_bytes = round_up((size_t)B * p->n_chunks * sizeof(float2), 256);
+  p->total = p->stats_bytes + p->resid_bytes + p->part_bytes + p->fb_bytes;
+  return TIDAR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -268,6 +287,54 @@ int tidar_verify_greedy(int B, int k, int V, const float* ar_logits, const float
   a.chunk_elems = kVerifyChunk;
   a.n_chunks = p.n_chunks;
   const hipError_t e = tidar::launch_verify(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
+}
+
+int tidar_verify_sample_workspace(int B, int k, int V, size_t* bytes) {
+  if (!bytes) return TIDAR_EINVAL;
+  SamplePlan p;
+  const int st = plan_sample(B, k, V, &p);
+  if (st != TIDAR_OK) return st;
+  *bytes = p.total;
+  return TIDAR_OK;
+}
+
+int tidar_verify_sample(int B, int k, int V, float temperature, const float* ar_logits, const float* q_logits,
+                        const float* draft_logits, const int32_t* cand, uint64_t seed, uint32_t step,
+                        int32_t* accept_len, int32_t* next_cand, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  SamplePlan p;
+  const int st = plan_sample(B, k, V, &p);
+  if (st != TIDAR_OK) return st;
+  if (!(temperature > 0.f) || !std::isfinite(temperature)) return TIDAR_EINVAL;
+  if (B == 0) return TIDAR_OK;
+  if (!aligned(ar_logits, 16) || !aligned(q_logits, 16) || !aligned(cand, 4) || !aligned(accept_len, 4) ||
+      !aligned(next_cand, 4))
+    return TIDAR_EINVAL;
+  if (k > 1 && !aligned(draft_logits, 16)) return TIDAR_EINVAL;
+  if (!aligned(workspace, 256) || workspace_bytes < p.total) return TIDAR_EWORKSPACE;
+
+  tidar::SampleArgs a;
+  a.ar_logits = ar_logits;
+  a.q_logits = q_logits;
+  a.draft_logits = draft_logits;
+  a.cand = cand;
+  a.accept_len = accept_len;
+  a.next_cand = next_cand;
+  char* ws = static_cast<char*>(workspace);
+  a.stats = reinterpret_cast<float2*>(ws);
+  a.resid = reinterpret_cast<float4*>(ws + p.stats_bytes);
+  a.part = reinterpret_cast<float2*>(ws + p.stats_bytes + p.resid_bytes);
+  a.part_fb = reinterpret_cast<float2*>(ws + p.stats_bytes + p.resid_bytes + p.part_bytes);
+  a.B = B;
+  a.k = k;
+  a.V = V;
+  a.n_chunks = p.n_chunks;
+  a.zscale = (float)(1.4426950408889634074 / (double)temperature);
+  a.key0 = (uint32_t)seed;
+  a.key1 = (uint32_t)(seed >> 32);
+  a.step = step;
+  const hipError_t e = tidar::launch_verify_sample(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
 }
 

@@ -47,6 +47,26 @@ struct VerifyArgs {
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
 
+constexpr int kSampleChunk = 4096;  // vocabulary entries per workgroup of the sampling kernels
+
+struct SampleArgs {
+  const float* ar_logits;     // [B][k+1][V]
+  const float* q_logits;      // [B][k][V]
+  const float* draft_logits;  // [B][k][k][V]
+  const int32_t* cand;        // [B][k]
+  int32_t* accept_len;
+  int32_t* next_cand;
+  float2* stats;    // [2*B*k][n_chunks] (max, sum of exp2) of z = logit * zscale
+  float4* resid;    // [B] (Mp, Zp, Mq, Zq) of the first rejected candidate's rows
+  float2* part;     // [B*k][n_chunks] (score, index bits) of the draws
+  float2* part_fb;  // [B][n_chunks]   the draw from p for the residual row
+  int B, k, V, n_chunks;
+  float zscale;     // log2(e) / T
+  unsigned key0, key1, step;
+};
+
+hipError_t launch_verify_sample(const SampleArgs& a, hipStream_t s);
+
 struct CommitArgs {
   void* k_cache;
   void* v_cache;

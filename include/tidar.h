@@ -149,6 +149,53 @@ int tidar_verify_greedy(int B, int k, int V, const float* ar_logits, const float
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Stochastic verification (temperature T > 0) and sampling of the next drafts.
+ *
+ * The final tokens are sampled autoregressively and the output matches
+ * sampling the AR model alone (engineer-news.pages.dev page, section on what
+ * TiDAR does; nodesdaily.com page, paragraph on the reported numbers).  The
+ * rule used is speculative sampling, with p_i = softmax(ar_logits[b][i] / T)
+ * and q_i = softmax(q_logits[b][i] / T), the distribution candidate i was
+ * drawn from:
+ *   candidate i (token x = cand[b][i]) is kept when u_i * q_i(x) < p_i(x);
+ *   accept_len[b] = a, the first i < k that is not kept (k if all are);
+ *   next_cand[b][0] is drawn from max(0, p_a - q_a) (normalised) if a < k,
+ *                   from p_k if a == k (from p_a if max(0, p_a - q_a) has no
+ *                   positive entry in fp32);
+ *   g = max(a, 1) - 1;
+ *   next_cand[b][m] is drawn from softmax(draft_logits[b][g][m] / T), m >= 1.
+ * Every random number comes from Philox4x32-10 (Salmon et al., SC 2011) with
+ * key (seed & 0xFFFFFFFF, seed >> 32) and a 32-bit output x mapped to
+ * u = ((x >> 9) + 0.5) * 2^-23:
+ *   u_i of the keep test: counter (i, 0xFFFFFFFF, b, step), word 0;
+ *   the draw of row j (0 = next_cand[b][0], m = next_cand[b][m]) is
+ *   argmax_v (log w_v - log(-log u_v)) (Gumbel-max, ties to the lower v)
+ *   with u_v from counter (v / 4, j, b, step), word v % 4.
+ * Identical (seed, step) give identical results; a caller advances `step`
+ * between decode steps.  Probabilities are computed in fp32; a decision
+ * within fp32 rounding of its threshold may differ from an exact evaluation.
+ *
+ *   temperature  finite and > 0 (TIDAR_EINVAL otherwise).
+ *   ar_logits    [B][k+1][V] f32 as for tidar_verify_greedy.
+ *   q_logits     [B][k][V] f32: row i is the distribution candidate i was
+ *                drawn from (row 0: the carried AR row, so candidate 0 is
+ *                always kept when q_logits[b][0] == ar_logits[b][0]).
+ *   draft_logits [B][k][k][V] f32; only group g's rows 1..k-1 are read.
+ *                May be NULL when k == 1.
+ *   Logits may be -inf (a zero weight) but every row needs a finite entry;
+ *   +inf and NaN are not allowed.  A candidate outside [0, V) is rejected.
+ *   cand         [B][k] int32.
+ *   accept_len   [B] int32 (written);  next_cand [B][k] int32 (written).
+ *   workspace    at least tidar_verify_sample_workspace() bytes.
+ * ---------------------------------------------------------------------- */
+int tidar_verify_sample_workspace(int B, int k, int V, size_t* bytes);
+
+int tidar_verify_sample(int B, int k, int V, float temperature, const float* ar_logits, const float* q_logits,
+                        const float* draft_logits, const int32_t* cand, uint64_t seed, uint32_t step,
+                        int32_t* accept_len, int32_t* next_cand, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* ------------------------------------------------------------------------
  * KV-cache commit / evict, in place.
  *
  * The settled cache is reused and rejected entries are evicted

@@ -36,7 +36,12 @@ half of the grid falls between fp32 values and its top rounds to 1.0).
 
 Everything is float64 here; the GPU computes the same quantities in fp32,
 so a decision may differ only where the two compared values are within
-rounding of each other -- decision_margins() reports how close each one is.
+rounding of each other.  With margins=True the oracle reports, for each
+decision, how far it is from flipping: the keep test's |u q - p| /
+max(u q, p) and a draw's gap between the best and runner-up Gumbel scores
+(a relative change e of the weights moves a score by at most e); for the
+residual draw, the gap left after a worst-case move of 1e-4 (p + q) of
+every weight.
 
 Pins (tests/test_oracle_verify_sample.py): the published Philox4x32-10
 known-answer vectors; the first emitted token is distributed as p (the
@@ -107,14 +112,39 @@ def softmax(logits, T):
     return e / e.sum()
 
 
-def gumbel_draw(weights, u):
-    """argmax_v (log w_v + G(u_v)); zero weights never win.  Returns (index,
-    gap between the best and second-best perturbed values)."""
+def gumbel_top2(weights, u):
+    """Gumbel-max scores argmax_v (log w_v + G(u_v)); zero weights never win.
+    Returns (best index, runner-up index, gap between their scores)."""
     with np.errstate(divide="ignore"):
         score = np.log(np.asarray(weights, dtype=np.float64)) - np.log(-np.log(u))
     order = np.argsort(-score, kind="stable")
-    gap = float(score[order[0]] - score[order[1]]) if len(score) > 1 else np.inf
-    return int(order[0]), gap
+    if len(score) == 1:
+        return int(order[0]), int(order[0]), np.inf
+    return int(order[0]), int(order[1]), float(score[order[0]] - score[order[1]])
+
+
+def gumbel_draw(weights, u):
+    """(index drawn with probability w / sum(w), gap to the runner-up score)."""
+    first, _, gap = gumbel_top2(weights, u)
+    return first, gap
+
+
+RESIDUAL_EPS = 1e-4
+
+
+def _residual_margin(w, p, q, u, first):
+    """Score gap of a residual draw that survives moving every weight w_v by
+    RESIDUAL_EPS * (p_v + q_v) against the drawn entry (p - q loses relative
+    precision where p and q nearly cancel); <= 0 when it does not survive."""
+    G = -np.log(-np.log(u))
+    slack = RESIDUAL_EPS * (p + q)
+    lo = w[first] - slack[first]
+    if not lo > 0:
+        return 0.0
+    with np.errstate(divide="ignore"):
+        hi = np.log(w + slack) + G
+    hi[first] = -np.inf
+    return float(np.log(lo) + G[first] - hi.max())
 
 
 def verify_sample_ref(ar_logits, q_logits, draft_logits, cand, T, seed, step, margins=False):
@@ -138,20 +168,24 @@ def verify_sample_ref(ar_logits, q_logits, draft_logits, cand, T, seed, step, ma
             x = int(cand[b, i])
             u = accept_uniform(seed, step, b, i)
             lhs, rhs = u * q[x], p[x]
-            mg.append(abs(lhs - rhs) / max(lhs, rhs, 1e-300))
+            # p(x) == 0 (a -inf logit) rejects exactly in any precision
+            mg.append(np.inf if rhs == 0 else abs(lhs - rhs) / max(lhs, rhs))
             if not lhs < rhs:
                 a = i
                 break
         accept[b] = a
+        u0 = row_uniforms(seed, step, b, 0, V)
         if a < k:
             p = softmax(ar_logits[b, a], T)
             q = softmax(q_logits[b, a], T)
             w = np.maximum(0.0, p - q)
             if not w.sum() > 0:  # p == q: every draw would have been kept
-                w = p
+                nxt[b, 0], gap = gumbel_draw(p, u0)
+            else:
+                nxt[b, 0], _ = gumbel_draw(w, u0)
+                gap = _residual_margin(w, p, q, u0, nxt[b, 0])
         else:
-            w = softmax(ar_logits[b, k], T)
-        nxt[b, 0], gap = gumbel_draw(w, row_uniforms(seed, step, b, 0, V))
+            nxt[b, 0], gap = gumbel_draw(softmax(ar_logits[b, k], T), u0)
         mg.append(gap)
         g = max(a, 1) - 1
         for m in range(1, k):

@@ -115,3 +115,30 @@ def test_commit_validation(T):
     assert L.tidar_kv_commit(0, 2, 8, 128, 60, 72, 8, p, p, p, p, p, p, None, None) == -1
     assert L.tidar_kv_commit(0, 2, 8, 128, 64, 72, 8, p, None, p, p, p, p, None, None) == -1
     assert L.tidar_kv_commit(0, 0, 8, 128, 64, 72, 8, None, None, None, None, None, None, None, None) == 0
+
+
+def test_verify_sample_validation_and_size(T):
+    n = ctypes.c_size_t(0)
+    L = T.lib()
+    assert L.tidar_verify_sample_workspace(16, 8, 128256, ctypes.byref(n)) == 0
+    chunks = -(-128256 // 4096)
+    # (max, sum) per chunk of 2k rows, (Mp, Zp, Mq, Zq) per sequence, draws per chunk of k rows, fallback draws
+    want = sum(-(-x // 256) * 256 for x in (16 * 16 * chunks * 8, 16 * 16, 16 * 8 * chunks * 8, 16 * chunks * 8))
+    assert n.value == want
+    assert L.tidar_verify_sample_workspace(16, 17, 100, ctypes.byref(n)) == -2
+    assert L.tidar_verify_sample_workspace(16, 0, 100, ctypes.byref(n)) == -1
+    assert L.tidar_verify_sample_workspace(4096, 16, 100, ctypes.byref(n)) == -2  # 2*B*k workgroup rows
+    p = ctypes.c_void_p(0x100000)
+    f = L.tidar_verify_sample
+    args = [2, 4, 100, 0.8, p, p, p, p, 1, 0, p, p, p, 1 << 20, None]
+    small_ws = list(args); small_ws[13] = 8
+    assert f(*small_ws) == -3
+    for T_bad in (0.0, -1.0, float("inf"), float("nan")):
+        bad_t = list(args); bad_t[3] = T_bad
+        assert f(*bad_t) == -1, T_bad
+    no_q = list(args); no_q[5] = None
+    assert f(*no_q) == -1
+    no_draft = list(args); no_draft[6] = None
+    assert f(*no_draft) == -1
+    empty = [0, 4, 100, 0.8] + [None] * 4 + [1, 0] + [None] * 3 + [0, None]
+    assert f(*empty) == 0

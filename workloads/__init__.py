@@ -41,6 +41,7 @@ import numpy as np
 _T_Q, _T_KS, _T_VS, _T_KC, _T_VC, _T_LENS = 1, 2, 3, 4, 5, 6
 _T_AR, _T_DRAFT, _T_CAND, _T_ACC, _T_BOOST = 11, 12, 13, 14, 15
 _T_TINY_W, _T_PROMPT, _T_INJECT = 21, 22, 23
+_T_QLOG, _T_QBOOST, _T_SHIFT, _T_MASK = 31, 32, 33, 34
 
 MASK_TOKEN_TINY = 1024  # extra embedding row of the tiny decoder; outside its LM head
 VPAGE = 64  # positions per value-cache page
@@ -277,6 +278,39 @@ def verify_inputs(B: int, k: int, V: int, seed: int, step: int = 0, config_id: i
     elif accept != "none":
         raise ValueError(accept)
     return {"ar_logits": ar, "draft_logits": dr, "cand": cand, "planted": planted}
+
+
+def sample_inputs(B: int, k: int, V: int, seed: int, step: int = 0, config_id: int = 0,
+                  carried: bool = True, masked: float = 0.0, shift=(-3.0, 1.0)) -> dict:
+    """Inputs of stochastic verification: ar/q/draft logits N(0,1) float32 and
+    candidate ids uniform in [0, V).  Each candidate's proposal logit gets a
+    boost U(2, 5) and its AR logit that boost plus a shift U(shift), by
+    default U(-3, 1), so the probability of keeping it ranges from small to
+    certain.
+
+    carried: q row 0 is a copy of ar row 0 (the carried AR row, the usual
+    case); otherwise it is drawn like the others.  masked: fraction of the
+    logits of every row set to -inf (a filtered vocabulary); a candidate's
+    proposal logit is never masked, its AR logit may be."""
+    ar = _normal(generator(seed, config_id, step, _T_AR), (B, k + 1, V))
+    q = _normal(generator(seed, config_id, step, _T_QLOG), (B, k, V))
+    dr = _normal(generator(seed, config_id, step, _T_DRAFT), (B, k, k, V)) if k > 1 else None
+    cand = generator(seed, config_id, step, _T_CAND).integers(0, V, size=(B, k)).astype(np.int32)
+    boost = generator(seed, config_id, step, _T_QBOOST).uniform(2.0, 5.0, size=(B, k)).astype(np.float32)
+    shift = generator(seed, config_id, step, _T_SHIFT).uniform(shift[0], shift[1], size=(B, k)).astype(np.float32)
+    if masked > 0:
+        g = generator(seed, config_id, step, _T_MASK)
+        for t in (ar, q) + ((dr,) if dr is not None else ()):
+            t[g.random(size=t.shape) < masked] = -np.inf
+        for t in (ar, q) + ((dr,) if dr is not None else ()):  # every row keeps a finite entry
+            t[..., 0] = np.where(np.isfinite(t[..., 0]), t[..., 0], np.float32(0.0))
+    bi = np.arange(B)[:, None]
+    ii = np.arange(k)[None, :]
+    q[bi, ii, cand] = np.where(np.isfinite(q[bi, ii, cand]), q[bi, ii, cand], np.float32(0.0)) + boost
+    ar[bi, ii, cand] = ar[bi, ii, cand] + boost + shift
+    if carried:
+        q[:, 0] = ar[:, 0]
+    return {"ar_logits": ar, "q_logits": q, "draft_logits": dr, "cand": cand}
 
 
 # ----------------------------------------------------------------------------- tiny decoder
