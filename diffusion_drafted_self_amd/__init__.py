@@ -1,8 +1,9 @@
 """TiDAR decode-step hot path on MI355X (gfx950): thin Python binding.
 
-The calls of ``include/tidar.h`` -- ``step_attention``, ``verify_greedy``,
-``verify_sample`` and ``kv_commit`` -- under the same names, taking torch
-tensors that live on the GPU.  This module only checks shapes and dtypes,
+The calls of ``include/tidar.h`` -- ``step_attention``,
+``step_attention_paged``, ``verify_greedy``, ``verify_sample``, ``kv_commit``
+and ``kv_commit_paged`` -- under the same names, taking torch tensors that
+live on the GPU.  This module only checks shapes and dtypes,
 marshals pointers and the current HIP stream, and allocates outputs /
 workspace with torch when the caller does not pass them.  Every step of the
 computation runs in the HIP kernels of ``libtidar.so``; there is no other
@@ -13,6 +14,9 @@ Tensor layouts (row-major, contiguous):
   q [B][R][Hq][D], k_step/v_step [B][R][Hkv][D],
   k_cache [B][Hkv][S_max][D], v_cache [B][Hkv][S_max/64][D][64] (values in
   pages of 64 positions, each page transposed),
+  paged caches: k_pool [n_pages][Hkv][64][D], v_pool [n_pages][Hkv][D][64],
+  block_table [B][max_pages] int32 (position p of sequence b is row p % 64 of
+  page block_table[b][p // 64]),
   lens [B] int32, ar_logits [B][k+1][V] f32, q_logits [B][k][V] f32,
   draft_logits [B][k][k][V] f32, cand [B][k] int32.
 """
@@ -42,6 +46,8 @@ SIGNATURES = {
     "tidar_verify_sample": (_c_int, [_c_int] * 3 + [_f] + [_p] * 4 + [ctypes.c_uint64, ctypes.c_uint32]
                             + [_p] * 3 + [_c_size, _p]),
     "tidar_kv_commit": (_c_int, [_c_int] * 7 + [_p] * 7 + [_p]),
+    "tidar_step_attention_paged": (_c_int, [_c_int] * 10 + [_f, _c_int] + [_p] * 10 + [_c_size, _p]),
+    "tidar_kv_commit_paged": (_c_int, [_c_int] * 8 + [_p] * 8 + [_p]),
 }
 
 
@@ -196,6 +202,56 @@ def step_attention(q, k_step, v_step, k_cache, v_cache, lens, k: int, n_groups: 
     return out, lse
 
 
+def step_attention_paged(q, k_step, v_step, k_pool, v_pool, block_table, lens, k: int, n_groups: int,
+                         sm_scale: float, max_len: int = None, out=None, lse=None, want_lse: bool = True,
+                         workspace=None, kv_chunk: int = 0):
+    """Structured-mask attention of one TiDAR step over paged caches (bf16).
+    Returns (out, lse)."""
+    _need(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    B, R, Hq, D = q.shape
+    _need(k_step, "k_step", torch.bfloat16, 4, dev)
+    _need(v_step, "v_step", torch.bfloat16, 4, dev)
+    _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
+    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(lens, "lens", torch.int32, 1, dev)
+    Hkv = k_step.shape[2]
+    n_pages = k_pool.shape[0]
+    max_pages = block_table.shape[1]
+    if R != k + n_groups * k:
+        raise ValueError(f"q has {R} step rows, expected k + n_groups*k = {k + n_groups * k}")
+    if tuple(k_step.shape) != (B, R, Hkv, D) or tuple(v_step.shape) != (B, R, Hkv, D):
+        raise ValueError("k_step/v_step must be [B][R][Hkv][D]")
+    if tuple(k_pool.shape) != (n_pages, Hkv, VALUE_PAGE, D) or tuple(v_pool.shape) != (n_pages, Hkv, D, VALUE_PAGE):
+        raise ValueError("k_pool must be [n_pages][Hkv][64][D] and v_pool [n_pages][Hkv][D][64]")
+    if block_table.shape[0] != B or lens.shape[0] != B:
+        raise ValueError("block_table must be [B][max_pages] and lens [B]")
+    if max_len is None:
+        max_len = int(lens.max().item()) if B > 0 else 0
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, 4, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, R), dtype=torch.float32, device=dev)
+    elif lse is not None:
+        _need(lse, "lse", torch.float32, 3, dev)
+        if tuple(lse.shape) != (B, Hq, R):
+            raise ValueError("lse must be [B][Hq][R]")
+    nbytes = step_attention_workspace_bytes(TIDAR_BF16, B, Hq, Hkv, D, max_pages * VALUE_PAGE, max_len, k,
+                                            n_groups, kv_chunk)
+    ws = _workspace(nbytes, dev, workspace)
+    _check("tidar_step_attention_paged",
+           lib().tidar_step_attention_paged(TIDAR_BF16, B, Hq, Hkv, D, max_pages, n_pages, int(max_len), k,
+                                           n_groups, float(sm_scale), int(kv_chunk), _ptr(q), _ptr(k_step),
+                                           _ptr(v_step), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                           _ptr(lens), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream()))
+    return out, lse
+
+
 # ------------------------------------------------------------------------ verify
 def verify_workspace_bytes(B: int, k: int, V: int) -> int:
     n = _c_size(0)
@@ -298,5 +354,35 @@ def kv_commit(k_cache, v_cache, lens, k_step, v_step, accept_len, k: int, err_fl
     return err_flags
 
 
+def kv_commit_paged(k_pool, v_pool, block_table, lens, k_step, v_step, accept_len, k: int, err_flags=None):
+    """Append the accepted candidate rows into their pages in place and
+    advance ``lens``.  Returns ``err_flags`` (or None when not requested)."""
+    _need(k_pool, "k_pool", ndim=4)
+    dev, dt = k_pool.device, k_pool.dtype
+    n_pages, Hkv, _, D = k_pool.shape
+    _need(v_pool, "v_pool", dt, 4, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(k_step, "k_step", dt, 4, dev)
+    _need(v_step, "v_step", dt, 4, dev)
+    _need(lens, "lens", torch.int32, 1, dev)
+    _need(accept_len, "accept_len", torch.int32, 1, dev)
+    B, R = k_step.shape[0], k_step.shape[1]
+    max_pages = block_table.shape[1]
+    if tuple(k_pool.shape) != (n_pages, Hkv, VALUE_PAGE, D) or tuple(v_pool.shape) != (n_pages, Hkv, D, VALUE_PAGE):
+        raise ValueError("k_pool must be [n_pages][Hkv][64][D] and v_pool [n_pages][Hkv][D][64]")
+    if tuple(k_step.shape) != (B, R, Hkv, D) or tuple(v_step.shape) != (B, R, Hkv, D):
+        raise ValueError("k_step/v_step must be [B][R][Hkv][D]")
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must be [B][max_pages]")
+    if err_flags is not None:
+        _need(err_flags, "err_flags", torch.int32, 1, dev)
+    _check("tidar_kv_commit_paged",
+           lib().tidar_kv_commit_paged(_dtype_code(k_pool), B, Hkv, D, max_pages, n_pages, R, k, _ptr(k_pool),
+                                      _ptr(v_pool), _ptr(block_table), _ptr(lens), _ptr(k_step), _ptr(v_step),
+                                      _ptr(accept_len), _ptr(err_flags), _stream()))
+    return err_flags
+
+
 __all__ = ["step_attention", "step_attention_workspace_bytes", "verify_greedy", "verify_workspace_bytes",
-           "verify_sample", "verify_sample_workspace_bytes", "kv_commit", "strerror", "lib", "TidarError", "LIB_PATH", "SIGNATURES"]
+           "verify_sample", "verify_sample_workspace_bytes", "kv_commit",
+           "step_attention_paged", "kv_commit_paged", "strerror", "lib", "TidarError", "LIB_PATH", "SIGNATURES"]

@@ -48,6 +48,26 @@ __device__ __forceinline__ size_t vpos(int d, int c, int D) {  // element (d, po
   return (size_t)(c / VPAGE) * D * VPAGE + (size_t)d * VPAGE + (c % VPAGE);
 }
 
+// Where tile t (settled positions 64t .. 64t+63) of one (sequence, KV head)
+// lives: its 64 key rows start at ktile(t), its transposed value page at
+// vtile(t).  Contiguous caches: tile t of the pair's own region.  Paged
+// caches: page table[t] of the pools ([n_pages][Hkv][64][D] keys,
+// [n_pages][Hkv][D][64] values), this KV head's slot at the same offset in
+// every page.  Only tiles holding settled positions may be asked for.
+template <int D, bool PAGED>
+struct KvMap {
+  const bf16* k;
+  const bf16* v;
+  const int32_t* tbl;  // this sequence's block-table row (paged)
+  size_t stride;       // elements from one page to the next
+  __device__ __forceinline__ size_t page(int t) const {
+    if constexpr (PAGED) return (size_t)tbl[t];
+    else return (size_t)t;
+  }
+  __device__ __forceinline__ const bf16* ktile(int t) const { return k + page(t) * stride; }
+  __device__ __forceinline__ const bf16* vtile(int t) const { return v + page(t) * stride; }
+};
+
 // LDS tile geometry.  K tile: TK rows of D bf16, row-major; V^T tile: D rows
 // of TK bf16.  Both are filled 1 KB at a time by direct global->LDS loads
 // (each lane moves 16 B; lane t lands at byte 16t of the 1 KB block), so a
@@ -159,29 +179,30 @@ __device__ __forceinline__ void dma_plan(DmaPlan<D>& pl, int wave, int lane) {
   }
 }
 
-// This wave's share of the direct loads of K tile / V^T tile (keys t0..t0+TK-1,
-// all settled): 64 contiguous cache rows, one contiguous value page.
+// This wave's share of the direct loads of a K tile / V^T tile (a tile of
+// 64 settled keys): 64 contiguous cache rows, one contiguous value page.
 template <int D>
-__device__ __forceinline__ void issue_k(lds_char* sK, const bf16* kc_base, const DmaPlan<D>& pl, int t0, int wave) {
+__device__ __forceinline__ void issue_k(lds_char* sK, const bf16* ktile, const DmaPlan<D>& pl, int wave) {
   using T = Tile<D>;
-  const char* kt = (const char*)(kc_base + (size_t)t0 * D);
+  const char* kt = (const char*)ktile;
 #pragma unroll
   for (int ii = 0; ii < T::NKW; ++ii) dma_b128(kt, pl.k[ii], sK + (wave * T::NKW + ii) * 1024);
 }
 template <int D>
-__device__ __forceinline__ void issue_v(lds_char* sV, const bf16* vc_base, const DmaPlan<D>& pl, int t0, int wave) {
+__device__ __forceinline__ void issue_v(lds_char* sV, const bf16* vtile, const DmaPlan<D>& pl, int wave) {
   using T = Tile<D>;
-  const char* vt = (const char*)(vc_base + (size_t)(t0 / VPAGE) * D * VPAGE);
+  const char* vt = (const char*)vtile;
 #pragma unroll
   for (int ii = 0; ii < T::NVW; ++ii) dma_b128(vt, pl.v[ii], sV + (wave * T::NVW + ii) * 1024);
 }
 
 // Stage a tile that reaches past the settled prefix (the step block, or
 // keys past the end) into the same swizzled layout.  Settled keys come from
-// the caches in 16 B pieces; step rows are read 16 B at a time and their
-// values scattered into V^T columns; everything else is zero.
+// the tile's cache rows `kt` / value page `vt` (null when the tile holds no
+// settled position) in 16 B pieces; step rows are read 16 B at a time and
+// their values scattered into V^T columns; everything else is zero.
 template <int D>
-__device__ __forceinline__ void stage_tail_tile(lds_char* sK, lds_char* sV, const bf16* kc_base, const bf16* vc_base,
+__device__ __forceinline__ void stage_tail_tile(lds_char* sK, lds_char* sV, const bf16* kt, const bf16* vt,
                                                 const bf16* ks_base, const bf16* vs_base, size_t step_stride,
                                                 int t0, int L, int Ltot, int tid) {
   using T = Tile<D>;
@@ -189,7 +210,7 @@ __device__ __forceinline__ void stage_tail_tile(lds_char* sK, lds_char* sV, cons
     const int row = id / T::KPPR, p = id % T::KPPR;
     const int c = t0 + row;
     bf16x8 val = {};
-    if (c < L) val = *(const bf16x8*)(kc_base + (size_t)c * D + p * 8);
+    if (c < L) val = *(const bf16x8*)(kt + (size_t)row * D + p * 8);
     else if (c < Ltot) val = *(const bf16x8*)(ks_base + (size_t)(c - L) * step_stride + p * 8);
     *(lds_bf16x8*)(sK + row * T::KROW + ((p ^ kswz<D>(row)) * 16)) = val;
   }
@@ -199,10 +220,10 @@ __device__ __forceinline__ void stage_tail_tile(lds_char* sK, lds_char* sV, cons
     const int c0 = t0 + q * 8;
     bf16x8 val = {};
     if (c0 + 8 <= L) {
-      val = *(const bf16x8*)(vc_base + vpos(d, c0, D));
+      val = *(const bf16x8*)(vt + (size_t)d * VPAGE + q * 8);
     } else if (c0 < L) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) val[e] = c0 + e < L ? vc_base[vpos(d, c0 + e, D)] : (bf16)0.f;
+      for (int e = 0; e < 8; ++e) val[e] = c0 + e < L ? vt[(size_t)d * VPAGE + q * 8 + e] : (bf16)0.f;
     }
     *(lds_bf16x8*)(sV + d * T::VROW + ((q ^ vswz(d)) * 16)) = val;
   }
@@ -565,7 +586,7 @@ __device__ __forceinline__ void pv_tile(const lds_char* sV, const Probs<NF, NS>&
 // softmax(t) | scores(t+1) | P.V(t-1).  Tiles that reach past the settled
 // prefix are staged through registers into the last slots first, before
 // the ring fills them.
-template <int D, int NF, int NS>
+template <int D, int NF, int NS, bool PAGED>
 __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_pipe_bf16_kernel(AttnArgs a) {
   using T = Tile<D>;
@@ -615,7 +636,27 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
   };
 
   const int L = a.lens[b];
-  if (L < 0 || L > a.max_len) {  // contract violation: NaN rows, written once
+  KvMap<D, PAGED> kv;
+  const size_t pair = (size_t)b * a.Hkv + kvh;
+  if constexpr (PAGED) {
+    kv.k = (const bf16*)a.k_cache + (size_t)kvh * TK * D;
+    kv.v = (const bf16*)a.v_cache + (size_t)kvh * D * TK;
+    kv.tbl = a.block_table + (size_t)b * a.max_pages;
+    kv.stride = (size_t)a.Hkv * TK * D;
+  } else {
+    kv.k = (const bf16*)a.k_cache + pair * a.S_max * D;
+    kv.v = (const bf16*)a.v_cache + pair * D * a.S_max;
+    kv.tbl = nullptr;
+    kv.stride = (size_t)TK * D;
+  }
+  bool violated = L < 0 || L > a.max_len;
+  if constexpr (PAGED) {  // every page holding a settled position must be in the pools
+    bool bad = false;
+    if (!violated)
+      for (int pg = tid; pg < (L + TK - 1) / TK; pg += NWV * 64) bad |= (unsigned)kv.tbl[pg] >= (unsigned)a.n_pages;
+    violated |= __syncthreads_or(bad) != 0;
+  }
+  if (violated) {  // contract violation: NaN rows, written once
     if (split == 0) {
       auto nan_row = [&](int m) {
         bf16* orow = out_row(m);
@@ -638,9 +679,6 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
   const int ke = min(kb + a.chunk, Ltot);
   const int n_valid = (Ltot + a.chunk - 1) / a.chunk;
 
-  const size_t pair = (size_t)b * a.Hkv + kvh;
-  const bf16* kc_base = (const bf16*)a.k_cache + pair * a.S_max * D;
-  const bf16* vc_base = (const bf16*)a.v_cache + pair * D * a.S_max;
   const size_t step_stride = (size_t)a.Hkv * D;
   const bf16* ks_base = (const bf16*)a.k_step + (size_t)b * a.R * step_stride + kvh * D;
   const bf16* vs_base = (const bf16*)a.v_step + (size_t)b * a.R * step_stride + kvh * D;
@@ -653,11 +691,12 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
   auto kslot = [&](int j) { return sK0 + (j & (RING - 1)) * T::K_BYTES; };
   auto vslot = [&](int j) { return sV0 + (j & (RING - 1)) * T::V_BYTES; };
   // ring prologue, as iterations -3..-1 would issue it: K(0); K(1), V(0); K(2), V(1)
-  if (n > 0) issue_k<D>(kslot(0), kc_base, plan, kb, wave);
-  if (n > 1) issue_k<D>(kslot(1), kc_base, plan, kb + TK, wave);
-  if (n > 0) issue_v<D>(vslot(0), vc_base, plan, kb, wave);
-  if (n > 2) issue_k<D>(kslot(2), kc_base, plan, kb + 2 * TK, wave);
-  if (n > 1) issue_v<D>(vslot(1), vc_base, plan, kb + TK, wave);
+  const int tb = kb / TK;  // the chunk's first tile
+  if (n > 0) issue_k<D>(kslot(0), kv.ktile(tb), plan, wave);
+  if (n > 1) issue_k<D>(kslot(1), kv.ktile(tb + 1), plan, wave);
+  if (n > 0) issue_v<D>(vslot(0), kv.vtile(tb), plan, wave);
+  if (n > 2) issue_k<D>(kslot(2), kv.ktile(tb + 2), plan, wave);
+  if (n > 1) issue_v<D>(vslot(1), kv.vtile(tb + 1), plan, wave);
 
   QFrags<D, NF, NS> q;
   auto load_q = [&](int m, bool ok_row, bf16x8 (&dst)[D / 32]) {
@@ -701,7 +740,9 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
       lds_char* sK = kslot(RING - 1);
       lds_char* sV = vslot(RING - 1);
       barrier();
-      stage_tail_tile<D>(sK, sV, kc_base, vc_base, ks_base, vs_base, step_stride, t0, L, Ltot, tid);
+      const bool settled = t0 < L;  // the tile holds settled positions (its page is in the table)
+      stage_tail_tile<D>(sK, sV, settled ? kv.ktile(t0 / TK) : nullptr, settled ? kv.vtile(t0 / TK) : nullptr,
+                         ks_base, vs_base, step_stride, t0, L, Ltot, tid);
       wait_all();
       barrier();
       s_tile<D, NF, NS>(sK, q, sA, lane, wave);
@@ -761,8 +802,8 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
       else wait_vmcnt<T::NVW>();
       wait_lgkmcnt0();
       barrier();
-      if (it + 3 < n) issue_k<D>(kslot(it + 3), kc_base, plan, kb + (it + 3) * TK, wave);
-      if (it + 2 < n) issue_v<D>(vslot(it + 2), vc_base, plan, kb + (it + 2) * TK, wave);
+      if (it + 3 < n) issue_k<D>(kslot(it + 3), kv.ktile(tb + it + 3), plan, wave);
+      if (it + 2 < n) issue_v<D>(vslot(it + 2), kv.vtile(tb + it + 2), plan, wave);
     };
     bool overflow = false;
     auto commit_sum = [&](bool big, const Probs<NF, NS>& pr) {
@@ -811,8 +852,8 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
       }
       for (int j = 0; j < n; ++j) {
         barrier();
-        issue_k<D>(kslot(0), kc_base, plan, kb + j * TK, wave);
-        issue_v<D>(vslot(0), vc_base, plan, kb + j * TK, wave);
+        issue_k<D>(kslot(0), kv.ktile(tb + j), plan, wave);
+        issue_v<D>(vslot(0), kv.vtile(tb + j), plan, wave);
         wait_vmcnt<0>();
         barrier();
         s_tile<D, NF, NS>(kslot(0), q, sA, lane, wave);
@@ -1024,7 +1065,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   float* lse = a.lse ? a.lse + ((size_t)b * a.Hq + h) * a.R + r : nullptr;
 
   const int L = a.lens[b];
-  if (L < 0 || L > a.max_len) {
+  bool violated = L < 0 || L > a.max_len;
+  if (a.block_table && !violated) {  // paged: the pages the split kernel checked
+    bool bad = false;
+    const int32_t* tbl = a.block_table + (size_t)b * a.max_pages;
+    for (int pg = lane; pg < (L + VPAGE - 1) / VPAGE; pg += 64) bad |= (unsigned)tbl[pg] >= (unsigned)a.n_pages;
+    violated = __any(bad);
+  }
+  if (violated) {
     for (int e = 0; e < E; ++e) store_out(orow + lane * E + e, NAN);
     if (lse && lane == 0) *lse = NAN;
     return;
@@ -1056,7 +1104,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 template <int D, int NF, int NS>
 hipError_t launch_bf16_pipe(const AttnArgs& a, hipStream_t s) {
   const int nblk = a.B * a.Hkv * a.n_split * a.n_rowblk;
-  hipLaunchKernelGGL((attn_pipe_bf16_kernel<D, NF, NS>), dim3(nblk), dim3(NWV * 64), 0, s, a);
+  if (a.block_table) hipLaunchKernelGGL((attn_pipe_bf16_kernel<D, NF, NS, true>), dim3(nblk), dim3(NWV * 64), 0, s, a);
+  else hipLaunchKernelGGL((attn_pipe_bf16_kernel<D, NF, NS, false>), dim3(nblk), dim3(NWV * 64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -170,39 +170,13 @@ int plan_sample(int B, int k, int V, SamplePlan* p) {
   return TIDAR_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* tidar_strerror(int status) {
-  switch (status) {
-    case TIDAR_OK: return "ok";
-    case TIDAR_EINVAL: return "invalid argument (shape, pointer, alignment or value)";
-    case TIDAR_EUNSUPPORTED: return "unsupported configuration (dtype, head dim, k or size)";
-    case TIDAR_EWORKSPACE: return "workspace missing or too small";
-    case TIDAR_ELAUNCH: return "kernel launch failed";
-    default: return "unknown status";
-  }
-}
-
-int tidar_abi_version(void) { return 1; }
-
-int tidar_step_attention_workspace(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_len,
-                                   int k, int n_groups, int kv_chunk, size_t* bytes) {
-  if (!bytes) return TIDAR_EINVAL;
-  AttnPlan p;
-  const int st = plan_attention(dtype, B, Hq, Hkv, D, S_max, max_len, k, n_groups, kv_chunk, &p);
-  if (st != TIDAR_OK) return st;
-  *bytes = p.total;
-  return TIDAR_OK;
-}
-
-int tidar_step_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_len,
-                         int k, int n_groups, float sm_scale, int kv_chunk,
-                         const void* q, const void* k_step, const void* v_step,
-                         const void* k_cache, const void* v_cache, const int32_t* lens,
-                         void* out, float* lse, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+// Both cache forms: block_table == nullptr for per-sequence contiguous
+// caches, else pools of n_pages pages with S_max = 64 * max_pages.
+int step_attention_impl(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_len, int k, int n_groups,
+                        float sm_scale, int kv_chunk, const void* q, const void* k_step, const void* v_step,
+                        const void* k_cache, const void* v_cache, const int32_t* block_table, int max_pages,
+                        int n_pages, const int32_t* lens, void* out, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   AttnPlan p;
   const int st = plan_attention(dtype, B, Hq, Hkv, D, S_max, max_len, k, n_groups, kv_chunk, &p);
   if (st != TIDAR_OK) return st;
@@ -244,10 +218,99 @@ int tidar_step_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, in
   a.n_rowblk = p.n_rowblk;
   a.scale_log2 = sm_scale * 1.44269504088896340736f;
   a.single_chunk_direct = dtype == TIDAR_BF16;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.n_pages = n_pages;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = dtype == TIDAR_BF16 ? tidar::launch_attention_bf16(a, s) : tidar::launch_attention_f32(a, s);
   return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
+}
+
+int kv_commit_impl(int dtype, int B, int Hkv, int D, int S_max, int R, int k, void* k_cache, void* v_cache,
+                   const int32_t* block_table, int max_pages, int n_pages, int32_t* lens, const void* k_step,
+                   const void* v_step, const int32_t* accept_len, int32_t* err_flags, void* stream) {
+  if (dtype != TIDAR_BF16 && dtype != TIDAR_F32) return TIDAR_EUNSUPPORTED;
+  if (D != 64 && D != 128) return TIDAR_EUNSUPPORTED;
+  if (B < 0 || Hkv < 1 || S_max < 1 || S_max % kValuePage != 0 || R < 1 || k < 1 || k > R) return TIDAR_EINVAL;
+  if (B == 0) return TIDAR_OK;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_step, 16) || !aligned(v_step, 16) ||
+      !aligned(lens, 4) || !aligned(accept_len, 4))
+    return TIDAR_EINVAL;
+  if (err_flags && !aligned(err_flags, 4)) return TIDAR_EINVAL;
+
+  tidar::CommitArgs a;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.lens = lens;
+  a.k_step = k_step;
+  a.v_step = v_step;
+  a.accept_len = accept_len;
+  a.err_flags = err_flags;
+  a.B = B;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.S_max = S_max;
+  a.R = R;
+  a.k = k;
+  a.elem_bytes = dtype == TIDAR_BF16 ? 2 : 4;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.n_pages = n_pages;
+  const hipError_t e = tidar::launch_commit(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tidar_strerror(int status) {
+  switch (status) {
+    case TIDAR_OK: return "ok";
+    case TIDAR_EINVAL: return "invalid argument (shape, pointer, alignment or value)";
+    case TIDAR_EUNSUPPORTED: return "unsupported configuration (dtype, head dim, k or size)";
+    case TIDAR_EWORKSPACE: return "workspace missing or too small";
+    case TIDAR_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int tidar_abi_version(void) { return 1; }
+
+int tidar_step_attention_workspace(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_len,
+                                   int k, int n_groups, int kv_chunk, size_t* bytes) {
+  if (!bytes) return TIDAR_EINVAL;
+  AttnPlan p;
+  const int st = plan_attention(dtype, B, Hq, Hkv, D, S_max, max_len, k, n_groups, kv_chunk, &p);
+  if (st != TIDAR_OK) return st;
+  *bytes = p.total;
+  return TIDAR_OK;
+}
+
+int tidar_step_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_len,
+                         int k, int n_groups, float sm_scale, int kv_chunk,
+                         const void* q, const void* k_step, const void* v_step,
+                         const void* k_cache, const void* v_cache, const int32_t* lens,
+                         void* out, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return step_attention_impl(dtype, B, Hq, Hkv, D, S_max, max_len, k, n_groups, sm_scale, kv_chunk, q, k_step,
+                             v_step, k_cache, v_cache, nullptr, 0, 0, lens, out, lse, workspace, workspace_bytes,
+                             stream);
+}
+
+int tidar_step_attention_paged(int dtype, int B, int Hq, int Hkv, int D, int max_pages, int n_pages, int max_len,
+                               int k, int n_groups, float sm_scale, int kv_chunk,
+                               const void* q, const void* k_step, const void* v_step,
+                               const void* k_pool, const void* v_pool, const int32_t* block_table,
+                               const int32_t* lens, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (dtype != TIDAR_BF16) return TIDAR_EUNSUPPORTED;  // paged pools: the bf16 kernels only
+  if (max_pages < 1 || max_pages > (1 << 24) || n_pages < 1) return TIDAR_EINVAL;
+  if (B > 0 && !aligned(block_table, 4)) return TIDAR_EINVAL;
+  return step_attention_impl(dtype, B, Hq, Hkv, D, max_pages * kValuePage, max_len, k, n_groups, sm_scale,
+                             kv_chunk, q, k_step, v_step, k_pool, v_pool, block_table, max_pages, n_pages, lens,
+                             out, lse, workspace, workspace_bytes, stream);
 }
 
 int tidar_verify_workspace(int B, int k, int V, size_t* bytes) {
@@ -342,32 +405,18 @@ int tidar_kv_commit(int dtype, int B, int Hkv, int D, int S_max, int R, int k,
                     void* k_cache, void* v_cache, int32_t* lens,
                     const void* k_step, const void* v_step, const int32_t* accept_len,
                     int32_t* err_flags, void* stream) {
-  if (dtype != TIDAR_BF16 && dtype != TIDAR_F32) return TIDAR_EUNSUPPORTED;
-  if (D != 64 && D != 128) return TIDAR_EUNSUPPORTED;
-  if (B < 0 || Hkv < 1 || S_max < 1 || S_max % kValuePage != 0 || R < 1 || k < 1 || k > R) return TIDAR_EINVAL;
-  if (B == 0) return TIDAR_OK;
-  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_step, 16) || !aligned(v_step, 16) ||
-      !aligned(lens, 4) || !aligned(accept_len, 4))
-    return TIDAR_EINVAL;
-  if (err_flags && !aligned(err_flags, 4)) return TIDAR_EINVAL;
+  return kv_commit_impl(dtype, B, Hkv, D, S_max, R, k, k_cache, v_cache, nullptr, 0, 0, lens, k_step, v_step,
+                        accept_len, err_flags, stream);
+}
 
-  tidar::CommitArgs a;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.lens = lens;
-  a.k_step = k_step;
-  a.v_step = v_step;
-  a.accept_len = accept_len;
-  a.err_flags = err_flags;
-  a.B = B;
-  a.Hkv = Hkv;
-  a.D = D;
-  a.S_max = S_max;
-  a.R = R;
-  a.k = k;
-  a.elem_bytes = dtype == TIDAR_BF16 ? 2 : 4;
-  const hipError_t e = tidar::launch_commit(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
+int tidar_kv_commit_paged(int dtype, int B, int Hkv, int D, int max_pages, int n_pages, int R, int k,
+                          void* k_pool, void* v_pool, const int32_t* block_table, int32_t* lens,
+                          const void* k_step, const void* v_step, const int32_t* accept_len,
+                          int32_t* err_flags, void* stream) {
+  if (max_pages < 1 || max_pages > (1 << 24) || n_pages < 1) return TIDAR_EINVAL;
+  if (B > 0 && !aligned(block_table, 4)) return TIDAR_EINVAL;
+  return kv_commit_impl(dtype, B, Hkv, D, max_pages * kValuePage, R, k, k_pool, v_pool, block_table, max_pages,
+                        n_pages, lens, k_step, v_step, accept_len, err_flags, stream);
 }
 
 }  // extern "C"

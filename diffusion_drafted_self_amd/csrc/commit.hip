@@ -9,6 +9,11 @@
 // their rows, values transposed into their 64-position value page -- then
 // advances lens in place.  Rejected candidates and slot rows are evicted by
 // never being written.  The work is a few KB per sequence: latency-bound.
+//
+// Paged caches: position p of sequence b lives in page table[b][p / 64] of
+// the pools (keys [n_pages][Hkv][64][D], values [n_pages][Hkv][D][64]), at
+// row p % 64.  The caller provides the pages; a page entry outside the pools
+// is reported and nothing of that sequence is written.
 #include "common.h"
 #include "launch.h"
 
@@ -25,7 +30,7 @@ namespace {
 // scatters its value piece (PER consecutive head-dim elements of one
 // position) into PER value-page rows.  The settled length moves after a
 // barrier that only orders it behind every thread's read of the old value.
-template <typename E, int D>
+template <typename E, int D, bool PAGED>
 __global__ __launch_bounds__(1024) void kv_commit_kernel(CommitArgs a) {
   constexpr int PER = 16 / sizeof(E);  // elements per 16 B piece
   constexpr int PPR = D / PER;         // pieces per row
@@ -38,6 +43,21 @@ __global__ __launch_bounds__(1024) void kv_commit_kernel(CommitArgs a) {
   const size_t row_stride = (size_t)a.Hkv * D;
   const E* ks = (const E*)a.k_step + (size_t)b * a.R * row_stride;
   const E* vs = (const E*)a.v_step + (size_t)b * a.R * row_stride;
+  // flags: 2 bad accept length, 1 capacity, 3 a page outside the pools.
+  // Paged: the (at most two) pages that positions L .. L+acc-1 fall in.
+  int pg0 = 0, pg1 = 0;
+  auto check = [&]() {
+    int f = (acc < 0 || acc > a.k) ? 2 : ((L < 0 || L + acc > a.S_max) ? 1 : 0);
+    if constexpr (PAGED) {
+      if (!f && acc > 0) {
+        const int32_t* tbl = a.block_table + (size_t)b * a.max_pages;
+        pg0 = tbl[L / 64];
+        pg1 = tbl[(L + acc - 1) / 64];
+        if ((unsigned)pg0 >= (unsigned)a.n_pages || (unsigned)pg1 >= (unsigned)a.n_pages) f = 3;
+      }
+    }
+    return f;
+  };
 
   for (int p0 = threadIdx.x; p0 < n_piece; p0 += kSlots * blockDim.x) {
     u32x4 kp[kSlots], vp[kSlots];
@@ -49,8 +69,7 @@ __global__ __launch_bounds__(1024) void kv_commit_kernel(CommitArgs a) {
         vp[u] = *(const u32x4*)(vs + (size_t)p * PER);
       }
     }
-    const int flag = (acc < 0 || acc > a.k) ? 2 : ((L < 0 || L + acc > a.S_max) ? 1 : 0);
-    if (flag) break;
+    if (check()) break;
 #pragma unroll
     for (int u = 0; u < kSlots; ++u) {
       const int p = p0 + u * blockDim.x;
@@ -59,18 +78,42 @@ __global__ __launch_bounds__(1024) void kv_commit_kernel(CommitArgs a) {
       const int h = ih % a.Hkv, i = ih / a.Hkv;
       if (i >= acc) continue;
       const int pos = L + i;
-      E* dk = (E*)a.k_cache + (((size_t)b * a.Hkv + h) * a.S_max + pos) * D + c * PER;
+      E* dk;
+      E* dv;
+      if constexpr (PAGED) {
+        const size_t slot = (size_t)(pos / 64 == L / 64 ? pg0 : pg1) * a.Hkv + h;  // (page, head)
+        dk = (E*)a.k_cache + (slot * 64 + pos % 64) * D + c * PER;
+        dv = (E*)a.v_cache + slot * D * 64 + pos % 64;
+      } else {
+        dk = (E*)a.k_cache + (((size_t)b * a.Hkv + h) * a.S_max + pos) * D + c * PER;
+        dv = (E*)a.v_cache + ((size_t)b * a.Hkv + h) * a.S_max * D + (size_t)(pos / 64) * D * 64 + pos % 64;
+      }
       *(u32x4*)dk = kp[u];
-      E* dv = (E*)a.v_cache + ((size_t)b * a.Hkv + h) * a.S_max * D + (size_t)(pos / 64) * D * 64 + pos % 64;
       const E* ve = (const E*)&vp[u];
 #pragma unroll
       for (int j = 0; j < PER; ++j) dv[(size_t)(c * PER + j) * 64] = ve[j];
     }
   }
-  const int flag = (acc < 0 || acc > a.k) ? 2 : ((L < 0 || L + acc > a.S_max) ? 1 : 0);
+  const int flag = check();
   if (threadIdx.x == 0 && a.err_flags) a.err_flags[b] = flag;
   __builtin_amdgcn_s_barrier();  // every thread has read lens[b]
   if (threadIdx.x == 0 && !flag) a.lens[b] = L + acc;
+}
+
+template <bool PAGED>
+void launch_paged(const CommitArgs& a, hipStream_t s, int threads) {
+  if (a.elem_bytes == 2) {
+    if (a.D == 128) hipLaunchKernelGGL((kv_commit_kernel<uint16_t, 128, PAGED>), dim3(a.B), dim3(threads), 0, s, a);
+    else hipLaunchKernelGGL((kv_commit_kernel<uint16_t, 64, PAGED>), dim3(a.B), dim3(threads), 0, s, a);
+  } else {
+    if (a.D == 128) hipLaunchKernelGGL((kv_commit_kernel<uint32_t, 128, PAGED>), dim3(a.B), dim3(threads), 0, s, a);
+    else hipLaunchKernelGGL((kv_commit_kernel<uint32_t, 64, PAGED>), dim3(a.B), dim3(threads), 0, s, a);
+  }
+}
+
+void launch_typed(const CommitArgs& a, hipStream_t s, int threads) {
+  if (a.block_table) launch_paged<true>(a, s, threads);
+  else launch_paged<false>(a, s, threads);
 }
 
 }  // namespace
@@ -79,14 +122,7 @@ hipError_t launch_commit(const CommitArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
   const int pieces = a.Hkv * a.k * a.D * a.elem_bytes / 16;
   const int threads = std::min(1024, std::max(64, ((pieces + 63) / 64) * 64));
-  if (a.elem_bytes == 2) {
-    if (a.D == 128) hipLaunchKernelGGL((kv_commit_kernel<uint16_t, 128>), dim3(a.B), dim3(threads), 0, s, a);
-    else hipLaunchKernelGGL((kv_commit_kernel<uint16_t, 64>), dim3(a.B), dim3(threads), 0, s, a);
-    // (bf16 elements move as raw 16-bit words)
-  } else {
-    if (a.D == 128) hipLaunchKernelGGL((kv_commit_kernel<uint32_t, 128>), dim3(a.B), dim3(threads), 0, s, a);
-    else hipLaunchKernelGGL((kv_commit_kernel<uint32_t, 64>), dim3(a.B), dim3(threads), 0, s, a);
-  }
+  launch_typed(a, s, threads);  // bf16 elements move as raw 16-bit words
   return hipGetLastError();
 }
 

@@ -28,6 +28,11 @@ struct AttnArgs {
                               // wave and tiles shared by key block; workgroups per (b, kvh)
   float scale_log2;     // sm_scale * log2(e)
   int single_chunk_direct;  // the split kernel writes sequences that fit one chunk (bf16 path)
+  // paged caches (bf16 path): k_cache / v_cache are pools of n_pages pages,
+  // block_table [B][max_pages] maps tile t of sequence b to its page;
+  // nullptr for per-sequence contiguous caches
+  const int32_t* block_table;
+  int max_pages, n_pages;
 };
 
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t s);
@@ -76,6 +81,8 @@ struct CommitArgs {
   const int32_t* accept_len;
   int32_t* err_flags;
   int B, Hkv, D, S_max, R, k, elem_bytes;
+  const int32_t* block_table;  // paged pools (S_max = 64 * max_pages), or nullptr
+  int max_pages, n_pages;
 };
 
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s);

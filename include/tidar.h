@@ -120,6 +120,41 @@ int tidar_step_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, in
                          void* stream);
 
 /* ------------------------------------------------------------------------
+ * Step attention over a paged (block-table) KV cache.
+ *
+ * The same computation as tidar_step_attention, with the settled keys and
+ * values held in pages of 64 positions drawn from shared pools, so
+ * sequences of very different lengths share one allocation.  The pages call
+ * the design serving-friendly as a standalone model with exact KV-cache
+ * support (abstract on the fugumt.com page; "KV Cache" section of the
+ * mauroscia.it page, on managing the cache without wasting memory); the
+ * block table is the reading taken for that.
+ *   position p of sequence b:  page pg = block_table[b][p / 64], row p % 64;
+ *   k_pool [n_pages][Hkv][64][D]   key of (p, h) at [pg][h][p % 64][:];
+ *   v_pool [n_pages][Hkv][D][64]   value of (p, h), element d, at
+ *                                  [pg][h][d][p % 64] (pages transposed).
+ *
+ *   dtype        TIDAR_BF16 only (TIDAR_EUNSUPPORTED otherwise).
+ *   max_pages    entries per block-table row; capacity 64 * max_pages
+ *                positions per sequence (plays the role of S_max).
+ *   n_pages      pages in each pool.
+ *   block_table  [B][max_pages] int32 (device memory).  Entries for pages
+ *                0 .. ceil(lens[b] / 64) - 1 must lie in [0, n_pages); a
+ *                sequence with any other entry there gets NaN outputs, like
+ *                a violated length bound.  Later entries are not read.
+ *                Pages may be shared between sequences.
+ *   workspace    at least what tidar_step_attention_workspace() reports for
+ *                S_max = 64 * max_pages and the same other arguments.
+ * Every other argument is as for tidar_step_attention.
+ * ---------------------------------------------------------------------- */
+int tidar_step_attention_paged(int dtype, int B, int Hq, int Hkv, int D, int max_pages, int n_pages, int max_len,
+                               int k, int n_groups, float sm_scale, int kv_chunk,
+                               const void* q, const void* k_step, const void* v_step,
+                               const void* k_pool, const void* v_pool, const int32_t* block_table,
+                               const int32_t* lens, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Greedy verification and next-draft selection.
  *
  * Candidates are confirmed strictly left to right; whichever outcome is
@@ -222,6 +257,28 @@ int tidar_kv_commit(int dtype, int B, int Hkv, int D, int S_max, int R, int k,
                     void* k_cache, void* v_cache, int32_t* lens,
                     const void* k_step, const void* v_step, const int32_t* accept_len,
                     int32_t* err_flags, void* stream);
+
+/* ------------------------------------------------------------------------
+ * KV-cache commit / evict into a paged cache, in place.
+ *
+ * tidar_kv_commit for the pools and block table of
+ * tidar_step_attention_paged: the accepted rows of sequence b go to
+ * positions p = lens[b] + i, i < a, i.e. key row p % 64 and value column
+ * p % 64 of page block_table[b][p / 64]; then lens[b] += a.  The caller
+ * provides the pages (entries for every page that positions lens[b] ..
+ * lens[b] + a - 1 fall in); a page written here must not be shared with
+ * another sequence.
+ *   flags (err_flags[b]): 0 ok, 1 lens[b] + a > 64 * max_pages, 2 a outside
+ *   0..k, 3 a needed page entry outside [0, n_pages).  A flagged sequence is
+ *   left untouched.
+ *   dtype        TIDAR_BF16 or TIDAR_F32.
+ *   max_pages, n_pages, block_table   as for tidar_step_attention_paged.
+ * Every other argument is as for tidar_kv_commit.
+ * ---------------------------------------------------------------------- */
+int tidar_kv_commit_paged(int dtype, int B, int Hkv, int D, int max_pages, int n_pages, int R, int k,
+                          void* k_pool, void* v_pool, const int32_t* block_table, int32_t* lens,
+                          const void* k_step, const void* v_step, const int32_t* accept_len,
+                          int32_t* err_flags, void* stream);
 
 #ifdef __cplusplus
 }

@@ -142,3 +142,30 @@ def test_verify_sample_validation_and_size(T):
     assert f(*no_draft) == -1
     empty = [0, 4, 100, 0.8] + [None] * 4 + [1, 0] + [None] * 3 + [0, None]
     assert f(*empty) == 0
+
+
+def test_paged_validation(T):
+    L = T.lib()
+    p = ctypes.c_void_p(0x100000)
+    f = L.tidar_step_attention_paged
+    #       dtype B  Hq Hkv D   max_pages n_pages max_len k  ng  scale kv_chunk
+    args = [0, 2, 8, 2, 128, 64, 200, 4000, 4, 4, 0.1, 0] + [p] * 7 + [p, None, p, 1 << 30, None]
+    f32 = list(args); f32[0] = 1
+    assert f(*f32) == -2  # paged pools: bf16 only
+    no_pages = list(args); no_pages[6] = 0
+    assert f(*no_pages) == -1
+    too_long = list(args); too_long[7] = 64 * 64 + 1  # max_len above 64 * max_pages
+    assert f(*too_long) == -1
+    no_table = list(args); no_table[17] = None
+    assert f(*no_table) == -1
+    small_ws = list(args); small_ws[22] = 16
+    assert f(*small_ws) == -3
+    c = L.tidar_kv_commit_paged
+    cargs = [0, 2, 8, 128, 64, 200, 72, 8] + [p] * 8 + [None, None]
+    bad_table = list(cargs); bad_table[10] = ctypes.c_void_p(0x100002)
+    assert c(*bad_table) == -1
+    no_pool = list(cargs); no_pool[8] = None
+    assert c(*no_pool) == -1
+    zero_pages = list(cargs); zero_pages[5] = 0
+    assert c(*zero_pages) == -1
+    assert c(*([0, 0, 8, 128, 64, 200, 72, 8] + [None] * 10)) == 0

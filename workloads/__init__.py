@@ -17,6 +17,10 @@ k_cache        [B][Hkv][S_max][D]           settled keys, rows < lens[b] valid
 v_cache        [B][Hkv][S_max/64][D][64]    settled values in pages of 64 positions,
                                             each page stored transposed
 lens           [B] int32                    settled prefix length per sequence
+k_pool         [n_pages][Hkv][64][D]        paged keys: position p of sequence b is row
+                                            p % 64 of page block_table[b][p // 64]
+v_pool         [n_pages][Hkv][D][64]        paged values, each page transposed
+block_table    [B][max_pages] int32         page of each 64-position tile
 ar_logits      [B][k+1][V] float32          row 0 carried, rows 1..k candidates
 draft_logits   [B][k][k][V] float32         group g, slot s
 cand           [B][k] int32                 carried-over draft candidates
@@ -42,6 +46,7 @@ _T_Q, _T_KS, _T_VS, _T_KC, _T_VC, _T_LENS = 1, 2, 3, 4, 5, 6
 _T_AR, _T_DRAFT, _T_CAND, _T_ACC, _T_BOOST = 11, 12, 13, 14, 15
 _T_TINY_W, _T_PROMPT, _T_INJECT = 21, 22, 23
 _T_QLOG, _T_QBOOST, _T_SHIFT, _T_MASK = 31, 32, 33, 34
+_T_PAGES = 41
 
 MASK_TOKEN_TINY = 1024  # extra embedding row of the tiny decoder; outside its LM head
 VPAGE = 64  # positions per value-cache page
@@ -216,6 +221,28 @@ def attention_inputs(shape: AttnShape, seed: int = 0, step: int = 0, config_id: 
     d = step_rows(shape, seed, step, config_id)
     d.update(kv_cache(shape, seed, config_id, tail))
     return d
+
+
+def to_pages(k_cache: np.ndarray, v_cache: np.ndarray, seed: int, spare: int = 8, config_id: int = 0) -> dict:
+    """Move contiguous caches (k [B][Hkv][S][D], v [B][Hkv][S/64][D][64])
+    into shared pools under a random block table (layout only).
+
+    Every (sequence, 64-position tile) gets its own page, in a seeded random
+    order over ``B*S/64 + spare`` pages; the spare pages are filled with NaN
+    so that a read of a page no table row names shows up.  Returns k_pool
+    [n_pages][Hkv][64][D], v_pool [n_pages][Hkv][D][64] and block_table
+    [B][S/64] int32."""
+    B, Hkv, S, D = k_cache.shape
+    P = S // VPAGE
+    n_pages = B * P + spare
+    order = generator(seed, config_id, 0, _T_PAGES).permutation(n_pages).astype(np.int32)
+    table = order[:B * P].reshape(B, P)
+    nan = BF16_NAN if k_cache.dtype == np.uint16 else np.float32(np.nan)
+    k_pool = np.full((n_pages, Hkv, VPAGE, D), nan, dtype=k_cache.dtype)
+    v_pool = np.full((n_pages, Hkv, D, VPAGE), nan, dtype=v_cache.dtype)
+    k_pool[table.reshape(-1)] = k_cache.reshape(B, Hkv, P, VPAGE, D).transpose(0, 2, 1, 3, 4).reshape(B * P, Hkv, VPAGE, D)
+    v_pool[table.reshape(-1)] = v_cache.transpose(0, 2, 1, 3, 4).reshape(B * P, Hkv, D, VPAGE)
+    return {"k_pool": k_pool, "v_pool": v_pool, "block_table": np.ascontiguousarray(table)}
 
 
 def to_f32(x: np.ndarray, dtype: str) -> np.ndarray:
