@@ -17,6 +17,9 @@ Prints ONE JSON line.  Options:
   --gpus N          only N = 1 is supported (one GPU per process, no collectives)
   --steps K --warmup W
   --no-cpu-baseline skip the oracle timing (for profiler runs)
+  --paged           settled keys/values in shared 64-position page pools under
+                    a shuffled block table (tidar_step_attention_paged and
+                    tidar_kv_commit_paged) instead of per-sequence caches
   --verify sample   stochastic verification (temperature --temperature, Philox
                     stream of --seed and the step number) in place of greedy;
                     inputs from the sampling generator, accept lengths as drawn
@@ -60,8 +63,10 @@ def parse():
     p.add_argument("--summarize", metavar="DIR", help="write profiles/ summaries from rocprofv3 outputs in DIR")
     p.add_argument("--verify", default="greedy", choices=["greedy", "sample"])
     p.add_argument("--temperature", type=float, default=1.0)
-    p.add_argument("--workload", default="step_8b", choices=["step_8b", "step_1p5b", "step_8b_long"],
-                   help="synthetic workload (the reported line is the 8B-shaped step)")
+    p.add_argument("--paged", action="store_true")
+    p.add_argument("--workload", default="step_8b", choices=["step_8b", "step_1p5b", "step_8b_long", "ragged_8b"],
+                   help="synthetic workload (the reported line is the 8B-shaped step; ragged_8b is one step of "
+                        "the serving loop's batch of 32 at its initial lengths)")
     return p.parse_args()
 
 
@@ -282,7 +287,15 @@ def main():
             return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(x).to(dev)
 
-    base = {n: to_dev(x, n != "lens") for n, x in d.items()}
+    if args.paged:
+        pg = W.to_pages(d["k_cache"], d["v_cache"], seed=args.seed, spare=0, config_id=wl.config_id)
+        d_dev = {n: x for n, x in d.items() if n not in ("k_cache", "v_cache")}
+        d_dev.update({"k_pool": pg["k_pool"], "v_pool": pg["v_pool"], "block_table": pg["block_table"]})
+        del pg
+    else:
+        d_dev = d
+    base = {n: to_dev(x, n not in ("lens", "block_table")) for n, x in d_dev.items()}
+    del d_dev
     base.update({n: to_dev(v[n], False) for n in v_names})
     per_rep = sum(t.numel() * t.element_size() for t in base.values())
     n_rep = max(2, math.ceil(args.cold_bytes / per_rep))
@@ -306,6 +319,11 @@ def main():
     torch.cuda.synchronize()
 
     def attention(r):
+        if args.paged:
+            tidar.step_attention_paged(r["q"], r["k_step"], r["v_step"], r["k_pool"], r["v_pool"], r["block_table"],
+                                       r["lens"], s.k, s.n_groups, s.sm_scale, max_len=s.max_len, out=r["out"],
+                                       lse=r["lse"], workspace=r["ws_a"], kv_chunk=args.kv_chunk)
+            return
         tidar.step_attention(r["q"], r["k_step"], r["v_step"], r["k_cache"], r["v_cache"], r["lens"], s.k,
                              s.n_groups, s.sm_scale, max_len=s.max_len, out=r["out"], lse=r["lse"],
                              workspace=r["ws_a"], kv_chunk=args.kv_chunk)
@@ -320,7 +338,12 @@ def main():
 
     def verify_commit(r, step_no):
         verify(r, step_no)
-        tidar.kv_commit(r["k_cache"], r["v_cache"], r["lens"], r["k_step"], r["v_step"], r["acc"], s.k, r["err"])
+        if args.paged:
+            tidar.kv_commit_paged(r["k_pool"], r["v_pool"], r["block_table"], r["lens"], r["k_step"], r["v_step"],
+                                  r["acc"], s.k, r["err"])
+        else:
+            tidar.kv_commit(r["k_cache"], r["v_cache"], r["lens"], r["k_step"], r["v_step"], r["acc"], s.k,
+                            r["err"])
         r["lens"].copy_(r["lens0"])
 
     stream = torch.cuda.current_stream()
@@ -389,6 +412,7 @@ def main():
         "config": {"workload": wl.name, "kv_chunk": args.kv_chunk or "auto", "batch": s.B, "q_heads": s.Hq, "kv_heads": s.Hkv, "head_dim": s.D,
                    "prefix": s.lens[0], "k": s.k, "draft_groups": s.n_groups, "step_rows": s.R, "vocab": wl.V,
                    "accept": wl.accept if args.verify == "greedy" else "sampled", "verify": args.verify,
+                   "kv_layout": "paged" if args.paged else "contiguous",
                    "cold_replicas": n_rep},
         "step_us": round(step_ms * 1e3, 2),
         "attention_us": round(attn_ms_mean * 1e3, 2),

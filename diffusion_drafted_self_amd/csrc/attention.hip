@@ -54,6 +54,21 @@ __device__ __forceinline__ size_t vpos(int d, int c, int D) {  // element (d, po
 // caches: page table[t] of the pools ([n_pages][Hkv][64][D] keys,
 // [n_pages][Hkv][D][64] values), this KV head's slot at the same offset in
 // every page.  Only tiles holding settled positions may be asked for.
+//
+// A table entry is read with a scalar load that waits inside its own asm
+// block: a plain load would be a vector load (the compiler cannot prove the
+// table unclobbered past the direct-to-LDS asm), and waiting for it would
+// drain every tile load in flight at each ring step.
+__device__ __forceinline__ int32_t scalar_load_i32(const int32_t* p) {
+  const unsigned long long a = (unsigned long long)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  const unsigned long long sa = ((unsigned long long)hi << 32) | lo;
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(sa));
+  return v;
+}
+
 template <int D, bool PAGED>
 struct KvMap {
   const bf16* k;
@@ -61,7 +76,7 @@ struct KvMap {
   const int32_t* tbl;  // this sequence's block-table row (paged)
   size_t stride;       // elements from one page to the next
   __device__ __forceinline__ size_t page(int t) const {
-    if constexpr (PAGED) return (size_t)tbl[t];
+    if constexpr (PAGED) return (size_t)scalar_load_i32(tbl + t);
     else return (size_t)t;
   }
   __device__ __forceinline__ const bf16* ktile(int t) const { return k + page(t) * stride; }
@@ -692,10 +707,16 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
   auto vslot = [&](int j) { return sV0 + (j & (RING - 1)) * T::V_BYTES; };
   // ring prologue, as iterations -3..-1 would issue it: K(0); K(1), V(0); K(2), V(1)
   const int tb = kb / TK;  // the chunk's first tile
+  // paged: the page of the last K tile requested; the V tile a ring step
+  // requests is the K tile of the step before, so its page is known
+  size_t pg_last_k = 0;
   if (n > 0) issue_k<D>(kslot(0), kv.ktile(tb), plan, wave);
   if (n > 1) issue_k<D>(kslot(1), kv.ktile(tb + 1), plan, wave);
   if (n > 0) issue_v<D>(vslot(0), kv.vtile(tb), plan, wave);
-  if (n > 2) issue_k<D>(kslot(2), kv.ktile(tb + 2), plan, wave);
+  if (n > 2) {
+    pg_last_k = kv.page(tb + 2);
+    issue_k<D>(kslot(2), kv.k + pg_last_k * kv.stride, plan, wave);
+  }
   if (n > 1) issue_v<D>(vslot(1), kv.vtile(tb + 1), plan, wave);
 
   QFrags<D, NF, NS> q;
@@ -802,8 +823,17 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
       else wait_vmcnt<T::NVW>();
       wait_lgkmcnt0();
       barrier();
-      if (it + 3 < n) issue_k<D>(kslot(it + 3), kv.ktile(tb + it + 3), plan, wave);
-      if (it + 2 < n) issue_v<D>(vslot(it + 2), kv.vtile(tb + it + 2), plan, wave);
+      if constexpr (PAGED) {
+        const size_t pg_v = pg_last_k;  // tile it + 2, requested as K by the previous step (or the prologue)
+        if (it + 3 < n) {
+          pg_last_k = kv.page(tb + it + 3);
+          issue_k<D>(kslot(it + 3), kv.k + pg_last_k * kv.stride, plan, wave);
+        }
+        if (it + 2 < n) issue_v<D>(vslot(it + 2), kv.v + pg_v * kv.stride, plan, wave);
+      } else {
+        if (it + 3 < n) issue_k<D>(kslot(it + 3), kv.ktile(tb + it + 3), plan, wave);
+        if (it + 2 < n) issue_v<D>(vslot(it + 2), kv.vtile(tb + it + 2), plan, wave);
+      }
     };
     bool overflow = false;
     auto commit_sum = [&](bool big, const Probs<NF, NS>& pr) {
