@@ -33,8 +33,10 @@ from .verify import argmax_first, verify_ref
 from .verify_sample import verify_sample_ref, philox4x32_10
 from .commit import commit_ref
 from .paged import gather_paged, paged_attention_ref, commit_paged_ref
+from .train_mask import train_mask_ref, train_attention_ref
 from .tiny_decoder import TinyDecoder, ar_greedy, tidar_greedy
 
 __all__ = ["step_mask_ref", "attention_ref", "attention_split_ref", "causal_attention_ref",
            "argmax_first", "verify_ref", "verify_sample_ref", "philox4x32_10", "commit_ref", "gather_paged", "paged_attention_ref", "commit_paged_ref",
+           "train_mask_ref", "train_attention_ref",
            "TinyDecoder", "ar_greedy", "tidar_greedy"]
