@@ -64,9 +64,11 @@ def parse():
     p.add_argument("--verify", default="greedy", choices=["greedy", "sample"])
     p.add_argument("--temperature", type=float, default=1.0)
     p.add_argument("--paged", action="store_true")
-    p.add_argument("--workload", default="step_8b", choices=["step_8b", "step_1p5b", "step_8b_long", "ragged_8b"],
+    p.add_argument("--workload", default="step_8b",
+                   choices=["step_8b", "step_1p5b", "step_8b_long", "ragged_8b", "train_8b"],
                    help="synthetic workload (the reported line is the 8B-shaped step; ragged_8b is one step of "
-                        "the serving loop's batch of 32 at its initial lengths)")
+                        "the serving loop's batch of 32 at its initial lengths; train_8b is the training-mask "
+                        "attention over a duplicated sequence, 8B heads, 4 x 2 x 4096 positions, block 8)")
     return p.parse_args()
 
 
@@ -245,6 +247,102 @@ def cpu_baseline(wl, d, v, a_planted, args):
                       f"float64 NumPy, {threads} BLAS threads on {cores} host cores"}
 
 
+TRAIN = {"B": 4, "Hq": 32, "Hkv": 8, "D": 128, "N": 4096, "block": 8}
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def train_pairs(N, bs):
+    """Visible (row, key) pairs of one head of the training mask: N(N+1)/2
+    for the clean half; each masked block of size s after lo clean tokens
+    contributes s*(lo + s)."""
+    masked = sum(min(bs, N - lo) * (lo + min(bs, N - lo)) for lo in range(0, N, bs))
+    return N * (N + 1) // 2 + masked
+
+
+def bench_train(args):
+    """Training-mask attention: K calls between HIP events, inputs rotating
+    over >= 2 GB of replicas; one JSON line with the MFMA roofline."""
+    import numpy as np
+    import torch
+
+    import diffusion_drafted_self_amd as tidar
+    import workloads as W
+
+    c = TRAIN
+    B, Hq, Hkv, D, N, bs = c["B"], c["Hq"], c["Hkv"], c["D"], c["N"], c["block"]
+    dev = torch.device("cuda:0")
+    d = W.train_inputs(B, Hq, Hkv, D, N, seed=args.seed)
+    scale = 1.0 / math.sqrt(D)
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    base = {n: to_dev(d[n]) for n in ("q", "k", "v")}
+    per_rep = sum(t.numel() * t.element_size() for t in base.values()) * 2  # + the output
+    n_rep = max(2, math.ceil(args.cold_bytes / per_rep))
+    reps = [{**{n: t.clone() for n, t in base.items()}, "out": torch.empty_like(base["q"]),
+             "lse": torch.empty((B, Hq, 2 * N), dtype=torch.float32, device=dev)} for _ in range(n_rep)]
+    del base
+
+    def call(r):
+        tidar.train_attention(r["q"], r["k"], r["v"], N, bs, scale, out=r["out"], lse=r["lse"])
+
+    K, Wu = args.steps, args.warmup
+    for i in range(Wu):
+        call(reps[i % n_rep])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(K):
+        call(reps[(Wu + i) % n_rep])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / K
+    assert torch.isfinite(reps[0]["out"].float()).all()
+    flops = 4 * D * train_pairs(N, bs) * B * Hq
+    tflops = flops / (ms * 1e-3) / 1e12
+    result = {
+        "metric": "training-mask attention throughput (TFLOP/s over visible pairs)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": Wu,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "train_8b", "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+                   "clean_positions": N, "sequence": 2 * N, "block": bs, "cold_replicas": n_rep},
+        "attention_us": round(ms * 1e3, 2),
+        "roofline": {"bound": "mfma", "kernel": "tidar_train_attention", "achieved": round(tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops": flops},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_train(d, N, bs, scale, B, Hq, D)
+    print(json.dumps(result))
+
+
+def cpu_baseline_train(d, N, bs, scale, B, Hq, D):
+    """The oracle (dense float64 over the whole T x T mask) on two of the
+    B*Hq heads; the rate counts the visible-pair flops of those heads."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+    cores = len(os.sched_getaffinity(0))
+    q, k, v = (W.bf16_to_f32(d[n]) for n in ("q", "k_nat", "v_nat"))
+    heads = [(0, 0), (B - 1, Hq - 1)]
+    G = Hq // k.shape[2]
+    # the two heads as a batch of two single-head sequences: one call, one mask
+    qs = np.stack([q[b, :, h] for b, h in heads])[:, :, None]
+    ks = np.stack([k[b, :, h // G] for b, h in heads])[:, :, None]
+    vs = np.stack([v[b, :, h // G] for b, h in heads])[:, :, None]
+    t0 = time.perf_counter()
+    oracle.train_attention_ref(qs, ks, vs, N, bs, scale)
+    dt = time.perf_counter() - t0
+    flops = 4 * D * train_pairs(N, bs) * len(heads)
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"{len(heads)} of {B * Hq} heads of train_8b (dense float64 over the full T x T mask)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -256,6 +354,9 @@ def main():
         return
     if args.summarize:
         summarize(args.summarize)
+        return
+    if args.workload == "train_8b":
+        bench_train(args)
         return
 
     import numpy as np

@@ -1,8 +1,8 @@
 """TiDAR decode-step hot path on MI355X (gfx950): thin Python binding.
 
 The calls of ``include/tidar.h`` -- ``step_attention``,
-``step_attention_paged``, ``verify_greedy``, ``verify_sample``, ``kv_commit``
-and ``kv_commit_paged`` -- under the same names, taking torch tensors that
+``step_attention_paged``, ``train_attention``, ``verify_greedy``,
+``verify_sample``, ``kv_commit`` and ``kv_commit_paged`` -- under the same names, taking torch tensors that
 live on the GPU.  This module only checks shapes and dtypes,
 marshals pointers and the current HIP stream, and allocates outputs /
 workspace with torch when the caller does not pass them.  Every step of the
@@ -48,6 +48,7 @@ SIGNATURES = {
     "tidar_kv_commit": (_c_int, [_c_int] * 7 + [_p] * 7 + [_p]),
     "tidar_step_attention_paged": (_c_int, [_c_int] * 10 + [_f, _c_int] + [_p] * 10 + [_c_size, _p]),
     "tidar_kv_commit_paged": (_c_int, [_c_int] * 8 + [_p] * 8 + [_p]),
+    "tidar_train_attention": (_c_int, [_c_int] * 7 + [_f] + [_p] * 6),
 }
 
 
@@ -252,6 +253,35 @@ def step_attention_paged(q, k_step, v_step, k_pool, v_pool, block_table, lens, k
     return out, lse
 
 
+def train_attention(q, k, v, N: int, block: int, sm_scale: float, out=None, lse=None, want_lse: bool = True):
+    """Attention over the duplicated training sequence (bf16): clean half
+    causal, masked half in blocks of ``block`` that see the clean prefix
+    before them and themselves.  q [B][2N][Hq][D], k [B][Hkv][2N][D],
+    v [B][Hkv][2N/64][D][64].  Returns (out, lse)."""
+    _need(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    B, T, Hq, D = q.shape
+    _need(k, "k", torch.bfloat16, 4, dev)
+    _need(v, "v", torch.bfloat16, 5, dev)
+    Hkv = k.shape[1]
+    if T != 2 * N or tuple(k.shape) != (B, Hkv, T, D) or tuple(v.shape) != (B, Hkv, T // VALUE_PAGE, D, VALUE_PAGE):
+        raise ValueError("expected q [B][2N][Hq][D], k [B][Hkv][2N][D], v [B][Hkv][2N/64][D][64]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, 4, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+    elif lse is not None:
+        _need(lse, "lse", torch.float32, 3, dev)
+    _check("tidar_train_attention",
+           lib().tidar_train_attention(TIDAR_BF16, B, Hq, Hkv, D, int(N), int(block), float(sm_scale), _ptr(q),
+                                      _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _stream()))
+    return out, lse
+
+
 # ------------------------------------------------------------------------ verify
 def verify_workspace_bytes(B: int, k: int, V: int) -> int:
     n = _c_size(0)
@@ -385,4 +415,4 @@ def kv_commit_paged(k_pool, v_pool, block_table, lens, k_step, v_step, accept_le
 
 __all__ = ["step_attention", "step_attention_workspace_bytes", "verify_greedy", "verify_workspace_bytes",
            "verify_sample", "verify_sample_workspace_bytes", "kv_commit",
-           "step_attention_paged", "kv_commit_paged", "strerror", "lib", "TidarError", "LIB_PATH", "SIGNATURES"]
+           "step_attention_paged", "kv_commit_paged", "train_attention", "strerror", "lib", "TidarError", "LIB_PATH", "SIGNATURES"]

@@ -601,7 +601,13 @@ __device__ __forceinline__ void pv_tile(const lds_char* sV, const Probs<NF, NS>&
 // softmax(t) | scores(t+1) | P.V(t-1).  Tiles that reach past the settled
 // prefix are staged through registers into the last slots first, before
 // the ring fills them.
-template <int D, int NF, int NS, bool PAGED>
+//
+// TRAIN: the duplicated training sequence (rows and keys are the T = 2N
+// positions of one sequence, keys in the cache layouts with S_max = T).  A
+// workgroup's rows lie in one half; the key tiles every row of it sees in
+// full go through the ring, the few tiles on its causal diagonal, at its
+// blocks' prefix ends and on its own blocks take the staged, masked path.
+template <int D, int NF, int NS, bool PAGED, bool TRAIN = false>
 __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_pipe_bf16_kernel(AttnArgs a) {
   using T = Tile<D>;
@@ -626,7 +632,18 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
 
   // this workgroup's tiles [T0, T1): wave w owns T0 + w*NF + f (f < NF);
   // the shared tiles T0 + 4*NF + s (s < NS) are split by key block
-  const int T0 = rw * a.n16 / a.n_rowblk, T1 = (rw + 1) * a.n16 / a.n_rowblk;
+  int T0, T1;
+  if constexpr (TRAIN) {
+    // 4*NF + NS tiles per workgroup, H workgroups per half; workgroup ids
+    // alternate between the halves from their last (heaviest) blocks down
+    const int H = a.n_rowblk / 2, n16h = a.n16 / 2, tpw = 4 * NF + NS;
+    const int half = rw & 1, blk = H - 1 - (rw >> 1);
+    T0 = half * n16h + blk * tpw;
+    T1 = min(T0 + tpw, (half + 1) * n16h);
+  } else {
+    T0 = rw * a.n16 / a.n_rowblk;
+    T1 = (rw + 1) * a.n16 / a.n_rowblk;
+  }
   int mrow[at_least_1<NF>()], mrow_s[NSa];
   bool ok[at_least_1<NF>()], ok_s[NSa];
 #pragma unroll
@@ -650,7 +667,7 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
     return a.lse + ((size_t)b * a.Hq + h) * a.R + r;
   };
 
-  const int L = a.lens[b];
+  const int L = TRAIN ? a.S_max : a.lens[b];  // TRAIN: every position's keys are in the buffers
   KvMap<D, PAGED> kv;
   const size_t pair = (size_t)b * a.Hkv + kvh;
   if constexpr (PAGED) {
@@ -664,7 +681,7 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
     kv.tbl = nullptr;
     kv.stride = (size_t)TK * D;
   }
-  bool violated = L < 0 || L > a.max_len;
+  bool violated = !TRAIN && (L < 0 || L > a.max_len);
   if constexpr (PAGED) {  // every page holding a settled position must be in the pools
     bool bad = false;
     if (!violated)
@@ -688,18 +705,39 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
     }
     return;
   }
-  const int Ltot = L + a.R;
+  const int Ltot = TRAIN ? L : L + a.R;
   const int kb = split * a.chunk;
   if (kb >= Ltot) return;
   const int ke = min(kb + a.chunk, Ltot);
   const int n_valid = (Ltot + a.chunk - 1) / a.chunk;
 
   const size_t step_stride = (size_t)a.Hkv * D;
-  const bf16* ks_base = (const bf16*)a.k_step + (size_t)b * a.R * step_stride + kvh * D;
-  const bf16* vs_base = (const bf16*)a.v_step + (size_t)b * a.R * step_stride + kvh * D;
+  const bf16* ks_base = TRAIN ? nullptr : (const bf16*)a.k_step + (size_t)b * a.R * step_stride + kvh * D;
+  const bf16* vs_base = TRAIN ? nullptr : (const bf16*)a.v_step + (size_t)b * a.R * step_stride + kvh * D;
 
-  const int fast_end = min(ke, (L / TK) * TK);
-  const int n = fast_end > kb ? (fast_end - kb) / TK : 0;  // prefix tiles through the rings
+  // keys [kb, fast_end) go through the rings unmasked; the tiles of
+  // [mA0, mA1) and [mB0, mB1) take the staged path with the zone mask
+  int fast_end, mA0, mA1, mB0 = 0, mB1 = 0;
+  if constexpr (TRAIN) {
+    const int N = a.train_N, bs = a.train_bs;
+    const int r_lo = 16 * T0 / a.G, r_hi = (min(16 * T1, a.M) - 1) / a.G;
+    if (r_lo < N) {  // clean rows: the causal diagonal
+      fast_end = (r_lo + 1) / TK * TK;
+      mA1 = (r_hi + TK) / TK * TK;
+    } else {  // masked rows: their blocks' prefix ends, then their own blocks
+      const int lo_min = (r_lo - N) / bs * bs, lo_max = (r_hi - N) / bs * bs;
+      fast_end = lo_min / TK * TK;
+      mA1 = (lo_max + TK - 1) / TK * TK;
+      mB0 = (N + lo_min) / TK * TK;
+      mB1 = (N + min(lo_max + bs, N) + TK - 1) / TK * TK;
+    }
+    mA0 = fast_end;
+  } else {
+    fast_end = min(ke, (L / TK) * TK);
+    mA0 = max(kb, fast_end);
+    mA1 = ke;
+  }
+  const int n = fast_end > kb ? (fast_end - kb) / TK : 0;  // tiles through the rings
   if (tid == 0) ovf_flag = 0;  // published by the first barrier below
   DmaPlan<D> plan;
   dma_plan<D>(plan, wave, lane);
@@ -753,11 +791,16 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
   Scores<NF, NS> sA, sB;
   Probs<NF, NS> pA, pB;
 
-  // Tiles reaching past the prefix: staged through registers into the last
-  // slots (free until the loop's first requests), masked by zone, softmax
-  // with the exact path.
+  // Masked tiles (decode: tiles reaching past the prefix): staged through
+  // registers into the last slots (free until the loop's first requests),
+  // masked by zone, softmax with the exact path.
+  const int zoff = TRAIN ? 0 : L;  // zone tests take step-row indices (decode) or positions (training)
+  auto zone = [&](int m) { return TRAIN ? train_zone(m / a.G, a.train_N, a.train_bs) : step_zone(m / a.G, a.k); };
   auto tail_tiles = [&]() {
-    for (int t0 = max(kb, fast_end); t0 < ke; t0 += TK) {
+    // one loop over both ranges: a single inlined body
+    const int nA = (mA1 - mA0 + TK - 1) / TK, nB = (mB1 - mB0 + TK - 1) / TK;  // a range may end mid-tile
+    for (int i = 0; i < nA + nB; ++i) {
+      const int t0 = i < nA ? mA0 + i * TK : mB0 + (i - nA) * TK;
       lds_char* sK = kslot(RING - 1);
       lds_char* sV = vslot(RING - 1);
       barrier();
@@ -771,23 +814,23 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
       // element updates
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        const StepZone z = step_zone(mrow[f] / a.G, a.k);
+        const StepZone z = zone(mrow[f]);
 #pragma unroll
         for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int c = t0 + krow_of(kb4, 4 * hi + v);
-            const bool vis = (c < ke) & z.sees(c - L);
+            const bool vis = (c < ke) & z.sees(c - zoff);
             sA.s[f][kb4][v] = vis ? sA.s[f][kb4][v] : -INFINITY;
           }
       }
 #pragma unroll
       for (int s2 = 0; s2 < NS; ++s2) {
-        const StepZone z = step_zone(mrow_s[s2] / a.G, a.k);
+        const StepZone z = zone(mrow_s[s2]);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int c = t0 + krow_of(wave, 4 * hi + v);
-          const bool vis = (c < ke) & z.sees(c - L);
+          const bool vis = (c < ke) & z.sees(c - zoff);
           sA.ss[s2][v] = vis ? sA.ss[s2][v] : -INFINITY;
         }
       }
@@ -1139,6 +1182,13 @@ hipError_t launch_bf16_pipe(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, int NF>
+hipError_t launch_bf16_train(const AttnArgs& a, hipStream_t s) {
+  const int nblk = a.B * a.Hkv * a.n_rowblk;
+  hipLaunchKernelGGL((attn_pipe_bf16_kernel<D, NF, 0, false, true>), dim3(nblk), dim3(NWV * 64), 0, s, a);
+  return hipGetLastError();
+}
+
 // (full tiles per wave, shared tiles per workgroup) shapes that are built
 template <int D>
 hipError_t launch_bf16_shape(const AttnArgs& a, hipStream_t s) {
@@ -1174,6 +1224,21 @@ hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t s) {
   else if (a.D == 64) e = launch_bf16_shape<64>(a, s);
   if (e != hipSuccess || a.n_split == 1) return e;
   return a.D == 128 ? launch_merge<bf16, 128>(a, s) : launch_merge<bf16, 64>(a, s);
+}
+
+hipError_t launch_train_attention_bf16(const AttnArgs& a, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  if (a.ns != 0) return hipErrorInvalidValue;
+  if (a.D == 128) {
+    if (a.nf == 1) return launch_bf16_train<128, 1>(a, s);
+    if (a.nf == 2) return launch_bf16_train<128, 2>(a, s);
+    if (a.nf == 3) return launch_bf16_train<128, 3>(a, s);
+  } else if (a.D == 64) {
+    if (a.nf == 1) return launch_bf16_train<64, 1>(a, s);
+    if (a.nf == 2) return launch_bf16_train<64, 2>(a, s);
+    if (a.nf == 3) return launch_bf16_train<64, 3>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t s) {

@@ -188,7 +188,7 @@ int step_attention_impl(int dtype, int B, int Hq, int Hkv, int D, int S_max, int
   if (lse && !aligned(lse, 4)) return TIDAR_EINVAL;
   if (p.total > 0 && (!aligned(workspace, 256) || workspace_bytes < p.total)) return TIDAR_EWORKSPACE;
 
-  tidar::AttnArgs a;
+  tidar::AttnArgs a = {};
   a.q = q;
   a.k_step = k_step;
   a.v_step = v_step;
@@ -311,6 +311,65 @@ int tidar_step_attention_paged(int dtype, int B, int Hq, int Hkv, int D, int max
   return step_attention_impl(dtype, B, Hq, Hkv, D, max_pages * kValuePage, max_len, k, n_groups, sm_scale,
                              kv_chunk, q, k_step, v_step, k_pool, v_pool, block_table, max_pages, n_pages, lens,
                              out, lse, workspace, workspace_bytes, stream);
+}
+
+int tidar_train_attention(int dtype, int B, int Hq, int Hkv, int D, int N, int block, float sm_scale,
+                          const void* q, const void* k, const void* v, void* out, float* lse, void* stream) {
+  if (dtype != TIDAR_BF16) return TIDAR_EUNSUPPORTED;
+  if (D != 64 && D != 128) return TIDAR_EUNSUPPORTED;
+  if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return TIDAR_EINVAL;
+  if (N < kTileKeys || N % kTileKeys != 0 || N > (1 << 24) || block < 1 || block > N) return TIDAR_EINVAL;
+  if (!(sm_scale > 0.f) || !(sm_scale < 3.0e38f)) return TIDAR_EINVAL;
+  const int G = Hq / Hkv;
+  const long T = 2L * N, M = T * G;
+  if (M > 0x7fffffffL) return TIDAR_EUNSUPPORTED;
+  if (B == 0) return TIDAR_OK;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return TIDAR_EINVAL;
+  if (lse && !aligned(lse, 4)) return TIDAR_EINVAL;
+
+  // row tiles of 16 per half; 4*nf tiles per workgroup, as many as keep
+  // the chip fed at least four workgroups per CU
+  const long n16h = M / 32;
+  const long pairs = (long)B * Hkv;
+  int nf = 1;
+  for (int c = 3; c >= 2; --c)
+    if (pairs * 2 * cdiv(n16h, 4 * c) >= 4L * kCUs) {
+      nf = c;
+      break;
+    }
+  const long H = cdiv(n16h, 4 * nf);
+  if (pairs * 2 * H > 0x7fffffffL) return TIDAR_EUNSUPPORTED;
+
+  tidar::AttnArgs a = {};
+  a.q = q;
+  a.k_cache = k;
+  a.v_cache = v;
+  a.lens = nullptr;
+  a.out = out;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.D = D;
+  a.S_max = (int)T;
+  a.max_len = (int)T;
+  a.k = 1;
+  a.R = (int)T;
+  a.M = (int)M;
+  a.chunk = (int)T;
+  a.n_split = 1;
+  a.n16 = (int)(M / 16);
+  a.nf = nf;
+  a.ns = 0;
+  a.n_rowblk = (int)(2 * H);
+  a.scale_log2 = sm_scale * 1.44269504088896340736f;
+  a.single_chunk_direct = 1;
+  a.block_table = nullptr;
+  a.train_N = N;
+  a.train_bs = block;
+  const hipError_t e = tidar::launch_train_attention_bf16(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
 }
 
 int tidar_verify_workspace(int B, int k, int V, size_t* bytes) {

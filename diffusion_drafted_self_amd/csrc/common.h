@@ -43,6 +43,20 @@ __device__ __forceinline__ StepZone step_zone(int r, int k) {
   return {g, k + g * k, k + (g + 1) * k};
 }
 
+// The duplicated training sequence [x_0 .. x_{N-1} ; m_0 .. m_{N-1}]: each
+// example appears once for next-token supervision and once as a fully
+// masked block filled in parallel ("TiDAR : l'hybride de NVIDIA ...",
+// nodesdaily.com, paragraph on training).  Clean row r sees positions
+// 0..r; masked row N + j of block [lo, hi) (lo = j - j % bs) sees the clean
+// prefix 0..lo-1 and its own block N+lo .. N+hi-1, as a draft group sees
+// the prefix, its accepted candidates and itself.  In the StepZone form
+// over absolute positions.
+__device__ __forceinline__ StepZone train_zone(int r, int N, int bs) {
+  if (r < N) return {r, 0, 0};
+  const int lo = (r - N) / bs * bs;
+  return {lo - 1, N + lo, N + min(lo + bs, N)};
+}
+
 // Block index remap for a 8-XCD part: the hardware hands consecutive
 // workgroup ids round-robin to the XCDs, so ids i, i+8, i+16, ... share an
 // XCD (and its L2).  The returned logical id makes runs of consecutive

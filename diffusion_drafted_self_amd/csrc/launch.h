@@ -33,10 +33,13 @@ struct AttnArgs {
   // nullptr for per-sequence contiguous caches
   const int32_t* block_table;
   int max_pages, n_pages;
+  // training sequence (train kernel only): N clean positions, masked blocks of train_bs
+  int train_N, train_bs;
 };
 
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t s);
+hipError_t launch_train_attention_bf16(const AttnArgs& a, hipStream_t s);
 
 struct VerifyArgs {
   const float* ar_logits;

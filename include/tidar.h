@@ -155,6 +155,36 @@ int tidar_step_attention_paged(int dtype, int B, int Hq, int Hkv, int D, int max
                                size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Training-mask attention over the duplicated training sequence.
+ *
+ * Each example appears twice in one long sequence: once for ordinary
+ * next-token supervision and once as a fully masked block filled in
+ * parallel (paragraph on training of the nodesdaily.com page; section
+ * "3. Training Recipe" of the mauroscia.it page).  The sequence is
+ * [x_0 .. x_{N-1} ; m_0 .. m_{N-1}], T = 2N positions, and
+ *   clean row r < N sees positions 0..r (causal);
+ *   masked row N + j, of block [lo, hi) with lo = j - j % block and
+ *   hi = min(lo + block, N), sees the clean prefix 0..lo-1 and its own
+ *   block N+lo .. N+hi-1 (bidirectional), as a draft group sees the prefix,
+ *   its accepted candidates and itself at decode time.
+ *   out[b][r][h] = softmax_c(sm_scale * q[b][r][h] . key_c) . value_c.
+ * Forward pass only; the losses and training stay with the caller.
+ *
+ *   dtype    TIDAR_BF16 only (TIDAR_EUNSUPPORTED otherwise).
+ *   N        clean positions: a multiple of 64, 64..2^24.
+ *   block    masked-block size, 1..N (the draft length at decode time).
+ *   q        [B][T][Hq][D]
+ *   k        [B][Hkv][T][D]          (the key-cache layout with S_max = T)
+ *   v        [B][Hkv][T/64][D][64]   (the value-cache layout: pages of 64
+ *                                     positions, each transposed)
+ *   out      [B][T][Hq][D] (written);  lse [B][Hq][T] f32 natural-log
+ *            softmax denominators (written; may be NULL).
+ * No workspace.  Other arguments as for tidar_step_attention.
+ * ---------------------------------------------------------------------- */
+int tidar_train_attention(int dtype, int B, int Hq, int Hkv, int D, int N, int block, float sm_scale,
+                          const void* q, const void* k, const void* v, void* out, float* lse, void* stream);
+
+/* ------------------------------------------------------------------------
  * Greedy verification and next-draft selection.
  *
  * Candidates are confirmed strictly left to right; whichever outcome is

@@ -169,3 +169,19 @@ def test_paged_validation(T):
     zero_pages = list(cargs); zero_pages[5] = 0
     assert c(*zero_pages) == -1
     assert c(*([0, 0, 8, 128, 64, 200, 72, 8] + [None] * 10)) == 0
+
+
+def test_train_attention_validation(T):
+    f = T.lib().tidar_train_attention
+    p = ctypes.c_void_p(0x100000)
+    ok = [0, 2, 8, 2, 128, 128, 8, 0.1, p, p, p, p, p, None]
+    bad = {
+        "f32": ([1] + ok[1:], -2), "head dim": (ok[:4] + [96] + ok[5:], -2),
+        "N % 64": (ok[:5] + [100] + ok[6:], -1), "N < 64": (ok[:5] + [0] + ok[6:], -1),
+        "block 0": (ok[:6] + [0] + ok[7:], -1), "block > N": (ok[:6] + [129] + ok[7:], -1),
+        "scale": (ok[:7] + [0.0] + ok[8:], -1), "Hq % Hkv": (ok[:2] + [7] + ok[3:], -1),
+        "unaligned q": (ok[:8] + [ctypes.c_void_p(0x100008)] + ok[9:], -1),
+    }
+    for name, (args, want) in bad.items():
+        assert f(*args) == want, name
+    assert f(*([0, 0, 8, 2, 128, 128, 8, 0.1] + [None] * 6)) == 0

@@ -47,6 +47,7 @@ _T_AR, _T_DRAFT, _T_CAND, _T_ACC, _T_BOOST = 11, 12, 13, 14, 15
 _T_TINY_W, _T_PROMPT, _T_INJECT = 21, 22, 23
 _T_QLOG, _T_QBOOST, _T_SHIFT, _T_MASK = 31, 32, 33, 34
 _T_PAGES = 41
+_T_TQ, _T_TK, _T_TV = 51, 52, 53
 
 MASK_TOKEN_TINY = 1024  # extra embedding row of the tiny decoder; outside its LM head
 VPAGE = 64  # positions per value-cache page
@@ -243,6 +244,21 @@ def to_pages(k_cache: np.ndarray, v_cache: np.ndarray, seed: int, spare: int = 8
     k_pool[table.reshape(-1)] = k_cache.reshape(B, Hkv, P, VPAGE, D).transpose(0, 2, 1, 3, 4).reshape(B * P, Hkv, VPAGE, D)
     v_pool[table.reshape(-1)] = v_cache.transpose(0, 2, 1, 3, 4).reshape(B * P, Hkv, D, VPAGE)
     return {"k_pool": k_pool, "v_pool": v_pool, "block_table": np.ascontiguousarray(table)}
+
+
+def train_inputs(B: int, Hq: int, Hkv: int, D: int, N: int, seed: int, config_id: int = 6) -> dict:
+    """Training-sequence attention inputs, bf16 bits from N(0,1) draws, T = 2N
+    positions: q [B][T][Hq][D]; keys and values in their natural layout
+    k_nat / v_nat [B][T][Hkv][D] and in the call's layouts k [B][Hkv][T][D],
+    v [B][Hkv][T/64][D][64] (layout only)."""
+    T = 2 * N
+    q = _normal(generator(seed, config_id, 0, _T_TQ), (B, T, Hq, D))
+    k = _normal(generator(seed, config_id, 0, _T_TK), (B, T, Hkv, D))
+    v = _normal(generator(seed, config_id, 0, _T_TV), (B, T, Hkv, D))
+    qb, kb, vb = bf16_bits(q), bf16_bits(k), bf16_bits(v)
+    k_l = np.ascontiguousarray(kb.transpose(0, 2, 1, 3))
+    v_l = v_paged(np.ascontiguousarray(vb.transpose(0, 2, 1, 3)))
+    return {"q": qb, "k_nat": kb, "v_nat": vb, "k": k_l, "v": v_l}
 
 
 def to_f32(x: np.ndarray, dtype: str) -> np.ndarray:
