@@ -34,9 +34,10 @@ from .verify_sample import verify_sample_ref, philox4x32_10
 from .commit import commit_ref
 from .paged import gather_paged, paged_attention_ref, commit_paged_ref
 from .train_mask import train_mask_ref, train_attention_ref
+from .lmhead import lmhead_verify_ref
 from .tiny_decoder import TinyDecoder, ar_greedy, tidar_greedy
 
 __all__ = ["step_mask_ref", "attention_ref", "attention_split_ref", "causal_attention_ref",
            "argmax_first", "verify_ref", "verify_sample_ref", "philox4x32_10", "commit_ref", "gather_paged", "paged_attention_ref", "commit_paged_ref",
-           "train_mask_ref", "train_attention_ref",
+           "train_mask_ref", "train_attention_ref", "lmhead_verify_ref",
            "TinyDecoder", "ar_greedy", "tidar_greedy"]
