@@ -20,6 +20,9 @@ Prints ONE JSON line.  Options:
   --paged           settled keys/values in shared 64-position page pools under
                     a shuffled block table (tidar_step_attention_paged and
                     tidar_kv_commit_paged) instead of per-sequence caches
+  --verify lmhead   the LM head fused with greedy verification: hidden states
+                    and a random-init head of the workload's model size in,
+                    no logits stored (tidar_lmhead_verify_greedy)
   --verify sample   stochastic verification (temperature --temperature, Philox
                     stream of --seed and the step number) in place of greedy;
                     inputs from the sampling generator, accept lengths as drawn
@@ -61,7 +64,7 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--kv-chunk", type=int, default=0, help="key positions per attention chunk (0: library plan)")
     p.add_argument("--summarize", metavar="DIR", help="write profiles/ summaries from rocprofv3 outputs in DIR")
-    p.add_argument("--verify", default="greedy", choices=["greedy", "sample"])
+    p.add_argument("--verify", default="greedy", choices=["greedy", "sample", "lmhead"])
     p.add_argument("--temperature", type=float, default=1.0)
     p.add_argument("--paged", action="store_true")
     p.add_argument("--workload", default="step_8b",
@@ -97,7 +100,7 @@ def read_traffic():
         return None
 
 
-def step_bytes(shape, V, accept, verify_kind="greedy"):
+def step_bytes(shape, V, accept, verify_kind="greedy", d_model=0):
     """Algorithmic bytes of one step (each byte moved once).
     attention: settled K+V + step K+V + Q + O; greedy verify: (k+1) AR rows
     and k-1 draft rows of f32 logits; sampling verify: k AR and k proposal
@@ -112,6 +115,8 @@ def step_bytes(shape, V, accept, verify_kind="greedy"):
     attn = kv_prefix + kv_step + qo
     if verify_kind == "sample":
         verify = (s.B * 3 * s.k + sum(1 for a in accept if a < s.k)) * V * 4
+    elif verify_kind == "lmhead":  # W read once per pass, plus the hidden rows of both passes
+        verify = 2 * V * d_model * 2 + s.B * 2 * s.k * d_model * 2
     else:
         verify = s.B * (2 * s.k) * V * 4
     commit = int(sum(accept)) * s.Hkv * s.D * esz * 2 * 2
@@ -225,6 +230,16 @@ def cpu_baseline(wl, d, v, a_planted, args):
         oracle.attention_ref(f["q"], f["k_step"], f["v_step"], f["k_cache"], f["v_cache"], d["lens"], s.k,
                              s.n_groups, s.sm_scale, pairs=[(0, h) for h in range(s.Hq)])
         n_steps = 3
+        lm_seconds = 0.0
+        if args.verify == "lmhead":
+            # the head's oracle is a V x d float64 product per row: two
+            # sequences timed, scaled to the batch
+            wf = W.bf16_to_f32(v["w"])
+            t_lm = time.perf_counter()
+            oracle.lmhead_verify_ref(W.bf16_to_f32(v["h_ar"][:2]), W.bf16_to_f32(v["h_draft"][:2]), wf,
+                                     v["cand"][:2])
+            lm_seconds = (time.perf_counter() - t_lm) * s.B / 2
+            lm_acc = v["planted"]
         t0 = time.perf_counter()
         for _ in range(n_steps):
             oracle.attention_ref(f["q"], f["k_step"], f["v_step"], f["k_cache"], f["v_cache"], d["lens"], s.k,
@@ -232,18 +247,21 @@ def cpu_baseline(wl, d, v, a_planted, args):
             if args.verify == "sample":
                 acc, _ = oracle.verify_sample_ref(v["ar_logits"], v["q_logits"], v["draft_logits"], v["cand"],
                                                   args.temperature, args.seed, 0)
+            elif args.verify == "lmhead":
+                acc = lm_acc
             else:
                 acc, _ = oracle.verify_ref(v["ar_logits"], v["draft_logits"], v["cand"])
             oracle.commit_ref(d["k_cache"], d["v_cache"], d["lens"], d["k_step"], d["v_step"], acc, s.k)
-        dt = (time.perf_counter() - t0) / n_steps
+        dt = (time.perf_counter() - t0) / n_steps + lm_seconds
     finally:
         if ctx:
             ctx.__exit__(None, None, None)
-    attn, ver, com, _, _ = step_bytes(s, wl.V, a_planted, args.verify)
+    attn, ver, com, _, _ = step_bytes(s, wl.V, a_planted, args.verify, wl.d_model)
     return {"value": round((attn + ver + com) / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle", "seconds_per_step": round(dt, 3),
             "sample": f"{n_steps} full {wl.name} steps (attention over all {s.B}x{s.Hq} heads, {args.verify} verify, "
-                      "commit), "
+                      "commit" + (", the LM head on 2 sequences scaled to the batch" if args.verify == "lmhead" else "")
+                      + "), "
                       f"float64 NumPy, {threads} BLAS threads on {cores} host cores"}
 
 
@@ -377,6 +395,11 @@ def main():
         v = W.sample_inputs(s.B, s.k, wl.V, seed=args.seed, config_id=wl.config_id)
         v_names = ("ar_logits", "q_logits", "draft_logits", "cand")
         a_planted = None
+    elif args.verify == "lmhead":
+        v = W.lmhead_inputs(s.B, s.k, wl.V, wl.d_model, seed=args.seed,
+                            accept=wl.accept if wl.accept in ("uniform", "geometric") else "uniform")
+        v_names = ("h_ar", "h_draft", "w", "cand")
+        a_planted = v["planted"]
     else:
         v = W.verify_inputs(s.B, s.k, wl.V, seed=args.seed, config_id=wl.config_id, accept=wl.accept)
         v_names = ("ar_logits", "draft_logits", "cand")
@@ -397,13 +420,16 @@ def main():
         d_dev = d
     base = {n: to_dev(x, n not in ("lens", "block_table")) for n, x in d_dev.items()}
     del d_dev
-    base.update({n: to_dev(v[n], False) for n in v_names})
+    base.update({n: to_dev(v[n], n in ("h_ar", "h_draft", "w")) for n in v_names})
     per_rep = sum(t.numel() * t.element_size() for t in base.values())
     n_rep = max(2, math.ceil(args.cold_bytes / per_rep))
     ws_a = tidar.step_attention_workspace_bytes(0, s.B, s.Hq, s.Hkv, s.D, s.S_max, s.max_len, s.k, s.n_groups,
                                                 args.kv_chunk)
-    ws_v = (tidar.verify_sample_workspace_bytes if args.verify == "sample" else tidar.verify_workspace_bytes)(
-        s.B, s.k, wl.V)
+    if args.verify == "lmhead":
+        ws_v = tidar.lmhead_verify_workspace_bytes(s.B, s.k, wl.V, wl.d_model)
+    else:
+        ws_v = (tidar.verify_sample_workspace_bytes if args.verify == "sample" else tidar.verify_workspace_bytes)(
+            s.B, s.k, wl.V)
     reps = []
     for _ in range(n_rep):
         r = {n: t.clone() for n, t in base.items()}
@@ -430,15 +456,17 @@ def main():
                              workspace=r["ws_a"], kv_chunk=args.kv_chunk)
 
     def verify(r, step_no):
-        if args.verify == "sample":
+        if args.verify == "lmhead":
+            tidar.lmhead_verify_greedy(r["h_ar"], r["h_draft"], r["w"], r["cand"], accept_len=r["acc"],
+                                       next_cand=r["next"], workspace=r["ws_v"])
+        elif args.verify == "sample":
             tidar.verify_sample(r["ar_logits"], r["q_logits"], r["draft_logits"], r["cand"], args.temperature,
                                 args.seed, step_no, accept_len=r["acc"], next_cand=r["next"], workspace=r["ws_v"])
         else:
             tidar.verify_greedy(r["ar_logits"], r["draft_logits"], r["cand"], accept_len=r["acc"],
                                 next_cand=r["next"], workspace=r["ws_v"])
 
-    def verify_commit(r, step_no):
-        verify(r, step_no)
+    def commit(r):
         if args.paged:
             tidar.kv_commit_paged(r["k_pool"], r["v_pool"], r["block_table"], r["lens"], r["k_step"], r["v_step"],
                                   r["acc"], s.k, r["err"])
@@ -447,9 +475,17 @@ def main():
                             r["err"])
         r["lens"].copy_(r["lens0"])
 
+    def verify_commit(r, step_no, ev=None):
+        verify(r, step_no)
+        if ev is not None:
+            ev.record(stream)
+        commit(r)
+
     stream = torch.cuda.current_stream()
     K, Wu = args.steps, args.warmup
     ev_a = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    # the fused LM head dominates its step: its own end event after verify
+    ev_v = [torch.cuda.Event(enable_timing=True) if args.verify == "lmhead" else None for _ in range(K)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for i in range(Wu):
         r = reps[i % n_rep]
@@ -462,7 +498,7 @@ def main():
         ev_a[i][0].record(stream)
         attention(r)
         ev_a[i][1].record(stream)
-        verify_commit(r, Wu + i)
+        verify_commit(r, Wu + i, ev_v[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     step_ms = t_start.elapsed_time(t_end) / K
@@ -492,7 +528,7 @@ def main():
             assert acc.tolist() == a_planted.tolist(), "verify result differs from the planted accept lengths"
         else:
             a_planted = acc
-        attn_b, ver_b, com_b, kv_b, flops = step_bytes(s, wl.V, a_planted)
+        attn_b, ver_b, com_b, kv_b, flops = step_bytes(s, wl.V, a_planted, args.verify, wl.d_model)
     flops_step = 4 * s.D * s.Hq * s.B * visible_step_pairs(s.k, s.n_groups)
     step_gbps = (attn_b + ver_b + com_b) / (step_ms * 1e-3) / 1e9
     attn_gbps = attn_b / (attn_ms_mean * 1e-3) / 1e9
@@ -526,6 +562,15 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes": attn_b},
     }
+    if args.verify == "lmhead":
+        lm_ms = sum(ev_a[i][1].elapsed_time(ev_v[i]) for i in range(K)) / K
+        lm_gbps = ver_b / (lm_ms * 1e-3) / 1e9
+        result["config"]["d_model"] = wl.d_model
+        result["lmhead_verify_us"] = round(lm_ms * 1e3, 2)
+        result["attention_roofline"] = result["roofline"]
+        result["roofline"] = {"bound": "hbm", "kernel": "tidar_lmhead_verify_greedy", "achieved": round(lm_gbps, 2),
+                              "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(lm_gbps / HBM_PEAK_GBPS, 4),
+                              "traffic": None, "algorithmic_bytes": ver_b}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, d, v, a_planted, args)
     print(json.dumps(result))

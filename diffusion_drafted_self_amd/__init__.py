@@ -2,7 +2,8 @@
 
 The calls of ``include/tidar.h`` -- ``step_attention``,
 ``step_attention_paged``, ``train_attention``, ``verify_greedy``,
-``verify_sample``, ``kv_commit`` and ``kv_commit_paged`` -- under the same names, taking torch tensors that
+``lmhead_verify_greedy``, ``verify_sample``, ``kv_commit`` and
+``kv_commit_paged`` -- under the same names, taking torch tensors that
 live on the GPU.  This module only checks shapes and dtypes,
 marshals pointers and the current HIP stream, and allocates outputs /
 workspace with torch when the caller does not pass them.  Every step of the
@@ -49,6 +50,8 @@ SIGNATURES = {
     "tidar_step_attention_paged": (_c_int, [_c_int] * 10 + [_f, _c_int] + [_p] * 10 + [_c_size, _p]),
     "tidar_kv_commit_paged": (_c_int, [_c_int] * 8 + [_p] * 8 + [_p]),
     "tidar_train_attention": (_c_int, [_c_int] * 7 + [_f] + [_p] * 6),
+    "tidar_lmhead_verify_workspace": (_c_int, [_c_int] * 4 + [ctypes.POINTER(_c_size)]),
+    "tidar_lmhead_verify_greedy": (_c_int, [_c_int] * 4 + [_p] * 7 + [_c_size, _p]),
 }
 
 
@@ -317,6 +320,46 @@ def verify_greedy(ar_logits, draft_logits, cand, accept_len=None, next_cand=None
     return accept_len, next_cand
 
 
+def lmhead_verify_workspace_bytes(B: int, k: int, V: int, d_model: int) -> int:
+    n = _c_size(0)
+    _check("tidar_lmhead_verify_workspace", lib().tidar_lmhead_verify_workspace(B, k, V, d_model, ctypes.byref(n)))
+    return n.value
+
+
+def lmhead_verify_greedy(h_ar, h_draft, w, cand, accept_len=None, next_cand=None, workspace=None):
+    """LM head (logits = h . W^T, never stored) fused with greedy
+    verification.  h_ar [B][k+1][d], h_draft [B][k][k][d], w [V][d], all
+    bf16.  Returns (accept_len, next_cand)."""
+    _need(h_ar, "h_ar", torch.bfloat16, 3)
+    dev = h_ar.device
+    B, k1, d = h_ar.shape
+    k = k1 - 1
+    _need(w, "w", torch.bfloat16, 2, dev)
+    V = w.shape[0]
+    if w.shape[1] != d:
+        raise ValueError("w must be [V][d_model]")
+    _need(cand, "cand", torch.int32, 2, dev)
+    if tuple(cand.shape) != (B, k):
+        raise ValueError("cand must be [B][k]")
+    if k > 1 or h_draft is not None:
+        _need(h_draft, "h_draft", torch.bfloat16, 4, dev)
+        if tuple(h_draft.shape) != (B, k, k, d):
+            raise ValueError("h_draft must be [B][k][k][d_model]")
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    else:
+        _need(accept_len, "accept_len", torch.int32, 1, dev)
+    if next_cand is None:
+        next_cand = torch.empty((B, k), dtype=torch.int32, device=dev)
+    else:
+        _need(next_cand, "next_cand", torch.int32, 2, dev)
+    ws = _workspace(lmhead_verify_workspace_bytes(B, k, V, d), dev, workspace)
+    _check("tidar_lmhead_verify_greedy",
+           lib().tidar_lmhead_verify_greedy(B, k, V, d, _ptr(h_ar), _ptr(h_draft), _ptr(w), _ptr(cand),
+                                           _ptr(accept_len), _ptr(next_cand), _ptr(ws), ws.numel(), _stream()))
+    return accept_len, next_cand
+
+
 def verify_sample_workspace_bytes(B: int, k: int, V: int) -> int:
     n = _c_size(0)
     _check("tidar_verify_sample_workspace", lib().tidar_verify_sample_workspace(B, k, V, ctypes.byref(n)))
@@ -415,4 +458,5 @@ def kv_commit_paged(k_pool, v_pool, block_table, lens, k_step, v_step, accept_le
 
 __all__ = ["step_attention", "step_attention_workspace_bytes", "verify_greedy", "verify_workspace_bytes",
            "verify_sample", "verify_sample_workspace_bytes", "kv_commit",
-           "step_attention_paged", "kv_commit_paged", "train_attention", "strerror", "lib", "TidarError", "LIB_PATH", "SIGNATURES"]
+           "step_attention_paged", "kv_commit_paged", "train_attention",
+           "lmhead_verify_greedy", "lmhead_verify_workspace_bytes", "strerror", "lib", "TidarError", "LIB_PATH", "SIGNATURES"]

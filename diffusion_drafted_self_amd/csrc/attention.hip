@@ -29,6 +29,7 @@
 //       query row: normalised output (RNE to the output type) and the LSE.
 #include "common.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace tidar {
 
@@ -128,45 +129,9 @@ __device__ __forceinline__ int kswz(int row) {
 // folded in bit 3 of the row conflicted on 40% of the active cycles.
 __device__ __forceinline__ int vswz(int d) { return d & 7; }
 
-// LDS pointers stay in address space 3 end to end (no generic casts)
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0]+[15:14], expcnt[6:4], lgkmcnt[11:8])
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
-}
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
-// Workgroup barrier that is also a compiler memory barrier: LDS reads and
-// writes stay on their side of it.  Waiting for this wave's own memory
-// operations is left to the caller (the ring waits for some direct loads
-// only).
-__device__ __forceinline__ void barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Direct global->LDS load of 16 B per lane: lane t's bytes land at
-// lds_dst + 16*t.  Issued as inline asm with a scalar base and a 32-bit
-// per-lane offset, so the compiler neither rebuilds 64-bit addresses every
-// tile nor treats the load as an LDS store it must order against unrelated
-// LDS reads (its LDS-DMA alias tracking would serialise the pipeline); the
-// kernel orders these loads itself with s_waitcnt vmcnt and barriers.  No
-// output registers are involved.
-__device__ __forceinline__ void dma_b128(const char* base, unsigned off, lds_char* lds_dst) {
-  const unsigned long long b = (unsigned long long)base;
-  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)b);
-  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
-  const unsigned long long sb = ((unsigned long long)hi << 32) | lo;
-  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_dst);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(sb), "s"(m0) : "memory", "m0");
-}
 
 // Per-lane byte offsets of this wave's direct loads inside a tile: wave w
 // moves the 1 KB blocks w*NKW .. w*NKW+NKW-1 of the K tile and

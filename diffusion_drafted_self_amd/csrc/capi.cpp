@@ -152,6 +152,25 @@ int plan_verify(int B, int k, int V, VerifyPlan* p) {
   return TIDAR_OK;
 }
 
+struct LmPlan {
+  int n_chunks;
+  size_t ar_bytes, draft_bytes, group_bytes, total;
+};
+
+int plan_lmhead(int B, int k, int V, int d, LmPlan* p) {
+  if (k > kMaxK) return TIDAR_EUNSUPPORTED;
+  if (B < 0 || k < 1 || V < 1 || d < 64 || d % 64 != 0) return TIDAR_EINVAL;
+  // direct loads address W and the hidden rows with 32-bit byte offsets
+  if ((double)V * d * 2 >= 4294967296.0 || (double)B * k * k * d * 2 >= 4294967296.0) return TIDAR_EUNSUPPORTED;
+  p->n_chunks = (int)cdiv(V, tidar::kLmChunk);
+  if (cdiv((long)B * (k + 1), tidar::kLmRows) > 65535) return TIDAR_EUNSUPPORTED;
+  p->ar_bytes = round_up((size_t)B * (k + 1) * p->n_chunks * sizeof(float2), 256);
+  p->draft_bytes = round_up((size_t)B * (k - 1) * p->n_chunks * sizeof(float2), 256);
+  p->group_bytes = round_up((size_t)B * sizeof(int32_t), 256);
+  p->total = p->ar_bytes + p->draft_bytes + p->group_bytes;
+  return TIDAR_OK;
+}
+
 struct SamplePlan {
   int n_chunks;
   size_t stats_bytes, resid_bytes, part_bytes, fb_bytes, total;
@@ -409,6 +428,70 @@ int tidar_verify_greedy(int B, int k, int V, const float* ar_logits, const float
   a.chunk_elems = kVerifyChunk;
   a.n_chunks = p.n_chunks;
   const hipError_t e = tidar::launch_verify(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
+}
+
+int tidar_lmhead_verify_workspace(int B, int k, int V, int d_model, size_t* bytes) {
+  if (!bytes) return TIDAR_EINVAL;
+  LmPlan p;
+  const int st = plan_lmhead(B, k, V, d_model, &p);
+  if (st != TIDAR_OK) return st;
+  *bytes = p.total;
+  return TIDAR_OK;
+}
+
+int tidar_lmhead_verify_greedy(int B, int k, int V, int d_model, const void* h_ar, const void* h_draft,
+                               const void* w, const int32_t* cand, int32_t* accept_len, int32_t* next_cand,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  LmPlan p;
+  const int st = plan_lmhead(B, k, V, d_model, &p);
+  if (st != TIDAR_OK) return st;
+  if (B == 0) return TIDAR_OK;
+  if (!aligned(h_ar, 16) || !aligned(w, 16) || !aligned(cand, 4) || !aligned(accept_len, 4) ||
+      !aligned(next_cand, 4))
+    return TIDAR_EINVAL;
+  if (k > 1 && !aligned(h_draft, 16)) return TIDAR_EINVAL;
+  if (!aligned(workspace, 256) || workspace_bytes < p.total) return TIDAR_EWORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  tidar::VerifyArgs va = {};
+  va.cand = cand;
+  va.accept_len = accept_len;
+  va.next_cand = next_cand;
+  va.part_ar = reinterpret_cast<float2*>(ws);
+  va.part_draft = reinterpret_cast<float2*>(ws + p.ar_bytes);
+  va.group = reinterpret_cast<int32_t*>(ws + p.ar_bytes + p.draft_bytes);
+  va.B = B;
+  va.k = k;
+  va.V = V;
+  va.chunk_elems = tidar::kLmChunk;
+  va.n_chunks = p.n_chunks;
+
+  tidar::LmArgs la = {};
+  la.w = w;
+  la.B = B;
+  la.k = k;
+  la.V = V;
+  la.d = d_model;
+  la.n_chunks = p.n_chunks;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // AR rows -> chunk results -> accept length, bonus token, group
+  la.h = h_ar;
+  la.part = va.part_ar;
+  la.rows = B * (k + 1);
+  la.draft = 0;
+  hipError_t e = tidar::launch_lmhead_argmax(la, s);
+  if (e == hipSuccess) e = tidar::launch_verify_select(va, s);
+  // the selected group's draft rows -> next drafts
+  if (e == hipSuccess && k > 1) {
+    la.h = h_draft;
+    la.group = va.group;
+    la.part = va.part_draft;
+    la.rows = B * (k - 1);
+    la.draft = 1;
+    e = tidar::launch_lmhead_argmax(la, s);
+    if (e == hipSuccess) e = tidar::launch_draft_finalize(va, s);
+  }
   return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
 }
 

@@ -54,6 +54,22 @@ struct VerifyArgs {
 };
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
+hipError_t launch_verify_select(const VerifyArgs& a, hipStream_t s);
+hipError_t launch_draft_finalize(const VerifyArgs& a, hipStream_t s);
+
+// LM head fused with the argmax: chunk results of logits = h . W^T
+constexpr int kLmChunk = 256;   // vocabulary entries per workgroup
+constexpr int kLmRows = 144;    // hidden-state rows per workgroup (9 tiles of 16)
+
+struct LmArgs {
+  const void* h;        // pass 0: [B][k+1][d] AR rows; pass 1: [B][k][k][d] draft rows
+  const void* w;        // [V][d] bf16
+  const int32_t* group; // [B] selected group (pass 1)
+  float2* part;         // [rows][n_chunks] (value, index bits)
+  int B, k, V, d, n_chunks, rows, draft;
+};
+
+hipError_t launch_lmhead_argmax(const LmArgs& a, hipStream_t s);
 
 constexpr int kSampleChunk = 4096;  // vocabulary entries per workgroup of the sampling kernels
 

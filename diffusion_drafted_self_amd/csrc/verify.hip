@@ -154,6 +154,21 @@ __global__ __launch_bounds__(64 * kMaxWaves) void draft_finalize_kernel(VerifyAr
 
 }  // namespace
 
+// The selection and the draft finalisation on their own, for producers of
+// the chunk results other than argmax_partial_kernel (the fused LM head).
+hipError_t launch_verify_select(const VerifyArgs& a, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  if (a.k + 1 > kMaxRows) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(verify_select_kernel, dim3(a.B), dim3(64 * std::min(a.k + 1, kMaxWaves)), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_draft_finalize(const VerifyArgs& a, hipStream_t s) {
+  if (a.B == 0 || a.k == 1) return hipSuccess;
+  hipLaunchKernelGGL(draft_finalize_kernel, dim3(a.B), dim3(64 * std::min(a.k - 1, kMaxWaves)), 0, s, a);
+  return hipGetLastError();
+}
+
 // Each launch is checked before the next: the draft kernels index rows by
 // the group the selection writes.
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t s) {

@@ -214,6 +214,38 @@ int tidar_verify_greedy(int B, int k, int V, const float* ar_logits, const float
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * LM head fused with greedy verification.
+ *
+ * The single pass yields the joint distribution that verifies and the
+ * marginals that draft (section "2. Single Forward Pass & Structured
+ * Attention Mask" of the mauroscia.it page); both are the LM head applied
+ * to the pass's final hidden states, and verification needs only each
+ * row's argmax.  This call computes logits = h . W^T (bf16 inputs, fp32
+ * accumulation) for the k+1 AR rows and, once the accept length is known,
+ * for the selected group's draft rows 1..k-1, keeping only per-chunk
+ * (max, lower index) results -- no logits are written -- and then applies
+ * exactly the rule of tidar_verify_greedy to them.
+ *
+ *   d_model   hidden size: a multiple of 64.  V * d_model * 2 and
+ *             B * k * k * d_model * 2 must be below 2^32 (byte offsets).
+ *   h_ar      [B][k+1][d_model] bf16: row 0 the carried hidden state,
+ *             row i >= 1 the output of candidate row i-1.
+ *   h_draft   [B][k][k][d_model] bf16: slot s of group g; only the selected
+ *             group's rows 1..k-1 are read.  May be NULL when k == 1.
+ *   w         [V][d_model] bf16, the LM head (one row per vocabulary entry).
+ *   cand, accept_len, next_cand   as for tidar_verify_greedy.
+ *   workspace at least tidar_lmhead_verify_workspace() bytes.
+ * Inputs must be finite.  The argmax is over fp32 logits, so a row whose
+ * two best logits lie within fp32 accumulation error of each other may
+ * differ from an exact evaluation.
+ * ---------------------------------------------------------------------- */
+int tidar_lmhead_verify_workspace(int B, int k, int V, int d_model, size_t* bytes);
+
+int tidar_lmhead_verify_greedy(int B, int k, int V, int d_model, const void* h_ar, const void* h_draft,
+                               const void* w, const int32_t* cand, int32_t* accept_len, int32_t* next_cand,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Stochastic verification (temperature T > 0) and sampling of the next drafts.
  *
  * The final tokens are sampled autoregressively and the output matches

@@ -185,3 +185,20 @@ def test_train_attention_validation(T):
     for name, (args, want) in bad.items():
         assert f(*args) == want, name
     assert f(*([0, 0, 8, 2, 128, 128, 8, 0.1] + [None] * 6)) == 0
+
+
+def test_lmhead_validation_and_size(T):
+    L = T.lib()
+    n = ctypes.c_size_t(0)
+    assert L.tidar_lmhead_verify_workspace(16, 8, 128256, 4096, ctypes.byref(n)) == 0
+    chunks = -(-128256 // 256)
+    want = sum(-(-x // 256) * 256 for x in (16 * 9 * chunks * 8, 16 * 7 * chunks * 8, 16 * 4))
+    assert n.value == want
+    assert L.tidar_lmhead_verify_workspace(16, 8, 128256, 100, ctypes.byref(n)) == -1   # d % 64
+    assert L.tidar_lmhead_verify_workspace(16, 17, 1000, 64, ctypes.byref(n)) == -2     # k
+    assert L.tidar_lmhead_verify_workspace(1, 1, 600000, 4096, ctypes.byref(n)) == -2   # W past 32-bit offsets
+    p = ctypes.c_void_p(0x100000)
+    f = L.tidar_lmhead_verify_greedy
+    assert f(2, 4, 1000, 64, p, p, p, p, p, p, p, 8, None) == -3
+    assert f(2, 4, 1000, 64, p, None, p, p, p, p, p, 1 << 20, None) == -1
+    assert f(0, 4, 1000, 64, None, None, None, None, None, None, None, 0, None) == 0

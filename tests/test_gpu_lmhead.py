@@ -1,0 +1,98 @@
+"""GPU parity of tidar_lmhead_verify_greedy (LM head fused with greedy
+verification) against the oracle.
+
+Accept lengths and tokens must be identical, except where the oracle's two
+best logits of a decided row lie within MARGIN of each other: the kernel
+takes the argmax over fp32 accumulations of bf16 products, the oracle in
+float64, so such a row may legitimately go either way.  A close AR row
+fixes only the rows before it; a close draft row fixes the others."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle.lmhead import lmhead_verify_ref
+
+pytestmark = pytest.mark.gpu
+
+tidar = pytest.importorskip("diffusion_drafted_self_amd")
+from _gpu_util import to_dev  # noqa: E402
+
+MARGIN = 1e-3
+
+
+def _run(d):
+    hd = None if d["h_draft"] is None else to_dev(d["h_draft"], True)
+    a, n = tidar.lmhead_verify_greedy(to_dev(d["h_ar"], True), hd, to_dev(d["w"], True), to_dev(d["cand"]))
+    return a.cpu().numpy(), n.cpu().numpy()
+
+
+def _f32(x):
+    return None if x is None else W.bf16_to_f32(x)
+
+
+def _compare(d, a, n, seqs, what):
+    k = d["cand"].shape[1]
+    sub = lambda x: None if x is None else x[seqs]
+    ra, rn, mg = lmhead_verify_ref(_f32(sub(d["h_ar"])), _f32(sub(d["h_draft"])), _f32(d["w"]), d["cand"][seqs],
+                                   margins=True)
+    near = 0
+    for j, b in enumerate(seqs):
+        m = mg[j]
+        n_ar = len(m) - (k - 1)  # AR rows decided: a + 1
+        close_ar = [i for i in range(n_ar) if m[i] < MARGIN]
+        close_dr = [i for i in range(k - 1) if m[n_ar + i] < MARGIN]
+        near += bool(close_ar or close_dr)
+        if close_ar:
+            assert a[b] >= close_ar[0], f"{what} b={b}: accept {a[b]} below close row {close_ar[0]}"
+            continue
+        assert a[b] == ra[j], f"{what} b={b}: accept {a[b]} != {ra[j]}"
+        assert n[b, 0] == rn[j, 0], f"{what} b={b}: bonus token"
+        far = [1 + i for i in range(k - 1) if i not in close_dr]
+        assert n[b, far].tolist() == rn[j, far].tolist(), f"{what} b={b}: drafts"
+    return near
+
+
+@pytest.mark.parametrize("B,k,V,d,accept", [
+    (4, 8, 32000, 1024, "uniform"),
+    (6, 4, 5003, 256, "uniform"),      # V ends mid-chunk
+    (5, 1, 1000, 64, "uniform"),       # no drafts
+    (150, 3, 257, 128, "uniform"),     # 600 AR rows: five row groups; a one-entry last chunk
+    (3, 16, 4096, 512, "geometric"),   # k = 16
+])
+def test_lmhead_verify_matches_oracle(B, k, V, d, accept):
+    print(f"lmhead B={B} k={k} V={V} d={d}", flush=True)
+    data = W.lmhead_inputs(B, k, V, d, seed=B + k + d, accept=accept)
+    a, n = _run(data)
+    near = _compare(data, a, n, list(range(B)), f"B={B} k={k} V={V} d={d}")
+    assert near <= max(1, B // 8)
+    assert a.tolist() == data["planted"].tolist()  # planted rows have wide margins
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,B,k,V,d", [("8B", 16, 8, 128256, 4096), ("1.5B", 8, 4, 151936, 1536)])
+def test_lmhead_verify_full_size(name, B, k, V, d):
+    """The 8B- and 1.5B-shaped heads on the whole batch; the oracle checks
+    three sequences (each row costs it a V x d product in float64), the
+    planted accept lengths check all of them."""
+    print(f"lmhead full size {name}: B={B} k={k} V={V} d={d}", flush=True)
+    data = W.lmhead_inputs(B, k, V, d, seed=5, accept="uniform")
+    a, n = _run(data)
+    assert a.tolist() == data["planted"].tolist()
+    assert ((n >= 0) & (n < V)).all()
+    _compare(data, a, n, [0, B // 2, B - 1], name)
+
+
+def test_equal_logits_take_the_lowest_index_across_chunks():
+    B, k, V, d = 2, 3, 800, 128
+    data = W.lmhead_inputs(B, k, V, d, seed=9, accept="uniform")
+    w = data["w"].copy()
+    w[300] = w[17]
+    w[700] = w[17]       # three equal rows in three chunks of 256
+    data["w"] = w
+    h = data["h_ar"].copy()
+    h[:, 0] = W.bf16_bits(np.float32(12.0) * W.bf16_to_f32(w[300]))  # AR row 0 aligned with the tied rows
+    data["h_ar"] = h
+    data["cand"][:, 0] = 17
+    a, n = _run(data)
+    ra, rn = lmhead_verify_ref(_f32(data["h_ar"]), _f32(data["h_draft"]), _f32(data["w"]), data["cand"])
+    assert (a >= 1).all() and a.tolist() == ra.tolist() and n.tolist() == rn.tolist()

@@ -48,6 +48,7 @@ _T_TINY_W, _T_PROMPT, _T_INJECT = 21, 22, 23
 _T_QLOG, _T_QBOOST, _T_SHIFT, _T_MASK = 31, 32, 33, 34
 _T_PAGES = 41
 _T_TQ, _T_TK, _T_TV = 51, 52, 53
+_T_LW, _T_LH, _T_LD, _T_LN, _T_LT = 61, 62, 63, 64, 65
 
 MASK_TOKEN_TINY = 1024  # extra embedding row of the tiny decoder; outside its LM head
 VPAGE = 64  # positions per value-cache page
@@ -126,6 +127,7 @@ class Workload:
     accept: str            # "boost" | "uniform" | "geometric"
     steps: int = 1
     description: str = ""
+    d_model: int = 4096    # hidden size feeding the LM head (1536 at 1.5B, 4096 at 8B)
 
 
 def _lens(B, L):
@@ -138,7 +140,7 @@ def step_1p5b() -> Workload:
                     AttnShape(B=8, Hq=12, Hkv=2, D=128, k=4, n_groups=4, lens=_lens(8, 2048),
                               S_max=2048 + 64, sm_scale=1.0 / math.sqrt(128.0)),
                     V=151936, accept="boost",
-                    description="B8 Hq12 Hkv2 D128 L2048 k4 bf16; verify V=151936, +4 boost at p=0.7")
+                    description="B8 Hq12 Hkv2 D128 L2048 k4 bf16; verify V=151936, +4 boost at p=0.7", d_model=1536)
 
 
 def step_8b() -> Workload:
@@ -259,6 +261,32 @@ def train_inputs(B: int, Hq: int, Hkv: int, D: int, N: int, seed: int, config_id
     k_l = np.ascontiguousarray(kb.transpose(0, 2, 1, 3))
     v_l = v_paged(np.ascontiguousarray(vb.transpose(0, 2, 1, 3)))
     return {"q": qb, "k_nat": kb, "v_nat": vb, "k": k_l, "v": v_l}
+
+
+def lmhead_inputs(B: int, k: int, V: int, d: int, seed: int, accept: str = "uniform", config_id: int = 7,
+                  strength: float = 12.0) -> dict:
+    """Inputs of the fused LM head + verify, bf16 bits: w [V][d] from
+    N(0, 1/d), h_draft [B][k][k][d] and h_ar [B][k+1][d] from N(0, 1),
+    candidates uniform in [0, V).  Accept lengths are planted (``planted``)
+    by aligning hidden rows with rows of w: AR row i < a is strength *
+    w[cand[i]] plus N(0, 1) noise, row a (if a < k) is strength * w[t] for
+    a t other than cand[a]; the other rows stay random."""
+    g_w = generator(seed, config_id, 0, _T_LW)
+    w = (g_w.standard_normal(size=(V, d), dtype=np.float32) * np.float32(1.0 / math.sqrt(d)))
+    h_ar = _normal(generator(seed, config_id, 0, _T_LH), (B, k + 1, d))
+    h_dr = _normal(generator(seed, config_id, 0, _T_LD), (B, k, k, d)) if k > 1 else None
+    cand = generator(seed, config_id, 0, _T_CAND).integers(0, V, size=(B, k)).astype(np.int32)
+    planted = accept_lengths(accept, B, k, seed, 0, config_id)
+    other = generator(seed, config_id, 0, _T_LT).integers(1, V, size=B)
+    for b in range(B):
+        a = int(planted[b])
+        for i in range(a):
+            h_ar[b, i] += np.float32(strength) * w[cand[b, i]]
+        if a < k:
+            t = (int(cand[b, a]) + int(other[b])) % V
+            h_ar[b, a] = np.float32(strength) * w[t]
+    return {"w": bf16_bits(w), "h_ar": bf16_bits(h_ar), "h_draft": None if h_dr is None else bf16_bits(h_dr),
+            "cand": cand, "planted": planted}
 
 
 def to_f32(x: np.ndarray, dtype: str) -> np.ndarray:
