@@ -50,7 +50,7 @@ HBM_PEAK_GBPS = 8000.0
 COPY_CALIB_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_step_8b_traffic.txt")
 ATTN_SOURCES = [os.path.join(ROOT, "diffusion_drafted_self_amd", "csrc", n)
-                for n in ("attention.hip", "common.h", "launch.h")]
+                for n in ("attention.hip", "common.h", "launch.h", "lds_dma.h")]
 
 
 def parse():
