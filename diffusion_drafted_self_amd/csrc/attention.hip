@@ -176,15 +176,11 @@ __device__ __forceinline__ void issue_v(lds_char* sV, const bf16* vtile, const D
   for (int ii = 0; ii < T::NVW; ++ii) dma_b128(vt, pl.v[ii], sV + (wave * T::NVW + ii) * 1024);
 }
 
-// Stage a tile that reaches past the settled prefix (the step block, or
-// keys past the end) into the same swizzled layout.  Settled keys come from
-// the tile's cache rows `kt` / value page `vt` (null when the tile holds no
-// settled position) in 16 B pieces; step rows are read 16 B at a time and
-// their values scattered into V^T columns; everything else is zero.
+// Stage a tile one 16 B piece at a time (see stage_tail_tile).
 template <int D>
-__device__ __forceinline__ void stage_tail_tile(lds_char* sK, lds_char* sV, const bf16* kt, const bf16* vt,
-                                                const bf16* ks_base, const bf16* vs_base, size_t step_stride,
-                                                int t0, int L, int Ltot, int tid) {
+__device__ __forceinline__ void stage_tail_tile_lean(lds_char* sK, lds_char* sV, const bf16* kt, const bf16* vt,
+                                                     const bf16* ks_base, const bf16* vs_base, size_t step_stride,
+                                                     int t0, int L, int Ltot, int tid) {
   using T = Tile<D>;
   for (int id = tid; id < TK * T::KPPR; id += NWV * 64) {
     const int row = id / T::KPPR, p = id % T::KPPR;
@@ -194,7 +190,6 @@ __device__ __forceinline__ void stage_tail_tile(lds_char* sK, lds_char* sV, cons
     else if (c < Ltot) val = *(const bf16x8*)(ks_base + (size_t)(c - L) * step_stride + p * 8);
     *(lds_bf16x8*)(sK + row * T::KROW + ((p ^ kswz<D>(row)) * 16)) = val;
   }
-  // settled part of V^T (pieces of 8 positions), zero elsewhere
   for (int id = tid; id < D * 8; id += NWV * 64) {
     const int d = id >> 3, q = id & 7;
     const int c0 = t0 + q * 8;
@@ -209,10 +204,6 @@ __device__ __forceinline__ void stage_tail_tile(lds_char* sK, lds_char* sV, cons
   }
   wait_all();
   barrier();
-  // step rows: one 16 B load of 8 head-dim elements, scattered into 8 V^T
-  // rows.  Consecutive lanes take consecutive keys, so each 2-byte store of
-  // a wave fills one V^T row across 64 columns (lanes on the same column
-  // would all hit one bank).
   const int j0 = max(t0, L), j1 = min(t0 + TK, Ltot);
   for (int id = tid; id < TK * (D / 8); id += NWV * 64) {
     const int cl = id % TK, dc = id / TK;
@@ -223,6 +214,91 @@ __device__ __forceinline__ void stage_tail_tile(lds_char* sK, lds_char* sV, cons
     for (int e = 0; e < 8; ++e) {
       const int d = dc * 8 + e;
       *(__attribute__((address_space(3))) bf16*)(sV + d * T::VROW + ((((cl >> 3) ^ vswz(d)) * 16)) + (cl & 7) * 2) = val[e];
+    }
+  }
+}
+
+// Stage a tile that reaches past the settled prefix (the step block, or
+// keys past the end) into the same swizzled layout.  Settled keys come from
+// the tile's cache rows `kt` / value page `vt` (null when the tile holds no
+// settled position) in 16 B pieces; step rows are read 16 B at a time and
+// their values scattered into V^T columns; everything else is zero.
+//
+// BATCH: the loads of a piece kind are issued together (their latencies
+// overlap); without it, one piece at a time (kernels whose registers are
+// already near the limit).
+template <int D, bool BATCH>
+__device__ __forceinline__ void stage_tail_tile(lds_char* sK, lds_char* sV, const bf16* kt, const bf16* vt,
+                                                const bf16* ks_base, const bf16* vs_base, size_t step_stride,
+                                                int t0, int L, int Ltot, int tid) {
+  using T = Tile<D>;
+  if constexpr (!BATCH) {
+    stage_tail_tile_lean<D>(sK, sV, kt, vt, ks_base, vs_base, step_stride, t0, L, Ltot, tid);
+    return;
+  }
+  constexpr int NT = NWV * 64;
+  constexpr int NK = TK * T::KPPR / NT;   // K pieces per thread
+  constexpr int NVS = D * 8 / NT;         // V^T pieces (8 positions) per thread
+  constexpr int NVR = TK * (D / 8) / NT;  // step-row value pieces per thread
+  static_assert(NK * NT == TK * T::KPPR && NVS * NT == D * 8 && NVR * NT == TK * (D / 8), "staging split");
+  const int j0 = max(t0, L), j1 = min(t0 + TK, Ltot);
+  // two batches of loads, each issued whole so their latencies overlap:
+  // K and the step rows' values (every masked tile has step rows or keys
+  // past the end), then the settled part of V^T (only a prefix that is not
+  // a multiple of the tile has one inside a masked tile)
+  bf16x8 kp[NK], vr[NVR];
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const int id = tid + i * NT, row = id / T::KPPR, p = id % T::KPPR;
+    const int c = t0 + row;
+    kp[i] = (bf16x8){};
+    if (c < L) kp[i] = *(const bf16x8*)(kt + (size_t)row * D + p * 8);
+    else if (c < Ltot) kp[i] = *(const bf16x8*)(ks_base + (size_t)(c - L) * step_stride + p * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < NVR; ++i) {  // step rows: 8 head-dim elements of one key
+    const int id = tid + i * NT, cl = id % TK, dc = id / TK;
+    const int c = t0 + cl;
+    vr[i] = (bf16x8){};
+    if (c >= j0 && c < j1) vr[i] = *(const bf16x8*)(vs_base + (size_t)(c - L) * step_stride + dc * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const int id = tid + i * NT, row = id / T::KPPR, p = id % T::KPPR;
+    *(lds_bf16x8*)(sK + row * T::KROW + ((p ^ kswz<D>(row)) * 16)) = kp[i];
+  }
+  bf16x8 vp[NVS];
+#pragma unroll
+  for (int i = 0; i < NVS; ++i) {  // settled part of V^T, zero elsewhere
+    const int id = tid + i * NT, d = id >> 3, q = id & 7;
+    const int c0 = t0 + q * 8;
+    vp[i] = (bf16x8){};
+    if (c0 + 8 <= L) {
+      vp[i] = *(const bf16x8*)(vt + (size_t)d * VPAGE + q * 8);
+    } else if (c0 < L) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vp[i][e] = c0 + e < L ? vt[(size_t)d * VPAGE + q * 8 + e] : (bf16)0.f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NVS; ++i) {
+    const int id = tid + i * NT, d = id >> 3, q = id & 7;
+    *(lds_bf16x8*)(sV + d * T::VROW + ((q ^ vswz(d)) * 16)) = vp[i];
+  }
+  wait_all();
+  barrier();  // the scatter below overwrites 2-byte parts of those pieces
+  // step rows scattered into 8 V^T rows.  Consecutive lanes take
+  // consecutive keys, so each 2-byte store of a wave fills one V^T row
+  // across 64 columns (lanes on the same column would all hit one bank).
+#pragma unroll
+  for (int i = 0; i < NVR; ++i) {
+    const int id = tid + i * NT, cl = id % TK, dc = id / TK;
+    const int c = t0 + cl;
+    if (c < j0 || c >= j1) continue;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = dc * 8 + e;
+      *(__attribute__((address_space(3))) bf16*)(sV + d * T::VROW + ((((cl >> 3) ^ vswz(d)) * 16)) + (cl & 7) * 2) = vr[i][e];
     }
   }
 }
@@ -378,8 +454,7 @@ __device__ __forceinline__ float exact_ref(const float* s, float& m, float& l, f
   float mx = -INFINITY;
 #pragma unroll
   for (int v = 0; v < NV; ++v) mx = fmaxf(mx, s[v]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = row4_max(mx);
   const float m_new = fmaxf(m, mx * sl2);
   const float alpha = __builtin_amdgcn_exp2f(m - m_new);
   m = m_new;
@@ -713,14 +788,18 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
   // paged: the page of the last K tile requested; the V tile a ring step
   // requests is the K tile of the step before, so its page is known
   size_t pg_last_k = 0;
-  if (n > 0) issue_k<D>(kslot(0), kv.ktile(tb), plan, wave);
-  if (n > 1) issue_k<D>(kslot(1), kv.ktile(tb + 1), plan, wave);
-  if (n > 0) issue_v<D>(vslot(0), kv.vtile(tb), plan, wave);
-  if (n > 2) {
-    pg_last_k = kv.page(tb + 2);
-    issue_k<D>(kslot(2), kv.k + pg_last_k * kv.stride, plan, wave);
-  }
-  if (n > 1) issue_v<D>(vslot(1), kv.vtile(tb + 1), plan, wave);
+  // issued once the masked tiles below have staged their data (their waits
+  // would otherwise include it), so it lands while they compute
+  auto ring_prologue = [&]() {
+    if (n > 0) issue_k<D>(kslot(0), kv.ktile(tb), plan, wave);
+    if (n > 1) issue_k<D>(kslot(1), kv.ktile(tb + 1), plan, wave);
+    if (n > 0) issue_v<D>(vslot(0), kv.vtile(tb), plan, wave);
+    if (n > 2) {
+      pg_last_k = kv.page(tb + 2);
+      issue_k<D>(kslot(2), kv.k + pg_last_k * kv.stride, plan, wave);
+    }
+    if (n > 1) issue_v<D>(vslot(1), kv.vtile(tb + 1), plan, wave);
+  };
 
   QFrags<D, NF, NS> q;
   auto load_q = [&](int m, bool ok_row, bf16x8 (&dst)[D / 32]) {
@@ -761,51 +840,66 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
   // masked by zone, softmax with the exact path.
   const int zoff = TRAIN ? 0 : L;  // zone tests take step-row indices (decode) or positions (training)
   auto zone = [&](int m) { return TRAIN ? train_zone(m / a.G, a.train_N, a.train_bs) : step_zone(m / a.G, a.k); };
-  auto tail_tiles = [&]() {
-    // one loop over both ranges: a single inlined body
-    const int nA = (mA1 - mA0 + TK - 1) / TK, nB = (mB1 - mB0 + TK - 1) / TK;  // a range may end mid-tile
-    for (int i = 0; i < nA + nB; ++i) {
-      const int t0 = i < nA ? mA0 + i * TK : mB0 + (i - nA) * TK;
-      lds_char* sK = kslot(RING - 1);
-      lds_char* sV = vslot(RING - 1);
-      barrier();
-      const bool settled = t0 < L;  // the tile holds settled positions (its page is in the table)
-      stage_tail_tile<D>(sK, sV, settled ? kv.ktile(t0 / TK) : nullptr, settled ? kv.vtile(t0 / TK) : nullptr,
-                         ks_base, vs_base, step_stride, t0, L, Ltot, tid);
-      wait_all();
-      barrier();
-      s_tile<D, NF, NS>(sK, q, sA, lane, wave);
-      // branch-free selects: no divergent control flow around the vector
-      // element updates
+  const int nA = (mA1 - mA0 + TK - 1) / TK, nB = (mB1 - mB0 + TK - 1) / TK;  // a range may end mid-tile
+  auto tail_t0 = [&](int i) { return i < nA ? mA0 + i * TK : mB0 + (i - nA) * TK; };
+  auto tail_stage = [&](int i) {
+    const int t0 = tail_t0(i);
+    barrier();
+    const bool settled = t0 < L;  // the tile holds settled positions (its page is in the table)
+    stage_tail_tile<D, !(D == 128 && NF + NS >= 4)>(kslot(RING - 1), vslot(RING - 1), settled ? kv.ktile(t0 / TK) : nullptr,
+                       settled ? kv.vtile(t0 / TK) : nullptr, ks_base, vs_base, step_stride, t0, L, Ltot, tid);
+    wait_all();
+    barrier();
+  };
+  auto tail_compute = [&](int i) {
+    const int t0 = tail_t0(i);
+    lds_char* sK = kslot(RING - 1);
+    lds_char* sV = vslot(RING - 1);
+    s_tile<D, NF, NS>(sK, q, sA, lane, wave);
+    // branch-free selects: no divergent control flow around the vector
+    // element updates
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const StepZone z = zone(mrow[f]);
+    for (int f = 0; f < NF; ++f) {
+      const StepZone z = zone(mrow[f]);
 #pragma unroll
-        for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int c = t0 + krow_of(kb4, 4 * hi + v);
-            const bool vis = (c < ke) & z.sees(c - zoff);
-            sA.s[f][kb4][v] = vis ? sA.s[f][kb4][v] : -INFINITY;
-          }
-      }
-#pragma unroll
-      for (int s2 = 0; s2 < NS; ++s2) {
-        const StepZone z = zone(mrow_s[s2]);
+      for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int c = t0 + krow_of(wave, 4 * hi + v);
+          const int c = t0 + krow_of(kb4, 4 * hi + v);
           const bool vis = (c < ke) & z.sees(c - zoff);
-          sA.ss[s2][v] = vis ? sA.ss[s2][v] : -INFINITY;
+          sA.s[f][kb4][v] = vis ? sA.s[f][kb4][v] : -INFINITY;
         }
-      }
-      const bool big = sm_tile<D, NF, NS>(sA, pA, ac, sl2);
-      softmax_commit<D, NF, NS>(big, sA, pA, ac, sl2);
-      pv_tile<D, NF, NS>(sV, pA, ac, lane, wave);
-      wait_lgkmcnt0();
     }
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2) {
+      const StepZone z = zone(mrow_s[s2]);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int c = t0 + krow_of(wave, 4 * hi + v);
+        const bool vis = (c < ke) & z.sees(c - zoff);
+        sA.ss[s2][v] = vis ? sA.ss[s2][v] : -INFINITY;
+      }
+    }
+    const bool big = sm_tile<D, NF, NS>(sA, pA, ac, sl2);
+    softmax_commit<D, NF, NS>(big, sA, pA, ac, sl2);
+    pv_tile<D, NF, NS>(sV, pA, ac, lane, wave);
+    wait_lgkmcnt0();
   };
-  tail_tiles();
+  // The ring prologue is requested once the last masked tile has landed:
+  // a load issued after it would wait for it (loads complete in order).
+  // It then lands while that tile computes (its slots 0..RING-2 are not
+  // that tile's).
+  for (int i = 0; i + 1 < nA + nB; ++i) {
+    tail_stage(i);
+    tail_compute(i);
+  }
+  if (nA + nB > 0) {
+    tail_stage(nA + nB - 1);
+    ring_prologue();
+    tail_compute(nA + nB - 1);
+  } else {
+    ring_prologue();
+  }
 
   if (n > 0) {
     // Tile 0 is scored and its softmax taken with the exact path, so every
@@ -900,7 +994,10 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
         pv_tile<D, NF, NS>(vslot(0), pA, ac, lane, wave);
         wait_lgkmcnt0();
       }
-      tail_tiles();
+      for (int i = 0; i < nA + nB; ++i) {
+        tail_stage(i);
+        tail_compute(i);
+      }
     }
   }
 
@@ -932,8 +1029,7 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     float lt = ac.l[f];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    lt = row4_sum(lt);
     emit(mrow[f], ok[f], ac.o[f], ac.m[f], lt);
   }
 
@@ -949,8 +1045,7 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int s2 = 0; s2 < NS; ++s2) {
       float lt = ac.ls[s2];
-      lt += __shfl_xor(lt, 16);
-      lt += __shfl_xor(lt, 32);
+      lt = row4_sum(lt);
 #pragma unroll
       for (int db = 0; db < D / 16; ++db)
         *(floatx4*)(mo + (((s2 * 4 + wave) * (D / 16) + db) * 64 + lane) * 4) = ac.os[s2][db];

@@ -13,6 +13,23 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
+// Reductions over the four lanes l, l^16, l^32, l^48 of a wave (the lanes
+// that hold one row of an MFMA 16x16 result), with the gfx950 row-swap
+// instructions instead of LDS permutes: the 32-lane halves are exchanged,
+// then the 16-lane rows within each half.
+__device__ __forceinline__ float row4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Running-max start value: finite, so a chunk that sees no key keeps
 // exp2(m_old - m_new) == 1 and contributes exp2(-inf - m) == 0.
 constexpr float kNoMax = -1.0e30f;
