@@ -18,7 +18,6 @@ constexpr int kMaxK = 16;
 constexpr int kTileKeys = 64;           // keys per attention tile
 constexpr int kValuePage = 64;          // positions per value-cache page
 constexpr int kMaxChunkF32 = 1024;      // LDS score buffer of the f32 kernel
-constexpr int kVerifyChunk = 4096;      // logits per argmax workgroup
 constexpr int kCUs = 256;               // compute units of the part
 
 bool aligned(const void* p, uintptr_t a) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -144,7 +143,7 @@ int plan_verify(int B, int k, int V, VerifyPlan* p) {
   if (k > kMaxK) return TIDAR_EUNSUPPORTED;
   if (B < 0 || k < 1 || V < 1) return TIDAR_EINVAL;
   if ((long)B * (k + 1) > 65535) return TIDAR_EUNSUPPORTED;  // grid y limit
-  p->n_chunks = (int)cdiv(V, kVerifyChunk);
+  p->n_chunks = (int)cdiv(V, tidar::kArgmaxChunk);
   p->ar_bytes = round_up((size_t)B * (k + 1) * p->n_chunks * sizeof(float2), 256);
   p->draft_bytes = round_up((size_t)B * (k - 1) * p->n_chunks * sizeof(float2), 256);
   p->group_bytes = round_up((size_t)B * sizeof(int32_t), 256);
@@ -425,7 +424,7 @@ int tidar_verify_greedy(int B, int k, int V, const float* ar_logits, const float
   a.B = B;
   a.k = k;
   a.V = V;
-  a.chunk_elems = kVerifyChunk;
+  a.chunk_elems = tidar::kArgmaxChunk;
   a.n_chunks = p.n_chunks;
   const hipError_t e = tidar::launch_verify(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;

@@ -30,6 +30,46 @@ __device__ __forceinline__ float row4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// (value, index) argmax across lanes: the larger value wins and equal
+// values keep the lower index, so the result is the same in every lane
+// whatever the pairing order.  Within a 16-lane row the partners come from
+// DPP (quad swaps, half-row mirror, row mirror); across rows from the
+// row-swap instructions.
+__device__ __forceinline__ bool argmax_better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+__device__ __forceinline__ void argmax_take(float& v, int& i, float ov, int oi) {
+  if (argmax_better(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(float& v, int& i) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xF, 0xF, false);
+  argmax_take(v, i, ov, oi);
+}
+__device__ __forceinline__ void argmax_row16(float& v, int& i) {
+  argmax_dpp<0xB1>(v, i);   // quad_perm [1,0,3,2]
+  argmax_dpp<0x4E>(v, i);   // quad_perm [2,3,0,1]
+  argmax_dpp<0x141>(v, i);  // half-row mirror
+  argmax_dpp<0x140>(v, i);  // row mirror
+}
+__device__ __forceinline__ void argmax_wave(float& v, int& i) {
+  argmax_row16(v, i);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap((unsigned)i, (unsigned)i, false, false);
+  v = __uint_as_float(a[0]);
+  i = (int)b[0];
+  argmax_take(v, i, __uint_as_float(a[1]), (int)b[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const auto d = __builtin_amdgcn_permlane32_swap((unsigned)i, (unsigned)i, false, false);
+  v = __uint_as_float(c[0]);
+  i = (int)d[0];
+  argmax_take(v, i, __uint_as_float(c[1]), (int)d[1]);
+}
+
 // Running-max start value: finite, so a chunk that sees no key keeps
 // exp2(m_old - m_new) == 1 and contributes exp2(-inf - m) == 0.
 constexpr float kNoMax = -1.0e30f;

@@ -71,6 +71,7 @@ struct LmArgs {
 
 hipError_t launch_lmhead_argmax(const LmArgs& a, hipStream_t s);
 
+constexpr int kArgmaxChunk = 4096;  // logits per workgroup of the greedy argmax
 constexpr int kSampleChunk = 4096;  // vocabulary entries per workgroup of the sampling kernels
 
 struct SampleArgs {

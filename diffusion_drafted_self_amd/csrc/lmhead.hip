@@ -46,10 +46,6 @@ static_assert(STAGES == 3 && LD < 64, "vmcnt accounting below");
 
 __device__ __forceinline__ int swz(int row) { return row & 7; }
 
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
-}
-
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void lmhead_argmax_kernel(LmArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
@@ -153,15 +149,7 @@ void lmhead_argmax_kernel(LmArgs a) {
           bi = v;
         }
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o);
-        if (better(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
+      argmax_row16(bv, bi);
       if ((lane & 15) == 0) {
         sv[wave][16 * i + 4 * (lane >> 4) + r] = bv;
         si[wave][16 * i + 4 * (lane >> 4) + r] = bi;
@@ -173,7 +161,7 @@ void lmhead_argmax_kernel(LmArgs a) {
     float bv = sv[0][tid];
     int bi = si[0][tid];
     for (int w = 1; w < 4; ++w)
-      if (better(sv[w][tid], si[w][tid], bv, bi)) {
+      if (argmax_better(sv[w][tid], si[w][tid], bv, bi)) {
         bv = sv[w][tid];
         bi = si[w][tid];
       }

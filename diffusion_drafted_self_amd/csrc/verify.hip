@@ -8,7 +8,8 @@
 // The work is a streaming argmax over fp32 logit rows (HBM-bound):
 //   argmax_partial_kernel<false>  (chunk, AR row): 16 B loads, per-thread
 //       (value, index) with strict '>' (indices ascend inside a thread, so
-//       the lowest index wins ties), wave shuffles, then LDS across waves.
+//       the lowest index wins ties), a register-only wave reduction, then
+//       LDS across waves.
 //   verify_select_kernel   one workgroup per sequence, one wave per AR row:
 //       each wave reduces its row's chunk results, then the first mismatch
 //       is taken by a ballot: accept length, bonus token, draft group.
@@ -25,22 +26,6 @@
 namespace tidar {
 
 namespace {
-
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
-}
-
-__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(bv, o);
-    const int oi = __shfl_xor(bi, o);
-    if (better(ov, oi, bv, bi)) {
-      bv = ov;
-      bi = oi;
-    }
-  }
-}
 
 template <bool DRAFT>
 __global__ __launch_bounds__(256) void argmax_partial_kernel(VerifyArgs a) {
@@ -64,7 +49,41 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(VerifyArgs a) {
   const int hi = min(a.V, lo + a.chunk_elems);
   float bv = -INFINITY;
   int bi = INT_MAX;
-  if ((a.V & 3) == 0) {
+  auto take = [&](float x, int i) {
+    if (x > bv) {
+      bv = x;
+      bi = i;
+    }
+  };
+  if (a.chunk_elems == kArgmaxChunk) {
+    // every load of the thread first (their latencies overlap), then the
+    // compares in ascending index order (strict '>' keeps the lowest index)
+    if ((a.V & 3) == 0) {
+      float4 x[kArgmaxChunk / 1024];
+#pragma unroll
+      for (int j = 0; j < kArgmaxChunk / 1024; ++j) {
+        const int i = lo + 4 * (int)threadIdx.x + 1024 * j;
+        x[j] = i < hi ? *(const float4*)(src + i) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      }
+#pragma unroll
+      for (int j = 0; j < kArgmaxChunk / 1024; ++j) {
+        const int i = lo + 4 * (int)threadIdx.x + 1024 * j;
+        take(x[j].x, i);
+        take(x[j].y, i + 1);
+        take(x[j].z, i + 2);
+        take(x[j].w, i + 3);
+      }
+    } else {
+      float x[kArgmaxChunk / 256];
+#pragma unroll
+      for (int j = 0; j < kArgmaxChunk / 256; ++j) {
+        const int i = lo + (int)threadIdx.x + 256 * j;
+        x[j] = i < hi ? src[i] : -INFINITY;
+      }
+#pragma unroll
+      for (int j = 0; j < kArgmaxChunk / 256; ++j) take(x[j], lo + (int)threadIdx.x + 256 * j);
+    }
+  } else if ((a.V & 3) == 0) {
     for (int i = lo + 4 * (int)threadIdx.x; i < hi; i += 4 * 256) {
       const float4 x = *(const float4*)(src + i);
       if (x.x > bv) { bv = x.x; bi = i; }
@@ -78,7 +97,7 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(VerifyArgs a) {
       if (x > bv) { bv = x; bi = i; }
     }
   }
-  wave_argmax(bv, bi);
+  argmax_wave(bv, bi);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) {
     sv[wave] = bv;
@@ -87,7 +106,7 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(VerifyArgs a) {
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int w = 1; w < 4; ++w)
-      if (better(sv[w], si[w], bv, bi)) {
+      if (argmax_better(sv[w], si[w], bv, bi)) {
         bv = sv[w];
         bi = si[w];
       }
@@ -109,12 +128,12 @@ __device__ __forceinline__ int reduce_row(const float2* part, int n_chunks) {
   for (int c = lane; c < n_chunks; c += 64) {
     const float2 p = part[c];
     const int pi = __float_as_int(p.y);
-    if (better(p.x, pi, bv, bi)) {
+    if (argmax_better(p.x, pi, bv, bi)) {
       bv = p.x;
       bi = pi;
     }
   }
-  wave_argmax(bv, bi);
+  argmax_wave(bv, bi);
   return bi;
 }
 
@@ -123,6 +142,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void verify_select_kernel(VerifyArg
   __shared__ int t_row[kMaxRows];
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  // the candidates, requested before the row reductions so the two round
+  // trips overlap
+  const int cand = wave == 0 && lane < a.k ? a.cand[(size_t)b * a.k + lane] : 0;
   for (int row = wave; row <= a.k; row += nw) {
     const int t = reduce_row(a.part_ar + ((size_t)b * (a.k + 1) + row) * a.n_chunks, a.n_chunks);
     if (lane == 0) t_row[row] = t;
@@ -131,7 +153,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void verify_select_kernel(VerifyArg
   const int row = wave;
   if (row == 0) {
     // the accepted length is the first i < k with cand[i] != t_i (k if none)
-    const bool miss = lane < a.k && a.cand[(size_t)b * a.k + lane] != t_row[lane];
+    const bool miss = lane < a.k && cand != t_row[lane];
     const unsigned long long mm = __ballot(miss || lane == a.k);
     const int acc = __ffsll((long long)mm) - 1;
     if (lane == 0) {

@@ -86,22 +86,6 @@ __device__ __forceinline__ float gumbel2(unsigned x) {
   return -__builtin_amdgcn_logf(-__builtin_amdgcn_logf(to_uniform(x)));
 }
 
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
-}
-
-__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(bv, o);
-    const int oi = __shfl_xor(bi, o);
-    if (better(ov, oi, bv, bi)) {
-      bv = ov;
-      bi = oi;
-    }
-  }
-}
-
 // merge of (max, sum of exp2(z - max)) pairs; (-inf, 0) is the empty pair
 __device__ __forceinline__ void stats_merge(float& m, float& s, float m2, float s2) {
   const float mn = fmaxf(m, m2);
@@ -258,7 +242,7 @@ __device__ __forceinline__ void draw_chunk(const SampleArgs& a, const float* src
 
 // (score, lower index) maximum over the workgroup; every thread returns it
 __device__ __forceinline__ void block_argmax(float& bv, int& bi, float* sv, int* si) {
-  wave_argmax(bv, bi);
+  argmax_wave(bv, bi);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) {
     sv[wave] = bv;
@@ -266,7 +250,7 @@ __device__ __forceinline__ void block_argmax(float& bv, int& bi, float* sv, int*
   }
   __syncthreads();
   for (int w = 0; w < 4; ++w)
-    if (better(sv[w], si[w], bv, bi)) {
+    if (argmax_better(sv[w], si[w], bv, bi)) {
       bv = sv[w];
       bi = si[w];
     }
@@ -304,12 +288,12 @@ __device__ __forceinline__ int reduce_draw(const float2* part, int n_chunks) {
   for (int c = threadIdx.x & 63; c < n_chunks; c += 64) {
     const float2 p = part[c];
     const int pi = __float_as_int(p.y);
-    if (better(p.x, pi, bv, bi)) {
+    if (argmax_better(p.x, pi, bv, bi)) {
       bv = p.x;
       bi = pi;
     }
   }
-  wave_argmax(bv, bi);
+  argmax_wave(bv, bi);
   return bi;
 }
 
