@@ -58,6 +58,9 @@ def _compare(d, a, n, seqs, what):
     (5, 1, 1000, 64, "uniform"),       # no drafts
     (150, 3, 257, 128, "uniform"),     # 600 AR rows: five row groups; a one-entry last chunk
     (3, 16, 4096, 512, "geometric"),   # k = 16
+    (18, 3, 3001, 128, "uniform"),     # 72 AR rows: five row tiles per workgroup
+    (22, 3, 2049, 64, "uniform"),      # 88 AR rows: six row tiles
+    (30, 3, 1024, 192, "geometric"),   # 120 AR rows: eight row tiles
 ])
 def test_lmhead_verify_matches_oracle(B, k, V, d, accept):
     print(f"lmhead B={B} k={k} V={V} d={d}", flush=True)
