@@ -639,8 +639,8 @@ __device__ __forceinline__ void pv_tile(const lds_char* sV, const Probs<NF, NS>&
 // passes one barrier (after which every wave is done with iteration t-1, so
 // slots K(t-1) and V(t-2) are free), requests K(t+3) and V(t+2), then runs
 // softmax(t) | scores(t+1) | P.V(t-1).  Tiles that reach past the settled
-// prefix are staged through registers into the last slots first, before
-// the ring fills them.
+// prefix are staged through registers into the last slot first; the ring's
+// prologue is requested once the last of them has landed.
 //
 // TRAIN: the duplicated training sequence (rows and keys are the T = 2N
 // positions of one sequence, keys in the cache layouts with S_max = T).  A
@@ -836,8 +836,9 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
   Probs<NF, NS> pA, pB;
 
   // Masked tiles (decode: tiles reaching past the prefix): staged through
-  // registers into the last slots (free until the loop's first requests),
-  // masked by zone, softmax with the exact path.
+  // registers into the last slot (not used by the ring before its first
+  // in-loop request), masked by zone, softmax against the held references
+  // (the exact path when they overflow, so always for the first tile).
   const int zoff = TRAIN ? 0 : L;  // zone tests take step-row indices (decode) or positions (training)
   auto zone = [&](int m) { return TRAIN ? train_zone(m / a.G, a.train_N, a.train_bs) : step_zone(m / a.G, a.k); };
   const int nA = (mA1 - mA0 + TK - 1) / TK, nB = (mB1 - mB0 + TK - 1) / TK;  // a range may end mid-tile
