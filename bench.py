@@ -36,6 +36,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -75,10 +76,18 @@ def parse():
     return p.parse_args()
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and whitespace: a counter summary stays
+    valid across edits that do not touch the code."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return "".join(text.split())
+
+
 def attention_source_sha() -> str:
     h = hashlib.sha256()
     for f in ATTN_SOURCES:
-        h.update(open(f, "rb").read())
+        h.update(_code_only(open(f, encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 
