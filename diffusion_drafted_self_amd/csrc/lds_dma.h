@@ -35,15 +35,21 @@ __device__ __forceinline__ void barrier() {
 // per-lane offset, so the compiler neither rebuilds 64-bit addresses every
 // tile nor treats the load as an LDS store it must order against unrelated
 // LDS reads (its LDS-DMA alias tracking would serialise the pipeline); the
-// kernel orders these loads itself with s_waitcnt vmcnt and barriers.  No
-// output registers are involved.
+// kernel orders these loads itself with s_waitcnt vmcnt and barriers.  The
+// load takes its LDS address from m0, which the block sets and then restores
+// (the load reads m0 when it issues, not when its data arrives), so whatever
+// the compiler keeps in m0 survives; no vector register is written.
 __device__ __forceinline__ void dma_b128(const char* base, unsigned off, lds_char* lds_dst) {
   const unsigned long long b = (unsigned long long)base;
   const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)b);
   const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
   const unsigned long long sb = ((unsigned long long)hi << 32) | lo;
-  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_dst);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(sb), "s"(m0) : "memory", "m0");
+  const unsigned dst = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_dst);
+  unsigned saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(off), "s"(sb), "s"(dst)
+               : "memory");
 }
 
 }  // namespace tidar
