@@ -52,6 +52,7 @@ SIGNATURES = {
     "tidar_train_attention": (_c_int, [_c_int] * 7 + [_f] + [_p] * 6),
     "tidar_lmhead_verify_workspace": (_c_int, [_c_int] * 4 + [ctypes.POINTER(_c_size)]),
     "tidar_lmhead_verify_greedy": (_c_int, [_c_int] * 4 + [_p] * 7 + [_c_size, _p]),
+    "tidar_read_probe": (_c_int, [_p, _c_size, _p, _p]),
 }
 
 
@@ -456,7 +457,28 @@ def kv_commit_paged(k_pool, v_pool, block_table, lens, k_step, v_step, accept_le
     return err_flags
 
 
+READ_PROBE_BLOCKS = 16384  # TIDAR_READ_PROBE_BLOCKS
+
+
+def read_probe(buf, sink=None):
+    """Read every byte of the contiguous device tensor ``buf`` once (the
+    library's streaming-read helper, for achievable-bandwidth figures).
+    Returns the int32 ``sink`` of READ_PROBE_BLOCKS words, whose XOR is the
+    XOR of all 32-bit words of ``buf``."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty(READ_PROBE_BLOCKS, dtype=torch.int32, device=buf.device)
+    _need(sink, "sink", torch.int32, 1, buf.device)
+    if sink.numel() < READ_PROBE_BLOCKS:
+        raise ValueError(f"sink must hold {READ_PROBE_BLOCKS} words")
+    _check("tidar_read_probe", lib().tidar_read_probe(_ptr(buf), nbytes, _ptr(sink), _stream()))
+    return sink
+
+
 __all__ = ["step_attention", "step_attention_workspace_bytes", "verify_greedy", "verify_workspace_bytes",
            "verify_sample", "verify_sample_workspace_bytes", "kv_commit",
            "step_attention_paged", "kv_commit_paged", "train_attention",
-           "lmhead_verify_greedy", "lmhead_verify_workspace_bytes", "strerror", "lib", "TidarError", "LIB_PATH", "SIGNATURES"]
+           "lmhead_verify_greedy", "lmhead_verify_workspace_bytes", "strerror", "lib", "TidarError", "LIB_PATH", "SIGNATURES",
+           "read_probe", "READ_PROBE_BLOCKS"]

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtidar.so")
-SOURCES = ["attention.hip", "verify.hip", "verify_sample.hip", "lmhead.hip", "commit.hip", "capi.cpp"]
+SOURCES = ["attention.hip", "verify.hip", "verify_sample.hip", "lmhead.hip", "commit.hip", "read_probe.hip", "capi.cpp"]
 ARCH = "gfx950"
 
 

@@ -560,4 +560,13 @@ int tidar_kv_commit_paged(int dtype, int B, int Hkv, int D, int max_pages, int n
                         n_pages, lens, k_step, v_step, accept_len, err_flags, stream);
 }
 
+static_assert(TIDAR_READ_PROBE_BLOCKS == tidar::kReadProbeBlocks, "read probe sink size");
+
+int tidar_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!aligned(src, 16) || !aligned(sink, 4) || bytes % 16 != 0) return TIDAR_EINVAL;
+  if (bytes == 0) return TIDAR_OK;
+  const hipError_t e = tidar::launch_read_probe(src, bytes, sink, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
+}
+
 }  // extern "C"

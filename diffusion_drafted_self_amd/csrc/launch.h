@@ -70,7 +70,9 @@ struct LmArgs {
 };
 
 hipError_t launch_lmhead_argmax(const LmArgs& a, hipStream_t s);
+hipError_t launch_read_probe(const void* src, size_t bytes, unsigned* sink, hipStream_t s);
 
+constexpr int kReadProbeBlocks = 16384;  // workgroups of the streaming-read probe
 constexpr int kArgmaxChunk = 4096;  // logits per workgroup of the greedy argmax
 constexpr int kSampleChunk = 4096;  // vocabulary entries per workgroup of the sampling kernels
 

@@ -39,6 +39,9 @@ __device__ __forceinline__ void barrier() {
 // load takes its LDS address from m0, which the block sets and then restores
 // (the load reads m0 when it issues, not when its data arrives), so whatever
 // the compiler keeps in m0 survives; no vector register is written.
+// NT: the nontemporal form, for data read once (a streaming hint to the
+// caches; measured on plain streaming reads to raise the delivered rate).
+template <bool NT = false>
 __device__ __forceinline__ void dma_b128(const char* base, unsigned off, lds_char* lds_dst) {
   const unsigned long long b = (unsigned long long)base;
   const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)b);
@@ -46,10 +49,16 @@ __device__ __forceinline__ void dma_b128(const char* base, unsigned off, lds_cha
   const unsigned long long sb = ((unsigned long long)hi << 32) | lo;
   const unsigned dst = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_dst);
   unsigned saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved)
-               : "v"(off), "s"(sb), "s"(dst)
-               : "memory");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2 nt\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(off), "s"(sb), "s"(dst)
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(off), "s"(sb), "s"(dst)
+                 : "memory");
 }
 
 }  // namespace tidar

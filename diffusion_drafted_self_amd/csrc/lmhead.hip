@@ -95,7 +95,9 @@ void lmhead_argmax_kernel(LmArgs a) {
   auto issue_one = [&](int st, int q) {
     lds_char* slot = ring + (st % STAGES) * STAGE_BYTES;
     const unsigned dk = (unsigned)st * ROWB;
-    dma_b128(q < W_LD ? (const char*)a.w : (const char*)a.h, off[q] + dk, slot + dst[q]);
+    // W is read once per pass (nontemporal); the hidden rows again for every slice
+    if (q < W_LD) dma_b128<true>((const char*)a.w, off[q] + dk, slot + dst[q]);
+    else dma_b128<false>((const char*)a.h, off[q] + dk, slot + dst[q]);
   };
 
   const int nst = a.d / LK;

@@ -56,14 +56,16 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(VerifyArgs a) {
     }
   };
   if (a.chunk_elems == kArgmaxChunk) {
-    // every load of the thread first (their latencies overlap), then the
-    // compares in ascending index order (strict '>' keeps the lowest index)
+    // every load of the thread first (their latencies overlap; nontemporal:
+    // each logit is read once), then the compares in ascending index order
+    // (strict '>' keeps the lowest index)
     if ((a.V & 3) == 0) {
-      float4 x[kArgmaxChunk / 1024];
+      floatx4 x[kArgmaxChunk / 1024];
 #pragma unroll
       for (int j = 0; j < kArgmaxChunk / 1024; ++j) {
         const int i = lo + 4 * (int)threadIdx.x + 1024 * j;
-        x[j] = i < hi ? *(const float4*)(src + i) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        x[j] = i < hi ? __builtin_nontemporal_load((const floatx4*)(src + i))
+                      : (floatx4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       }
 #pragma unroll
       for (int j = 0; j < kArgmaxChunk / 1024; ++j) {
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(VerifyArgs a) {
 #pragma unroll
       for (int j = 0; j < kArgmaxChunk / 256; ++j) {
         const int i = lo + (int)threadIdx.x + 256 * j;
-        x[j] = i < hi ? src[i] : -INFINITY;
+        x[j] = i < hi ? __builtin_nontemporal_load(src + i) : -INFINITY;
       }
 #pragma unroll
       for (int j = 0; j < kArgmaxChunk / 256; ++j) take(x[j], lo + (int)threadIdx.x + 256 * j);

@@ -342,6 +342,27 @@ int tidar_kv_commit_paged(int dtype, int B, int Hkv, int D, int max_pages, int n
                           const void* k_step, const void* v_step, const int32_t* accept_len,
                           int32_t* err_flags, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Measurement helper (not part of the decode step).
+ *
+ * tidar_read_probe reads `bytes` of device memory at `src` once, in 16 B
+ * loads spread over TIDAR_READ_PROBE_BLOCKS workgroups, and writes one 32-bit
+ * word per workgroup to `sink`: the XOR of every 32-bit word that workgroup
+ * read.  The XOR of all sink words therefore equals the XOR of all 32-bit
+ * words of the buffer, which a host can check.  Timed over a buffer much
+ * larger than the GPU's caches, it gives the read bandwidth the memory
+ * delivers to a plain streaming kernel: the denominator for reporting a
+ * kernel's bandwidth against what is achievable, beside the data-sheet peak.
+ *
+ *   src    device pointer, 16-byte aligned; bytes a multiple of 16.
+ *   sink   device pointer to TIDAR_READ_PROBE_BLOCKS uint32 (4-byte aligned).
+ *   Returns TIDAR_EINVAL for a null or misaligned pointer or a size not a
+ *   multiple of 16; bytes == 0 enqueues nothing.
+ * ------------------------------------------------------------------------- */
+#define TIDAR_READ_PROBE_BLOCKS 16384
+
+int tidar_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -202,3 +202,16 @@ def test_lmhead_validation_and_size(T):
     assert f(2, 4, 1000, 64, p, p, p, p, p, p, p, 8, None) == -3
     assert f(2, 4, 1000, 64, p, None, p, p, p, p, p, 1 << 20, None) == -1
     assert f(0, 4, 1000, 64, None, None, None, None, None, None, None, 0, None) == 0
+
+
+def test_read_probe_validation(T):
+    f = T.lib().tidar_read_probe
+    buf = (ctypes.c_uint8 * 64)()
+    base = ctypes.addressof(buf)
+    a16 = base + (-base) % 16  # a 16-byte aligned host address inside buf (never dereferenced)
+    sink = (ctypes.c_uint32 * 4)()
+    assert f(None, 16, sink, None) == -1
+    assert f(a16, 16, None, None) == -1
+    assert f(a16 + 4, 16, sink, None) == -1   # misaligned source
+    assert f(a16, 24, sink, None) == -1       # not a multiple of 16
+    assert f(a16, 0, sink, None) == 0         # nothing to read: nothing enqueued

@@ -1,0 +1,22 @@
+"""GPU check of the streaming-read helper used for achievable-bandwidth
+figures: the XOR of its per-workgroup words equals the XOR of every 32-bit
+word of the buffer (so every byte was read, once)."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+tidar = pytest.importorskip("diffusion_drafted_self_amd")
+import torch  # noqa: E402
+
+
+# the third size is the smallest that runs the eight-load loop (8 strides of 16384 x 256 pieces) plus a tail
+@pytest.mark.parametrize("n_words", [4, 12, 16384 * 256 * 4 * 8 + 12, 3 * (1 << 20) + 4])
+def test_read_probe_folds_every_word(n_words):
+    print(f"read probe: {n_words} words", flush=True)
+    g = np.random.default_rng(n_words)
+    host = g.integers(0, 2**32, size=n_words, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).cuda()
+    sink = tidar.read_probe(buf)
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(host)
