@@ -100,16 +100,20 @@ __device__ __forceinline__ void wave_stats(float& m, float& s) {
 }
 
 // entries v .. v+3 of a row; -inf past hi
+// NT: nontemporal, for rows read once.  The statistics kernel reads every
+// AR and proposal row once; the draw kernel reads the draft rows once, but
+// the accepted position's AR and proposal rows (the residual) a second time.
+template <bool NT>
 __device__ __forceinline__ void load_row4(const float* src, int v, int hi, bool vec, float x[4]) {
   if (vec && v < hi) {
-    const float4 f = *(const float4*)(src + v);
-    x[0] = f.x;
-    x[1] = f.y;
-    x[2] = f.z;
-    x[3] = f.w;
+    const floatx4 f = NT ? __builtin_nontemporal_load((const floatx4*)(src + v)) : *(const floatx4*)(src + v);
+    x[0] = f[0];
+    x[1] = f[1];
+    x[2] = f[2];
+    x[3] = f[3];
   } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = v + e < hi ? src[v + e] : -INFINITY;
+    for (int e = 0; e < 4; ++e) x[e] = v + e < hi ? (NT ? __builtin_nontemporal_load(src + v + e) : src[v + e]) : -INFINITY;
   }
 }
 
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(256) void sample_stats_kernel(SampleArgs a) {
   const bool vec = (a.V & 3) == 0;
   float x[kPerThread];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) load_row4(src, lo + 4 * (int)threadIdx.x + 1024 * r, hi, vec, x + 4 * r);
+  for (int r = 0; r < 4; ++r) load_row4<true>(src, lo + 4 * (int)threadIdx.x + 1024 * r, hi, vec, x + 4 * r);
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
@@ -209,8 +213,8 @@ __device__ __forceinline__ void draw_chunk(const SampleArgs& a, const float* src
     const int v = lo + 4 * (int)threadIdx.x + 1024 * r;
     if (v >= hi) break;
     float x[4], y[4];
-    load_row4(src, v, hi, vec, x);
-    if (MODE) load_row4(qsrc, v, hi, vec, y);
+    load_row4<!MODE>(src, v, hi, vec, x);
+    if (MODE) load_row4<false>(qsrc, v, hi, vec, y);
     const U4 rnd = philox4x32_10(U4{(unsigned)(v >> 2), (unsigned)j, (unsigned)b, a.step}, a.key0, a.key1);
     const unsigned w4[4] = {rnd.x, rnd.y, rnd.z, rnd.w};
 #pragma unroll
