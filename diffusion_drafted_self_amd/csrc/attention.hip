@@ -903,8 +903,9 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
   }
 
   if (n > 0) {
-    // Tile 0 is scored and its softmax taken with the exact path, so every
-    // row's reference is a true max of fully visible keys before the
+    // Tile 0 is scored against the held references, with the exact path
+    // when they are unset (no masked tile in this chunk) or overflow, so
+    // every row has a reference from an attained score before the
     // pipelined loop.  Inside the loop a reference is never moved: a tile
     // whose sum of p passes 2^64 (scores 64 above the reference, in log2
     // units) raises the workgroup's overflow flag, and the chunk is then
