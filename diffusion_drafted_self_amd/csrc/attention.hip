@@ -852,7 +852,9 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
     wait_all();
     barrier();
   };
-  auto tail_compute = [&](int i) {
+  // fresh: no reference is set yet (the kernel's first masked tile), so the
+  // held-reference attempt, which would overflow, is skipped
+  auto tail_compute = [&](int i, bool fresh) {
     const int t0 = tail_t0(i);
     lds_char* sK = kslot(RING - 1);
     lds_char* sV = vslot(RING - 1);
@@ -881,7 +883,10 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
         sA.ss[s2][v] = vis ? sA.ss[s2][v] : -INFINITY;
       }
     }
-    const bool big = sm_tile<D, NF, NS>(sA, pA, ac, sl2);
+    // (the instances nearest the register limit always make the attempt)
+    constexpr bool kSkipFresh = !(D == 128 && NF + NS >= 4);
+    bool big = true;
+    if (!(kSkipFresh && fresh)) big = sm_tile<D, NF, NS>(sA, pA, ac, sl2);
     softmax_commit<D, NF, NS>(big, sA, pA, ac, sl2);
     pv_tile<D, NF, NS>(sV, pA, ac, lane, wave);
     wait_lgkmcnt0();
@@ -892,12 +897,12 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
   // that tile's).
   for (int i = 0; i + 1 < nA + nB; ++i) {
     tail_stage(i);
-    tail_compute(i);
+    tail_compute(i, i == 0);
   }
   if (nA + nB > 0) {
     tail_stage(nA + nB - 1);
     ring_prologue();
-    tail_compute(nA + nB - 1);
+    tail_compute(nA + nB - 1, nA + nB == 1);
   } else {
     ring_prologue();
   }
@@ -998,7 +1003,7 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
       }
       for (int i = 0; i < nA + nB; ++i) {
         tail_stage(i);
-        tail_compute(i);
+        tail_compute(i, false);
       }
     }
   }
