@@ -176,7 +176,15 @@ __device__ __forceinline__ void issue_v(lds_char* sV, const bf16* vtile, const D
   for (int ii = 0; ii < T::NVW; ++ii) dma_b128(vt, pl.v[ii], sV + (wave * T::NVW + ii) * 1024);
 }
 
-// Stage a tile one 16 B piece at a time (see stage_tail_tile).
+// Stage a tile that reaches past the settled prefix (the step block, or
+// keys past the end) into the same swizzled layout.  Settled keys come from
+// the tile's cache rows `kt` / value page `vt` (null when the tile holds no
+// settled position) in 16 B pieces, one at a time; step rows are read 16 B at a time and
+// their values scattered into V^T columns; everything else is zero.
+//
+// Kernels whose registers are not near the limit use the two-part form
+// below instead (stage_issue / stage_commit), so a tile's loads can be in
+// flight while the tile before it computes.
 template <int D>
 __device__ __forceinline__ void stage_tail_tile_lean(lds_char* sK, lds_char* sV, const bf16* kt, const bf16* vt,
                                                      const bf16* ks_base, const bf16* vs_base, size_t step_stride,
@@ -218,59 +226,62 @@ __device__ __forceinline__ void stage_tail_tile_lean(lds_char* sK, lds_char* sV,
   }
 }
 
-// Stage a tile that reaches past the settled prefix (the step block, or
-// keys past the end) into the same swizzled layout.  Settled keys come from
-// the tile's cache rows `kt` / value page `vt` (null when the tile holds no
-// settled position) in 16 B pieces; step rows are read 16 B at a time and
-// their values scattered into V^T columns; everything else is zero.
-//
-// BATCH: the loads of a piece kind are issued together (their latencies
-// overlap); without it, one piece at a time (kernels whose registers are
-// already near the limit).
-template <int D, bool BATCH>
-__device__ __forceinline__ void stage_tail_tile(lds_char* sK, lds_char* sV, const bf16* kt, const bf16* vt,
-                                                const bf16* ks_base, const bf16* vs_base, size_t step_stride,
-                                                int t0, int L, int Ltot, int tid) {
-  using T = Tile<D>;
-  if constexpr (!BATCH) {
-    stage_tail_tile_lean<D>(sK, sV, kt, vt, ks_base, vs_base, step_stride, t0, L, Ltot, tid);
-    return;
-  }
-  constexpr int NT = NWV * 64;
-  constexpr int NK = TK * T::KPPR / NT;   // K pieces per thread
-  constexpr int NVS = D * 8 / NT;         // V^T pieces (8 positions) per thread
-  constexpr int NVR = TK * (D / 8) / NT;  // step-row value pieces per thread
-  static_assert(NK * NT == TK * T::KPPR && NVS * NT == D * 8 && NVR * NT == TK * (D / 8), "staging split");
-  const int j0 = max(t0, L), j1 = min(t0 + TK, Ltot);
-  // two batches of loads, each issued whole so their latencies overlap:
-  // K and the step rows' values (every masked tile has step rows or keys
-  // past the end), then the settled part of V^T (only a prefix that is not
-  // a multiple of the tile has one inside a masked tile)
+template <int D>
+struct StagedRows {  // a masked tile's K pieces and step-row values, in flight
+  static constexpr int NT = NWV * 64;
+  static constexpr int NK = TK * Tile<D>::KPPR / NT;  // K pieces per thread
+  static constexpr int NVS = D * 8 / NT;              // V^T pieces (8 positions) per thread
+  static constexpr int NVR = TK * (D / 8) / NT;       // step-row value pieces per thread
+  static_assert(NK * NT == TK * Tile<D>::KPPR && NVS * NT == D * 8 && NVR * NT == TK * (D / 8), "staging split");
   bf16x8 kp[NK], vr[NVR];
+};
+
+// The loads of a masked tile's K pieces and step rows' values, all issued at
+// once (their latencies overlap); every masked tile has step rows or keys
+// past the end.
+template <int D>
+__device__ __forceinline__ void stage_issue(StagedRows<D>& st, const bf16* kt, const bf16* ks_base,
+                                            const bf16* vs_base, size_t step_stride, int t0, int L, int Ltot,
+                                            int tid) {
+  using S = StagedRows<D>;
+  using T = Tile<D>;
+  const int j0 = max(t0, L), j1 = min(t0 + TK, Ltot);
 #pragma unroll
-  for (int i = 0; i < NK; ++i) {
-    const int id = tid + i * NT, row = id / T::KPPR, p = id % T::KPPR;
+  for (int i = 0; i < S::NK; ++i) {
+    const int id = tid + i * S::NT, row = id / T::KPPR, p = id % T::KPPR;
     const int c = t0 + row;
-    kp[i] = (bf16x8){};
-    if (c < L) kp[i] = *(const bf16x8*)(kt + (size_t)row * D + p * 8);
-    else if (c < Ltot) kp[i] = *(const bf16x8*)(ks_base + (size_t)(c - L) * step_stride + p * 8);
+    st.kp[i] = (bf16x8){};
+    if (c < L) st.kp[i] = *(const bf16x8*)(kt + (size_t)row * D + p * 8);
+    else if (c < Ltot) st.kp[i] = *(const bf16x8*)(ks_base + (size_t)(c - L) * step_stride + p * 8);
   }
 #pragma unroll
-  for (int i = 0; i < NVR; ++i) {  // step rows: 8 head-dim elements of one key
-    const int id = tid + i * NT, cl = id % TK, dc = id / TK;
+  for (int i = 0; i < S::NVR; ++i) {  // step rows: 8 head-dim elements of one key
+    const int id = tid + i * S::NT, cl = id % TK, dc = id / TK;
     const int c = t0 + cl;
-    vr[i] = (bf16x8){};
-    if (c >= j0 && c < j1) vr[i] = *(const bf16x8*)(vs_base + (size_t)(c - L) * step_stride + dc * 8);
+    st.vr[i] = (bf16x8){};
+    if (c >= j0 && c < j1) st.vr[i] = *(const bf16x8*)(vs_base + (size_t)(c - L) * step_stride + dc * 8);
   }
+}
+
+// The rest of staging a masked tile whose loads stage_issue made: the K
+// pieces into their rows, the settled part of V^T (a second batch of loads,
+// present only when the prefix is not a multiple of the tile), then the
+// step rows' values scattered into V^T columns.
+template <int D>
+__device__ __forceinline__ void stage_commit(const StagedRows<D>& st, lds_char* sK, lds_char* sV, const bf16* vt,
+                                             int t0, int L, int Ltot, int tid) {
+  using S = StagedRows<D>;
+  using T = Tile<D>;
+  const int j0 = max(t0, L), j1 = min(t0 + TK, Ltot);
 #pragma unroll
-  for (int i = 0; i < NK; ++i) {
-    const int id = tid + i * NT, row = id / T::KPPR, p = id % T::KPPR;
-    *(lds_bf16x8*)(sK + row * T::KROW + ((p ^ kswz<D>(row)) * 16)) = kp[i];
+  for (int i = 0; i < S::NK; ++i) {
+    const int id = tid + i * S::NT, row = id / T::KPPR, p = id % T::KPPR;
+    *(lds_bf16x8*)(sK + row * T::KROW + ((p ^ kswz<D>(row)) * 16)) = st.kp[i];
   }
-  bf16x8 vp[NVS];
+  bf16x8 vp[S::NVS];
 #pragma unroll
-  for (int i = 0; i < NVS; ++i) {  // settled part of V^T, zero elsewhere
-    const int id = tid + i * NT, d = id >> 3, q = id & 7;
+  for (int i = 0; i < S::NVS; ++i) {  // settled part of V^T, zero elsewhere
+    const int id = tid + i * S::NT, d = id >> 3, q = id & 7;
     const int c0 = t0 + q * 8;
     vp[i] = (bf16x8){};
     if (c0 + 8 <= L) {
@@ -281,8 +292,8 @@ __device__ __forceinline__ void stage_tail_tile(lds_char* sK, lds_char* sV, cons
     }
   }
 #pragma unroll
-  for (int i = 0; i < NVS; ++i) {
-    const int id = tid + i * NT, d = id >> 3, q = id & 7;
+  for (int i = 0; i < S::NVS; ++i) {
+    const int id = tid + i * S::NT, d = id >> 3, q = id & 7;
     *(lds_bf16x8*)(sV + d * T::VROW + ((q ^ vswz(d)) * 16)) = vp[i];
   }
   wait_all();
@@ -291,14 +302,14 @@ __device__ __forceinline__ void stage_tail_tile(lds_char* sK, lds_char* sV, cons
   // consecutive keys, so each 2-byte store of a wave fills one V^T row
   // across 64 columns (lanes on the same column would all hit one bank).
 #pragma unroll
-  for (int i = 0; i < NVR; ++i) {
-    const int id = tid + i * NT, cl = id % TK, dc = id / TK;
+  for (int i = 0; i < S::NVR; ++i) {
+    const int id = tid + i * S::NT, cl = id % TK, dc = id / TK;
     const int c = t0 + cl;
     if (c < j0 || c >= j1) continue;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int d = dc * 8 + e;
-      *(__attribute__((address_space(3))) bf16*)(sV + d * T::VROW + ((((cl >> 3) ^ vswz(d)) * 16)) + (cl & 7) * 2) = vr[i][e];
+      *(__attribute__((address_space(3))) bf16*)(sV + d * T::VROW + ((((cl >> 3) ^ vswz(d)) * 16)) + (cl & 7) * 2) = st.vr[i][e];
     }
   }
 }
@@ -843,12 +854,26 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
   auto zone = [&](int m) { return TRAIN ? train_zone(m / a.G, a.train_N, a.train_bs) : step_zone(m / a.G, a.k); };
   const int nA = (mA1 - mA0 + TK - 1) / TK, nB = (mB1 - mB0 + TK - 1) / TK;  // a range may end mid-tile
   auto tail_t0 = [&](int i) { return i < nA ? mA0 + i * TK : mB0 + (i - nA) * TK; };
-  auto tail_stage = [&](int i) {
+  // the two instances nearest the register limit stage one piece at a time
+  constexpr bool kBatch = !(D == 128 && NF + NS >= 4);
+  StagedRows<D> staged;
+  auto tail_issue = [&](int i) {  // batched: masked tile i's loads, into registers
+    if constexpr (kBatch) {
+      const int t0 = tail_t0(i);
+      const bool settled = t0 < L;  // the tile holds settled positions (its page is in the table)
+      stage_issue<D>(staged, settled ? kv.ktile(t0 / TK) : nullptr, ks_base, vs_base, step_stride, t0, L, Ltot, tid);
+    }
+  };
+  auto tail_stage = [&](int i) {  // masked tile i into the last slot
     const int t0 = tail_t0(i);
     barrier();
-    const bool settled = t0 < L;  // the tile holds settled positions (its page is in the table)
-    stage_tail_tile<D, !(D == 128 && NF + NS >= 4)>(kslot(RING - 1), vslot(RING - 1), settled ? kv.ktile(t0 / TK) : nullptr,
-                       settled ? kv.vtile(t0 / TK) : nullptr, ks_base, vs_base, step_stride, t0, L, Ltot, tid);
+    const bool settled = t0 < L;
+    if constexpr (kBatch)
+      stage_commit<D>(staged, kslot(RING - 1), vslot(RING - 1), settled ? kv.vtile(t0 / TK) : nullptr, t0, L, Ltot,
+                      tid);
+    else
+      stage_tail_tile_lean<D>(kslot(RING - 1), vslot(RING - 1), settled ? kv.ktile(t0 / TK) : nullptr,
+                              settled ? kv.vtile(t0 / TK) : nullptr, ks_base, vs_base, step_stride, t0, L, Ltot, tid);
     wait_all();
     barrier();
   };
@@ -895,8 +920,10 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
   // a load issued after it would wait for it (loads complete in order).
   // It then lands while that tile computes (its slots 0..RING-2 are not
   // that tile's).
+  if (nA + nB > 0) tail_issue(0);
   for (int i = 0; i + 1 < nA + nB; ++i) {
     tail_stage(i);
+    tail_issue(i + 1);  // in flight while tile i computes
     tail_compute(i, i == 0);
   }
   if (nA + nB > 0) {
@@ -1002,6 +1029,7 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
         wait_lgkmcnt0();
       }
       for (int i = 0; i < nA + nB; ++i) {
+        tail_issue(i);
         tail_stage(i);
         tail_compute(i, false);
       }
