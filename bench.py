@@ -176,7 +176,9 @@ def summarize(dirname):
         name = r["Name"].replace("(anonymous namespace)::", "").replace("tidar::", "")
         lines.append(f"| `{name[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
-    lines += ["", "`copyBuffer` is the 64-byte restore of the settled lengths after each timed step (harness). "
+    lines += ["", "Each step kernel runs once per eager step (warm-up and timed), once more per input "
+              "replica as the warm-up before its graph capture, and once per graph replay (warm-up and timed). "
+              "`copyBuffer` is the 64-byte restore of the settled lengths after each timed step (harness). "
               "`read_probe_kernel` is the achievable-bandwidth measurement after the timed steps "
               "(a streaming read of 4 GiB, six calls).", ""]
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
