@@ -22,7 +22,9 @@ Prints ONE JSON line.  Options:
                     tidar_kv_commit_paged) instead of per-sequence caches
   --verify lmhead   the LM head fused with greedy verification: hidden states
                     and a random-init head of the workload's model size in,
-                    no logits stored (tidar_lmhead_verify_greedy)
+                    no logits stored (tidar_lmhead_verify_greedy_packed on
+                    the head packed before timing; --lm-layout rowmajor for
+                    tidar_lmhead_verify_greedy on the [V][d] head)
   --verify sample   stochastic verification (temperature --temperature, Philox
                     stream of --seed and the step number) in place of greedy;
                     inputs from the sampling generator, accept lengths as drawn
@@ -66,6 +68,8 @@ def parse():
     p.add_argument("--kv-chunk", type=int, default=0, help="key positions per attention chunk (0: library plan)")
     p.add_argument("--summarize", metavar="DIR", help="write profiles/ summaries from rocprofv3 outputs in DIR")
     p.add_argument("--verify", default="greedy", choices=["greedy", "sample", "lmhead"])
+    p.add_argument("--lm-layout", default="packed", choices=["packed", "rowmajor"],
+                   help="layout of W for --verify lmhead (packed once, before timing, as at weight load)")
     p.add_argument("--temperature", type=float, default=1.0)
     p.add_argument("--paged", action="store_true")
     p.add_argument("--workload", default="step_8b",
@@ -461,9 +465,12 @@ def main():
     else:
         ws_v = (tidar.verify_sample_workspace_bytes if args.verify == "sample" else tidar.verify_workspace_bytes)(
             s.B, s.k, wl.V)
+    packed_w = args.verify == "lmhead" and args.lm_layout == "packed"
     reps = []
     for _ in range(n_rep):
-        r = {n: t.clone() for n, t in base.items()}
+        r = {n: t.clone() for n, t in base.items() if not (packed_w and n == "w")}
+        if packed_w:  # the head is packed once, when weights are loaded
+            r["wp"] = tidar.lmhead_pack(base["w"])
         r["lens0"] = base["lens"].clone()
         r["out"] = torch.empty_like(base["q"])
         r["lse"] = torch.empty((s.B, s.Hq, s.R), dtype=torch.float32, device=dev)
@@ -487,7 +494,10 @@ def main():
                              workspace=r["ws_a"], kv_chunk=args.kv_chunk)
 
     def verify(r, step_no):
-        if args.verify == "lmhead":
+        if packed_w:
+            tidar.lmhead_verify_greedy_packed(r["h_ar"], r["h_draft"], r["wp"], wl.V, r["cand"], accept_len=r["acc"],
+                                              next_cand=r["next"], workspace=r["ws_v"])
+        elif args.verify == "lmhead":
             tidar.lmhead_verify_greedy(r["h_ar"], r["h_draft"], r["w"], r["cand"], accept_len=r["acc"],
                                        next_cand=r["next"], workspace=r["ws_v"])
         elif args.verify == "sample":
@@ -639,9 +649,12 @@ def main():
         lm_ms = sum(ev_a[i][1].elapsed_time(ev_v[i]) for i in range(K)) / K
         lm_gbps = ver_b / (lm_ms * 1e-3) / 1e9
         result["config"]["d_model"] = wl.d_model
+        result["config"]["w_layout"] = args.lm_layout
         result["lmhead_verify_us"] = round(lm_ms * 1e3, 2)
         result["attention_roofline"] = result["roofline"]
-        result["roofline"] = {"bound": "hbm", "kernel": "tidar_lmhead_verify_greedy", "achieved": round(lm_gbps, 2),
+        result["roofline"] = {"bound": "hbm",
+                              "kernel": "tidar_lmhead_verify_greedy" + ("_packed" if packed_w else ""),
+                              "achieved": round(lm_gbps, 2),
                               "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(lm_gbps / HBM_PEAK_GBPS, 4),
                               "traffic": None, "algorithmic_bytes": ver_b}
     if not args.no_cpu_baseline:

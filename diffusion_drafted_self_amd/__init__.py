@@ -52,6 +52,9 @@ SIGNATURES = {
     "tidar_train_attention": (_c_int, [_c_int] * 7 + [_f] + [_p] * 6),
     "tidar_lmhead_verify_workspace": (_c_int, [_c_int] * 4 + [ctypes.POINTER(_c_size)]),
     "tidar_lmhead_verify_greedy": (_c_int, [_c_int] * 4 + [_p] * 7 + [_c_size, _p]),
+    "tidar_lmhead_packed_bytes": (_c_int, [_c_int] * 2 + [ctypes.POINTER(_c_size)]),
+    "tidar_lmhead_pack": (_c_int, [_c_int] * 2 + [_p] * 3),
+    "tidar_lmhead_verify_greedy_packed": (_c_int, [_c_int] * 4 + [_p] * 7 + [_c_size, _p]),
     "tidar_read_probe": (_c_int, [_p, _c_size, _p, _p]),
 }
 
@@ -327,18 +330,11 @@ def lmhead_verify_workspace_bytes(B: int, k: int, V: int, d_model: int) -> int:
     return n.value
 
 
-def lmhead_verify_greedy(h_ar, h_draft, w, cand, accept_len=None, next_cand=None, workspace=None):
-    """LM head (logits = h . W^T, never stored) fused with greedy
-    verification.  h_ar [B][k+1][d], h_draft [B][k][k][d], w [V][d], all
-    bf16.  Returns (accept_len, next_cand)."""
-    _need(h_ar, "h_ar", torch.bfloat16, 3)
+def _lmhead_outputs(h_ar, h_draft, cand, d, accept_len, next_cand):
+    """Checks the hidden rows and candidates; returns (B, k, accept_len, next_cand)."""
     dev = h_ar.device
-    B, k1, d = h_ar.shape
+    B, k1, _ = h_ar.shape
     k = k1 - 1
-    _need(w, "w", torch.bfloat16, 2, dev)
-    V = w.shape[0]
-    if w.shape[1] != d:
-        raise ValueError("w must be [V][d_model]")
     _need(cand, "cand", torch.int32, 2, dev)
     if tuple(cand.shape) != (B, k):
         raise ValueError("cand must be [B][k]")
@@ -354,10 +350,66 @@ def lmhead_verify_greedy(h_ar, h_draft, w, cand, accept_len=None, next_cand=None
         next_cand = torch.empty((B, k), dtype=torch.int32, device=dev)
     else:
         _need(next_cand, "next_cand", torch.int32, 2, dev)
+    return B, k, accept_len, next_cand
+
+
+def lmhead_verify_greedy(h_ar, h_draft, w, cand, accept_len=None, next_cand=None, workspace=None):
+    """LM head (logits = h . W^T, never stored) fused with greedy
+    verification.  h_ar [B][k+1][d], h_draft [B][k][k][d], w [V][d], all
+    bf16.  Returns (accept_len, next_cand)."""
+    _need(h_ar, "h_ar", torch.bfloat16, 3)
+    dev = h_ar.device
+    d = h_ar.shape[2]
+    _need(w, "w", torch.bfloat16, 2, dev)
+    V = w.shape[0]
+    if w.shape[1] != d:
+        raise ValueError("w must be [V][d_model]")
+    B, k, accept_len, next_cand = _lmhead_outputs(h_ar, h_draft, cand, d, accept_len, next_cand)
     ws = _workspace(lmhead_verify_workspace_bytes(B, k, V, d), dev, workspace)
     _check("tidar_lmhead_verify_greedy",
            lib().tidar_lmhead_verify_greedy(B, k, V, d, _ptr(h_ar), _ptr(h_draft), _ptr(w), _ptr(cand),
                                            _ptr(accept_len), _ptr(next_cand), _ptr(ws), ws.numel(), _stream()))
+    return accept_len, next_cand
+
+
+def lmhead_packed_bytes(V: int, d_model: int) -> int:
+    n = _c_size(0)
+    _check("tidar_lmhead_packed_bytes", lib().tidar_lmhead_packed_bytes(V, d_model, ctypes.byref(n)))
+    return n.value
+
+
+def lmhead_pack(w, out=None):
+    """The packed layout of the LM head w [V][d] bf16 (tiles of 256 rows by
+    64 columns, each one contiguous 32 KB block), as a flat bf16 tensor."""
+    _need(w, "w", torch.bfloat16, 2)
+    V, d = w.shape
+    n = lmhead_packed_bytes(V, d) // 2
+    if out is None:
+        out = torch.empty(n, dtype=torch.bfloat16, device=w.device)
+    else:
+        _need(out, "out", torch.bfloat16, 1, w.device)
+        if out.numel() < n:
+            raise ValueError(f"out holds {out.numel()} elements; the packed head needs {n}")
+    _check("tidar_lmhead_pack", lib().tidar_lmhead_pack(V, d, _ptr(w), _ptr(out), _stream()))
+    return out
+
+
+def lmhead_verify_greedy_packed(h_ar, h_draft, w_packed, V: int, cand, accept_len=None, next_cand=None,
+                                workspace=None):
+    """lmhead_verify_greedy with the head given as lmhead_pack(w) for a w
+    of V rows.  Returns (accept_len, next_cand)."""
+    _need(h_ar, "h_ar", torch.bfloat16, 3)
+    dev = h_ar.device
+    d = h_ar.shape[2]
+    _need(w_packed, "w_packed", torch.bfloat16, 1, dev)
+    if w_packed.numel() * 2 < lmhead_packed_bytes(V, d):
+        raise ValueError("w_packed is smaller than the packed head of V rows")
+    B, k, accept_len, next_cand = _lmhead_outputs(h_ar, h_draft, cand, d, accept_len, next_cand)
+    ws = _workspace(lmhead_verify_workspace_bytes(B, k, V, d), dev, workspace)
+    _check("tidar_lmhead_verify_greedy_packed",
+           lib().tidar_lmhead_verify_greedy_packed(B, k, V, d, _ptr(h_ar), _ptr(h_draft), _ptr(w_packed),
+                                                  _ptr(cand), _ptr(accept_len), _ptr(next_cand), _ptr(ws),
+                                                  ws.numel(), _stream()))
     return accept_len, next_cand
 
 
@@ -480,5 +532,6 @@ def read_probe(buf, sink=None):
 __all__ = ["step_attention", "step_attention_workspace_bytes", "verify_greedy", "verify_workspace_bytes",
            "verify_sample", "verify_sample_workspace_bytes", "kv_commit",
            "step_attention_paged", "kv_commit_paged", "train_attention",
-           "lmhead_verify_greedy", "lmhead_verify_workspace_bytes", "strerror", "lib", "TidarError", "LIB_PATH", "SIGNATURES",
+           "lmhead_verify_greedy", "lmhead_verify_workspace_bytes", "lmhead_pack", "lmhead_packed_bytes",
+           "lmhead_verify_greedy_packed", "strerror", "lib", "TidarError", "LIB_PATH", "SIGNATURES",
            "read_probe", "READ_PROBE_BLOCKS"]

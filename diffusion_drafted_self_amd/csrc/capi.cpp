@@ -156,11 +156,13 @@ struct LmPlan {
   size_t ar_bytes, draft_bytes, group_bytes, total;
 };
 
-int plan_lmhead(int B, int k, int V, int d, LmPlan* p) {
+int plan_lmhead(int B, int k, int V, int d, bool packed, LmPlan* p) {
   if (k > kMaxK) return TIDAR_EUNSUPPORTED;
   if (B < 0 || k < 1 || V < 1 || d < 64 || d % 64 != 0) return TIDAR_EINVAL;
-  // direct loads address W and the hidden rows with 32-bit byte offsets
-  if ((double)V * d * 2 >= 4294967296.0 || (double)B * k * k * d * 2 >= 4294967296.0) return TIDAR_EUNSUPPORTED;
+  // direct loads address the hidden rows, and a row-major W, with 32-bit
+  // byte offsets (a packed W from the start of each chunk's tiles)
+  if ((!packed && (double)V * d * 2 >= 4294967296.0) || (double)B * k * k * d * 2 >= 4294967296.0)
+    return TIDAR_EUNSUPPORTED;
   p->n_chunks = (int)cdiv(V, tidar::kLmChunk);
   if (cdiv((long)B * (k + 1), tidar::kLmRows) > 65535) return TIDAR_EUNSUPPORTED;
   p->ar_bytes = round_up((size_t)B * (k + 1) * p->n_chunks * sizeof(float2), 256);
@@ -433,17 +435,31 @@ int tidar_verify_greedy(int B, int k, int V, const float* ar_logits, const float
 int tidar_lmhead_verify_workspace(int B, int k, int V, int d_model, size_t* bytes) {
   if (!bytes) return TIDAR_EINVAL;
   LmPlan p;
-  const int st = plan_lmhead(B, k, V, d_model, &p);
+  const int st = plan_lmhead(B, k, V, d_model, true, &p);
   if (st != TIDAR_OK) return st;
   *bytes = p.total;
   return TIDAR_OK;
 }
 
-int tidar_lmhead_verify_greedy(int B, int k, int V, int d_model, const void* h_ar, const void* h_draft,
-                               const void* w, const int32_t* cand, int32_t* accept_len, int32_t* next_cand,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+int tidar_lmhead_packed_bytes(int V, int d_model, size_t* bytes) {
+  if (!bytes || V < 1 || d_model < 64 || d_model % 64 != 0) return TIDAR_EINVAL;
+  *bytes = tidar::lmhead_packed_bytes(V, d_model);
+  return TIDAR_OK;
+}
+
+int tidar_lmhead_pack(int V, int d_model, const void* w, void* w_packed, void* stream) {
+  if (V < 1 || d_model < 64 || d_model % 64 != 0) return TIDAR_EINVAL;
+  if (!aligned(w, 16) || !aligned(w_packed, 16)) return TIDAR_EINVAL;
+  const hipError_t e = tidar::launch_lmhead_pack(w, w_packed, V, d_model, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
+}
+
+// the two layouts of W share everything but the kernel's W addressing
+static int lmhead_verify(bool packed, int B, int k, int V, int d_model, const void* h_ar, const void* h_draft,
+                         const void* w, const int32_t* cand, int32_t* accept_len, int32_t* next_cand,
+                         void* workspace, size_t workspace_bytes, void* stream) {
   LmPlan p;
-  const int st = plan_lmhead(B, k, V, d_model, &p);
+  const int st = plan_lmhead(B, k, V, d_model, packed, &p);
   if (st != TIDAR_OK) return st;
   if (B == 0) return TIDAR_OK;
   if (!aligned(h_ar, 16) || !aligned(w, 16) || !aligned(cand, 4) || !aligned(accept_len, 4) ||
@@ -473,6 +489,7 @@ int tidar_lmhead_verify_greedy(int B, int k, int V, int d_model, const void* h_a
   la.V = V;
   la.d = d_model;
   la.n_chunks = p.n_chunks;
+  la.packed = packed ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // AR rows -> chunk results -> accept length, bonus token, group
   la.h = h_ar;
@@ -492,6 +509,20 @@ int tidar_lmhead_verify_greedy(int B, int k, int V, int d_model, const void* h_a
     if (e == hipSuccess) e = tidar::launch_draft_finalize(va, s);
   }
   return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
+}
+
+int tidar_lmhead_verify_greedy(int B, int k, int V, int d_model, const void* h_ar, const void* h_draft,
+                               const void* w, const int32_t* cand, int32_t* accept_len, int32_t* next_cand,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return lmhead_verify(false, B, k, V, d_model, h_ar, h_draft, w, cand, accept_len, next_cand, workspace,
+                       workspace_bytes, stream);
+}
+
+int tidar_lmhead_verify_greedy_packed(int B, int k, int V, int d_model, const void* h_ar, const void* h_draft,
+                                      const void* w_packed, const int32_t* cand, int32_t* accept_len,
+                                      int32_t* next_cand, void* workspace, size_t workspace_bytes, void* stream) {
+  return lmhead_verify(true, B, k, V, d_model, h_ar, h_draft, w_packed, cand, accept_len, next_cand, workspace,
+                       workspace_bytes, stream);
 }
 
 int tidar_verify_sample_workspace(int B, int k, int V, size_t* bytes) {

@@ -63,13 +63,15 @@ constexpr int kLmRows = 144;    // hidden-state rows per workgroup (9 tiles of 1
 
 struct LmArgs {
   const void* h;        // pass 0: [B][k+1][d] AR rows; pass 1: [B][k][k][d] draft rows
-  const void* w;        // [V][d] bf16
+  const void* w;        // [V][d] bf16, or packed (lmhead_pack_kernel)
   const int32_t* group; // [B] selected group (pass 1)
   float2* part;         // [rows][n_chunks] (value, index bits)
-  int B, k, V, d, n_chunks, rows, draft;
+  int B, k, V, d, n_chunks, rows, draft, packed;
 };
 
 hipError_t launch_lmhead_argmax(const LmArgs& a, hipStream_t s);
+size_t lmhead_packed_bytes(int V, int d);
+hipError_t launch_lmhead_pack(const void* w, void* wp, int V, int d, hipStream_t s);
 hipError_t launch_read_probe(const void* src, size_t bytes, unsigned* sink, hipStream_t s);
 
 constexpr int kReadProbeBlocks = 16384;  // workgroups of the streaming-read probe

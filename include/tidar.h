@@ -246,6 +246,37 @@ int tidar_lmhead_verify_greedy(int B, int k, int V, int d_model, const void* h_a
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * The same LM head with W in a packed layout, made once when the weights
+ * are loaded.  The fused head reads W in tiles of 256 vocabulary rows by 64
+ * hidden elements; in the row-major layout such a tile is 256 separate
+ * 128-byte runs, 2*d_model bytes apart, while in the packed layout it is
+ * one contiguous 32 KB block, which memory serves faster.  Results are
+ * bit-for-bit those of tidar_lmhead_verify_greedy on the row-major W.
+ *
+ * tidar_lmhead_packed_bytes: size of the packed W,
+ *   ceil(V / 256) * 256 * d_model * 2 bytes.  EINVAL for V < 1 or a
+ *   d_model that is not a positive multiple of 64.
+ * tidar_lmhead_pack: w [V][d_model] bf16 (row-major, 16-byte aligned) ->
+ *   w_packed (16-byte aligned, tidar_lmhead_packed_bytes() bytes, owned by
+ *   the caller; must not overlap w).  Asynchronous on `stream`.  Layout:
+ *   tile (c, s), c < ceil(V/256), s < d_model/64, is the 32 KB block at
+ *   byte (c * (d_model/64) + s) * 32768; its bytes 128*r + 16*j .. +15 hold
+ *   w[256*c + r][64*s + 8*(j ^ (r % 8)) .. +7] (r < 256, j < 8), and zeros
+ *   for rows 256*c + r >= V.
+ * tidar_lmhead_verify_greedy_packed: as tidar_lmhead_verify_greedy, with
+ *   w_packed from tidar_lmhead_pack(V, d_model, ...) in place of w.  The
+ *   2^32 bound on V * d_model * 2 does not apply; the one on the draft
+ *   rows does.  The workspace is the same.
+ * ---------------------------------------------------------------------- */
+int tidar_lmhead_packed_bytes(int V, int d_model, size_t* bytes);
+
+int tidar_lmhead_pack(int V, int d_model, const void* w, void* w_packed, void* stream);
+
+int tidar_lmhead_verify_greedy_packed(int B, int k, int V, int d_model, const void* h_ar, const void* h_draft,
+                                      const void* w_packed, const int32_t* cand, int32_t* accept_len,
+                                      int32_t* next_cand, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Stochastic verification (temperature T > 0) and sampling of the next drafts.
  *
  * The final tokens are sampled autoregressively and the output matches

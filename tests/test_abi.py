@@ -196,12 +196,33 @@ def test_lmhead_validation_and_size(T):
     assert n.value == want
     assert L.tidar_lmhead_verify_workspace(16, 8, 128256, 100, ctypes.byref(n)) == -1   # d % 64
     assert L.tidar_lmhead_verify_workspace(16, 17, 1000, 64, ctypes.byref(n)) == -2     # k
-    assert L.tidar_lmhead_verify_workspace(1, 1, 600000, 4096, ctypes.byref(n)) == -2   # W past 32-bit offsets
+    # a head past 32-bit byte offsets: the packed form takes it, the row-major one does not
+    assert L.tidar_lmhead_verify_workspace(1, 1, 600000, 4096, ctypes.byref(n)) == 0
     p = ctypes.c_void_p(0x100000)
-    f = L.tidar_lmhead_verify_greedy
-    assert f(2, 4, 1000, 64, p, p, p, p, p, p, p, 8, None) == -3
-    assert f(2, 4, 1000, 64, p, None, p, p, p, p, p, 1 << 20, None) == -1
-    assert f(0, 4, 1000, 64, None, None, None, None, None, None, None, 0, None) == 0
+    for f in (L.tidar_lmhead_verify_greedy, L.tidar_lmhead_verify_greedy_packed):
+        assert f(2, 4, 1000, 64, p, p, p, p, p, p, p, 8, None) == -3
+        assert f(2, 4, 1000, 64, p, None, p, p, p, p, p, 1 << 20, None) == -1
+        assert f(0, 4, 1000, 64, None, None, None, None, None, None, None, 0, None) == 0
+    assert L.tidar_lmhead_verify_greedy(1, 1, 600000, 4096, p, p, p, p, p, p, p, 1 << 30, None) == -2
+    assert L.tidar_lmhead_verify_greedy_packed(1, 1, 600000, 4096, p, p, p, p, p, p, p, 8, None) == -3
+
+
+def test_lmhead_pack_validation_and_size(T):
+    L = T.lib()
+    n = ctypes.c_size_t(0)
+    assert L.tidar_lmhead_packed_bytes(1000, 64, ctypes.byref(n)) == 0
+    assert n.value == 4 * 256 * 64 * 2            # V rounded up to whole 256-row chunks
+    assert L.tidar_lmhead_packed_bytes(128256, 4096, ctypes.byref(n)) == 0
+    assert n.value == 128256 * 4096 * 2           # 128256 = 501 chunks exactly
+    assert L.tidar_lmhead_packed_bytes(0, 64, ctypes.byref(n)) == -1
+    assert L.tidar_lmhead_packed_bytes(1000, 100, ctypes.byref(n)) == -1
+    assert L.tidar_lmhead_packed_bytes(1000, 64, None) == -1
+    p = ctypes.c_void_p(0x100000)
+    f = L.tidar_lmhead_pack
+    assert f(1000, 100, p, p, None) == -1          # d % 64
+    assert f(0, 64, p, p, None) == -1
+    assert f(1000, 64, ctypes.c_void_p(0x100004), p, None) == -1   # misaligned w
+    assert f(1000, 64, p, None, None) == -1
 
 
 def test_read_probe_validation(T):

@@ -15,7 +15,7 @@ from oracle.lmhead import lmhead_verify_ref
 pytestmark = pytest.mark.gpu
 
 tidar = pytest.importorskip("diffusion_drafted_self_amd")
-from _gpu_util import to_dev  # noqa: E402
+from _gpu_util import bits, to_dev  # noqa: E402
 
 MARGIN = 1e-3
 
@@ -23,6 +23,14 @@ MARGIN = 1e-3
 def _run(d):
     hd = None if d["h_draft"] is None else to_dev(d["h_draft"], True)
     a, n = tidar.lmhead_verify_greedy(to_dev(d["h_ar"], True), hd, to_dev(d["w"], True), to_dev(d["cand"]))
+    return a.cpu().numpy(), n.cpu().numpy()
+
+
+def _run_packed(d):
+    hd = None if d["h_draft"] is None else to_dev(d["h_draft"], True)
+    w = to_dev(d["w"], True)
+    a, n = tidar.lmhead_verify_greedy_packed(to_dev(d["h_ar"], True), hd, tidar.lmhead_pack(w), w.shape[0],
+                                             to_dev(d["cand"]))
     return a.cpu().numpy(), n.cpu().numpy()
 
 
@@ -52,7 +60,7 @@ def _compare(d, a, n, seqs, what):
     return near
 
 
-@pytest.mark.parametrize("B,k,V,d,accept", [
+SHAPES = [
     (4, 8, 32000, 1024, "uniform"),
     (6, 4, 5003, 256, "uniform"),      # V ends mid-chunk
     (5, 1, 1000, 64, "uniform"),       # no drafts
@@ -61,7 +69,10 @@ def _compare(d, a, n, seqs, what):
     (18, 3, 3001, 128, "uniform"),     # 72 AR rows: five row tiles per workgroup
     (22, 3, 2049, 64, "uniform"),      # 88 AR rows: six row tiles
     (30, 3, 1024, 192, "geometric"),   # 120 AR rows: eight row tiles
-])
+]
+
+
+@pytest.mark.parametrize("B,k,V,d,accept", SHAPES)
 def test_lmhead_verify_matches_oracle(B, k, V, d, accept):
     print(f"lmhead B={B} k={k} V={V} d={d}", flush=True)
     data = W.lmhead_inputs(B, k, V, d, seed=B + k + d, accept=accept)
@@ -83,6 +94,47 @@ def test_lmhead_verify_full_size(name, B, k, V, d):
     assert a.tolist() == data["planted"].tolist()
     assert ((n >= 0) & (n < V)).all()
     _compare(data, a, n, [0, B // 2, B - 1], name)
+    # the packed head gives the same bits: the same products in the same order
+    ap, np_ = _run_packed(data)
+    assert ap.tolist() == a.tolist() and np_.tolist() == n.tolist()
+
+
+def _packed_layout(w_bits, V, d):
+    """The packed layout as tidar.h states it: tile (c, s) at byte
+    (c * (d/64) + s) * 32768 holds, at byte 128 r + 16 j, the 8 elements of
+    row 256 c + r from column 64 s + 8 (j ^ (r % 8)); rows past V are zero."""
+    nc, ns = -(-V // 256), d // 64
+    wp = np.zeros((nc * 256, d), dtype=np.uint16)
+    wp[:V] = w_bits
+    out = np.empty((nc, ns, 256, 8, 8), dtype=np.uint16)
+    r = np.arange(256)
+    for j in range(8):
+        src = 8 * (j ^ (r % 8))                       # first column of physical piece j, per row
+        for s in range(ns):
+            cols = 64 * s + src[:, None] + np.arange(8)[None, :]
+            out[:, s, :, j, :] = wp.reshape(nc, 256, d)[:, r[:, None], cols]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("V,d", [(3001, 128), (256, 64), (5, 192)])
+def test_pack_layout(V, d):
+    print(f"lmhead pack V={V} d={d}", flush=True)
+    w = W.lmhead_inputs(1, 1, V, d, seed=V + d)["w"]
+    got = bits(tidar.lmhead_pack(to_dev(w, True)))
+    assert got.tolist() == _packed_layout(w, V, d).tolist()
+
+
+@pytest.mark.parametrize("B,k,V,d,accept", SHAPES)
+def test_packed_head_matches_row_major(B, k, V, d, accept):
+    """The packed W changes only where the kernel reads each tile from: the
+    results are the row-major head's, bit for bit, and the planted accept
+    lengths."""
+    print(f"lmhead packed B={B} k={k} V={V} d={d}", flush=True)
+    data = W.lmhead_inputs(B, k, V, d, seed=B + k + d, accept=accept)
+    a, n = _run(data)
+    ap, np_ = _run_packed(data)
+    assert ap.tolist() == a.tolist() and np_.tolist() == n.tolist()
+    assert ap.tolist() == data["planted"].tolist()
 
 
 def test_equal_logits_take_the_lowest_index_across_chunks():
