@@ -265,11 +265,12 @@ __device__ __forceinline__ void stage_issue(StagedRows<D>& st, const bf16* kt, c
 
 // The rest of staging a masked tile whose loads stage_issue made: the K
 // pieces into their rows, the settled part of V^T (a second batch of loads,
-// present only when the prefix is not a multiple of the tile), then the
-// step rows' values scattered into V^T columns.
-template <int D>
+// present only when the tile holds settled positions), then the step rows'
+// values scattered into V^T columns.  wait_loads waits for this tile's
+// loads and LDS stores (the caller knows what else is in flight).
+template <int D, class Wait>
 __device__ __forceinline__ void stage_commit(const StagedRows<D>& st, lds_char* sK, lds_char* sV, const bf16* vt,
-                                             int t0, int L, int Ltot, int tid) {
+                                             int t0, int L, int Ltot, int tid, Wait&& wait_loads) {
   using S = StagedRows<D>;
   using T = Tile<D>;
   const int j0 = max(t0, L), j1 = min(t0 + TK, Ltot);
@@ -296,8 +297,8 @@ __device__ __forceinline__ void stage_commit(const StagedRows<D>& st, lds_char* 
     const int id = tid + i * S::NT, d = id >> 3, q = id & 7;
     *(lds_bf16x8*)(sV + d * T::VROW + ((q ^ vswz(d)) * 16)) = vp[i];
   }
-  wait_all();
-  barrier();  // the scatter below overwrites 2-byte parts of those pieces
+  wait_loads();  // this tile's loads and stores are done
+  barrier();     // the scatter below overwrites 2-byte parts of those pieces
   // step rows scattered into 8 V^T rows.  Consecutive lanes take
   // consecutive keys, so each 2-byte store of a wave fills one V^T row
   // across 64 columns (lanes on the same column would all hit one bank).
@@ -864,17 +865,38 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
       stage_issue<D>(staged, settled ? kv.ktile(t0 / TK) : nullptr, ks_base, vs_base, step_stride, t0, L, Ltot, tid);
     }
   };
-  auto tail_stage = [&](int i) {  // masked tile i into the last slot
+  // The ring prologue goes out right after the last masked tile's loads
+  // when that tile holds no settled position: its staging then issues no
+  // load after them, so its waits can leave the prologue in flight (loads
+  // complete in order) and the prologue lands during that tile's staging
+  // and compute.  Otherwise (lean staging, or a settled part) it goes out
+  // once that tile has landed, and lands while it computes.
+  const int n_tail = nA + nB;
+  const bool early = kBatch && n_tail > 0 && tail_t0(n_tail - 1) >= L;
+  // the staged tile's loads (and LDS stores) are done; with the prologue
+  // pending, its direct loads are the only ones that may still be in flight
+  auto wait_staged = [&](bool prologue_pending) {
+    if (!prologue_pending) {
+      wait_all();
+      return;
+    }
+    if (n > 2) wait_vmcnt<3 * T::NKW + 2 * T::NVW>();
+    else if (n > 1) wait_vmcnt<2 * T::NKW + 2 * T::NVW>();
+    else if (n > 0) wait_vmcnt<T::NKW + T::NVW>();
+    else wait_vmcnt<0>();
+    wait_lgkmcnt0();
+  };
+  auto tail_stage = [&](int i, bool prologue_pending) {  // masked tile i into the last slot
     const int t0 = tail_t0(i);
     barrier();
     const bool settled = t0 < L;
     if constexpr (kBatch)
       stage_commit<D>(staged, kslot(RING - 1), vslot(RING - 1), settled ? kv.vtile(t0 / TK) : nullptr, t0, L, Ltot,
-                      tid);
+                      tid, [&] { wait_staged(prologue_pending); });
     else
       stage_tail_tile_lean<D>(kslot(RING - 1), vslot(RING - 1), settled ? kv.ktile(t0 / TK) : nullptr,
                               settled ? kv.vtile(t0 / TK) : nullptr, ks_base, vs_base, step_stride, t0, L, Ltot, tid);
-    wait_all();
+    wait_staged(prologue_pending);
     barrier();
   };
   // fresh: no reference is set yet (the kernel's first masked tile), so the
@@ -916,20 +938,19 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
     pv_tile<D, NF, NS>(sV, pA, ac, lane, wave);
     wait_lgkmcnt0();
   };
-  // The ring prologue is requested once the last masked tile has landed:
-  // a load issued after it would wait for it (loads complete in order).
-  // It then lands while that tile computes (its slots 0..RING-2 are not
-  // that tile's).
-  if (nA + nB > 0) tail_issue(0);
-  for (int i = 0; i + 1 < nA + nB; ++i) {
-    tail_stage(i);
+  // (the prologue's slots 0..RING-2 are not the masked tiles' slot)
+  if (n_tail > 0) tail_issue(0);
+  if (early && n_tail == 1) ring_prologue();
+  for (int i = 0; i + 1 < n_tail; ++i) {
+    tail_stage(i, false);
     tail_issue(i + 1);  // in flight while tile i computes
+    if (early && i + 2 == n_tail) ring_prologue();
     tail_compute(i, i == 0);
   }
-  if (nA + nB > 0) {
-    tail_stage(nA + nB - 1);
-    ring_prologue();
-    tail_compute(nA + nB - 1, nA + nB == 1);
+  if (n_tail > 0) {
+    tail_stage(n_tail - 1, early);
+    if (!early) ring_prologue();
+    tail_compute(n_tail - 1, n_tail == 1);
   } else {
     ring_prologue();
   }
@@ -1030,7 +1051,7 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
       }
       for (int i = 0; i < nA + nB; ++i) {
         tail_issue(i);
-        tail_stage(i);
+        tail_stage(i, false);  // nothing else is in flight here
         tail_compute(i, false);
       }
     }
