@@ -37,6 +37,7 @@ Prints ONE JSON line.  Options:
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import re
 import json
@@ -72,6 +73,9 @@ def parse():
                    help="layout of W for --verify lmhead (packed once, before timing, as at weight load)")
     p.add_argument("--temperature", type=float, default=1.0)
     p.add_argument("--paged", action="store_true")
+    p.add_argument("--loop", type=int, default=0, metavar="N",
+                   help="serving loop: N consecutive steps on one cache whose lengths the commit advances in "
+                        "place (no restore), per-step p50/p99 and mean GB/s as the lengths grow")
     p.add_argument("--workload", default="step_8b",
                    choices=["step_8b", "step_1p5b", "step_8b_long", "ragged_8b", "train_8b"],
                    help="synthetic workload (the reported line is the 8B-shaped step; ragged_8b is one step of "
@@ -396,6 +400,88 @@ def achievable_read_gbps(tidar, torch, dev, stream, gib: int = 4, reps: int = 5)
     return gbps
 
 
+def bench_loop(args, wl, d, v, a_planted, reps, n_rep, attention, verify_commit, tidar, torch, np, dev, stream):
+    """The serving loop: args.loop consecutive steps on replica 0's cache.
+    Each step's commit advances the device-side lengths in place; the host
+    keeps the exact lengths (the accept lengths are planted) only to bound
+    max_len and to count each step's algorithmic bytes.  Step rows and
+    logits cycle over the input replicas, which all carry the same planted
+    accept lengths."""
+    s = wl.attn
+    N = args.loop
+    if args.paged or args.verify != "greedy":
+        sys.exit("--loop runs the contiguous cache with greedy verification")
+    lens_h = np.array(s.lens, dtype=np.int64)
+    a = np.asarray(a_planted, dtype=np.int64)
+    if int(lens_h.max()) + N * s.k > s.S_max:
+        sys.exit(f"--loop {N}: the cache of this workload holds {s.S_max} positions, "
+                 f"lengths reach up to {int(lens_h.max()) + N * s.k}")
+    r0 = reps[0]
+    for i in range(args.warmup):  # ordinary steps (lengths restored)
+        r = reps[i % n_rep]
+        attention(r)
+        verify_commit(r, i)
+    torch.cuda.synchronize()
+    max_lens = [int(lens_h.max() + t * a.max()) for t in range(N)]
+    ws = max(tidar.step_attention_workspace_bytes(0, s.B, s.Hq, s.Hkv, s.D, s.S_max, ml, s.k, s.n_groups,
+                                                  args.kv_chunk) for ml in max_lens)
+    ws_a = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(N)]
+    step_b, attn_b, flops = [], [], []
+    for t in range(N):
+        r = reps[t % n_rep]
+        sh = dataclasses.replace(s, lens=tuple(int(x) for x in lens_h))
+        ab, vb, cb, _, fl = step_bytes(sh, wl.V, a, "greedy")
+        step_b.append(ab + vb + cb)
+        attn_b.append(ab)
+        flops.append(fl + 4 * s.D * s.Hq * s.B * visible_step_pairs(s.k, s.n_groups))
+        ev[t][0].record(stream)
+        tidar.step_attention(r["q"], r["k_step"], r["v_step"], r0["k_cache"], r0["v_cache"], r0["lens"], s.k,
+                             s.n_groups, s.sm_scale, max_len=max_lens[t], out=r["out"], lse=r["lse"],
+                             workspace=ws_a, kv_chunk=args.kv_chunk)
+        ev[t][1].record(stream)
+        tidar.verify_greedy(r["ar_logits"], r["draft_logits"], r["cand"], accept_len=r0["acc"],
+                            next_cand=r0["next"], workspace=r["ws_v"])
+        tidar.kv_commit(r0["k_cache"], r0["v_cache"], r0["lens"], r["k_step"], r["v_step"], r0["acc"], s.k,
+                        r0["err"])
+        ev[t][2].record(stream)
+        lens_h = lens_h + a
+    torch.cuda.synchronize()
+    assert r0["acc"].cpu().numpy().tolist() == a.tolist(), "verify result differs from the planted accept lengths"
+    assert r0["lens"].cpu().numpy().tolist() == lens_h.tolist() and int(r0["err"].abs().sum()) == 0
+    step_ms = np.array([ev[t][0].elapsed_time(ev[t][2]) for t in range(N)])
+    attn_ms = np.array([ev[t][0].elapsed_time(ev[t][1]) for t in range(N)])
+    total_ms = ev[0][0].elapsed_time(ev[N - 1][2])
+    step_gbps = sum(step_b) / (total_ms * 1e-3) / 1e9
+    attn_gbps = sum(attn_b) / (attn_ms.sum() * 1e-3) / 1e9
+    result = {
+        "metric": METRIC, "value": round(step_gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": N,
+        "warmup": args.warmup, "ms_per_step": round(total_ms / N, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name + "_loop", "batch": s.B, "q_heads": s.Hq, "kv_heads": s.Hkv,
+                   "head_dim": s.D, "prefix_start_mean": float(np.mean(s.lens)),
+                   "prefix_end_mean": float(lens_h.mean()), "k": s.k, "draft_groups": s.n_groups,
+                   "step_rows": s.R, "vocab": wl.V, "accept": wl.accept, "verify": "greedy",
+                   "kv_layout": "contiguous", "input_replicas": n_rep},
+        "step_us_mean": round(total_ms / N * 1e3, 2),
+        "step_us_p50": round(float(np.percentile(step_ms, 50)) * 1e3, 2),
+        "step_us_p99": round(float(np.percentile(step_ms, 99)) * 1e3, 2),
+        "attention_us_p50": round(float(np.percentile(attn_ms, 50)) * 1e3, 2),
+        "attention_us_p99": round(float(np.percentile(attn_ms, 99)) * 1e3, 2),
+        "attention_us_first": round(float(attn_ms[0]) * 1e3, 2),
+        "attention_us_last": round(float(attn_ms[-1]) * 1e3, 2),
+        "attention_gbps_mean": round(attn_gbps, 2),
+        "attention_hbm_frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
+        "attention_tflops_mean": round(sum(flops) / (attn_ms.sum() * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "hbm", "kernel": "tidar_step_attention", "achieved": round(attn_gbps, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "algorithmic_bytes": int(np.mean(attn_b))},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, d, v, a_planted, args)
+    print(json.dumps(result))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -524,6 +610,9 @@ def main():
 
     stream = torch.cuda.current_stream()
     K, Wu = args.steps, args.warmup
+    if args.loop:
+        bench_loop(args, wl, d, v, a_planted, reps, n_rep, attention, verify_commit, tidar, torch, np, dev, stream)
+        return
     ev_a = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     # the fused LM head dominates its step: its own end event after verify
     ev_v = [torch.cuda.Event(enable_timing=True) if args.verify == "lmhead" else None for _ in range(K)]

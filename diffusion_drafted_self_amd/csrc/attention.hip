@@ -37,7 +37,8 @@ namespace {
 
 constexpr int TK = 64;    // keys per tile
 constexpr int NWV = 4;    // waves per bf16 workgroup, one per SIMD
-constexpr int RING = 4;   // LDS slots for K tiles, and as many for V^T tiles
+constexpr int RING = 4;
+constexpr int kMaxRankedB = 256;  // batches up to this size run longest sequences first   // LDS slots for K tiles, and as many for V^T tiles
 
 // The value cache holds pages of VPAGE positions, each stored transposed
 // ([S_max/VPAGE][D][VPAGE] per (b, kvh)), so one 64-key V^T tile is one
@@ -674,13 +675,50 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
   const int wave = tid >> 6;
   const int hi = lane >> 4;
 
-  int t = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int rw = t % a.n_rowblk;
-  t /= a.n_rowblk;
-  const int split = t % a.n_split;
-  t /= a.n_split;
-  const int kvh = t % a.Hkv;
-  const int b = t / a.Hkv;
+  // The (sequence, KV head) unit this workgroup serves; a unit's n_rowblk
+  // x n_split workgroups are consecutive and on one XCD (blocks are dealt
+  // round-robin over the 8 XCDs, and each XCD starts its blocks in order).
+  // Decode steps order the units longest sequence first (equal lengths in
+  // sequence order) and deal each group of 8 ranks over the XCDs in a
+  // snake, so every XCD gets a similar total and starts its longest units
+  // first: with ragged lengths, consecutive sequences per XCD left some
+  // XCDs with far more keys than others.  Each workgroup ranks the
+  // lengths itself (B*B compares in LDS), so no pass before the kernel is
+  // needed.  Other shapes keep the plain interleaved order.
+  int rw, split, kvh, b;
+  if (!TRAIN && a.B <= kMaxRankedB && (a.B * a.Hkv) % 8 == 0) {
+    __shared__ int s_len[kMaxRankedB];
+    __shared__ int s_pick;
+    const int wpu = a.n_rowblk * a.n_split;
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int pos = j / wpu, within = j % wpu;
+    const int rank = pos * 8 + ((pos & 1) ? 7 - x : x);
+    const int rank_b = rank / a.Hkv;
+    kvh = rank % a.Hkv;
+    rw = within % a.n_rowblk;
+    split = within / a.n_rowblk;
+    for (int i = tid; i < a.B; i += 64 * NWV) s_len[i] = a.lens[i];
+    __syncthreads();
+    for (int i = tid; i < a.B; i += 64 * NWV) {
+      const int li = s_len[i];
+      int r = 0;
+      for (int q2 = 0; q2 < a.B; ++q2) {
+        const int lq = s_len[q2];
+        r += (lq > li) | ((lq == li) & (q2 < i));
+      }
+      if (r == rank_b) s_pick = i;  // exactly one sequence has each rank
+    }
+    __syncthreads();
+    b = s_pick;
+  } else {
+    int t = xcd_logical_block(blockIdx.x, gridDim.x);
+    rw = t % a.n_rowblk;
+    t /= a.n_rowblk;
+    split = t % a.n_split;
+    t /= a.n_split;
+    kvh = t % a.Hkv;
+    b = t / a.Hkv;
+  }
 
   // this workgroup's tiles [T0, T1): wave w owns T0 + w*NF + f (f < NF);
   // the shared tiles T0 + 4*NF + s (s < NS) are split by key block
