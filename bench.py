@@ -28,6 +28,10 @@ Prints ONE JSON line.  Options:
   --verify sample   stochastic verification (temperature --temperature, Philox
                     stream of --seed and the step number) in place of greedy;
                     inputs from the sampling generator, accept lengths as drawn
+  --loop N          the serving loop: N consecutive steps on one cache whose
+                    lengths the commit advances in place (no restore); per-step
+                    p50/p99 and mean GB/s as the lengths grow (e.g. with
+                    --workload ragged_8b --loop 256)
   --calibrate-copy  run only a plain device copy of known size (for scaling
                     the FETCH_SIZE / WRITE_SIZE counters)
   --summarize DIR   turn rocprofv3 outputs under DIR (kt/, pmc_FETCH_SIZE/,
