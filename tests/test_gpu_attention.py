@@ -48,6 +48,11 @@ CASES = {
     "bf16_k1_one_group": _shape(2, 4, 1, 64, 1, 1, (5, 191)),
     "bf16_prescaled_keys_scale1": _shape(2, 32, 8, 128, 8, 8, (257, 64), scale=1.0, k_prescale=1 / math.sqrt(128)),
     "f32_tiny_mha_d64_k4": _shape(1, 4, 4, 64, 4, 4, (64,), dtype="f32"),
+    # work order: longest sequences first when B <= 256 and B*Hkv is a
+    # multiple of 8 (ties broken by sequence index), plain order otherwise
+    "bf16_ranked_ties_and_zeros": _shape(8, 8, 2, 64, 4, 4, (300, 0, 300, 65, 0, 129, 64, 300)),
+    "bf16_ranked_batch256": _shape(256, 2, 1, 64, 1, 0, tuple((i * 53) % 197 for i in range(256))),
+    "bf16_plain_order_batch264": _shape(264, 2, 1, 64, 1, 0, tuple((i * 37) % 131 for i in range(264))),
     "f32_gqa4_d128_k8": _shape(2, 8, 2, 128, 8, 8, (1000, 3), dtype="f32"),
     "f32_zero_drafts": _shape(2, 4, 2, 64, 3, 0, (0, 33), dtype="f32"),
 }
