@@ -37,6 +37,9 @@ Prints ONE JSON line.  Options:
   --summarize DIR   turn rocprofv3 outputs under DIR (kt/, pmc_FETCH_SIZE/,
                     pmc_WRITE_SIZE/, pmc_copy_FETCH_SIZE/, pmc_copy_WRITE_SIZE/)
                     into the summaries kept under profiles/
+  --summarize-lmhead DIR  the same for the fused LM head's FETCH_SIZE /
+                    WRITE_SIZE runs (pmc_FETCH_SIZE/, pmc_WRITE_SIZE/ of
+                    --verify lmhead); its bench line then carries the traffic
 """
 from __future__ import annotations
 
@@ -59,6 +62,9 @@ COPY_CALIB_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_step_8b_traffic.txt")
 ATTN_SOURCES = [os.path.join(ROOT, "diffusion_drafted_self_amd", "csrc", n)
                 for n in ("attention.hip", "common.h", "launch.h", "lds_dma.h")]
+LM_SOURCES = [os.path.join(ROOT, "diffusion_drafted_self_amd", "csrc", n)
+              for n in ("lmhead.hip", "common.h", "launch.h", "lds_dma.h")]
+LM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_verify_8b_traffic.txt")
 
 
 def parse():
@@ -72,6 +78,8 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--kv-chunk", type=int, default=0, help="key positions per attention chunk (0: library plan)")
     p.add_argument("--summarize", metavar="DIR", help="write profiles/ summaries from rocprofv3 outputs in DIR")
+    p.add_argument("--summarize-lmhead", metavar="DIR",
+                   help="write the fused LM head's traffic summary from FETCH_SIZE / WRITE_SIZE runs in DIR")
     p.add_argument("--verify", default="greedy", choices=["greedy", "sample", "lmhead"])
     p.add_argument("--lm-layout", default="packed", choices=["packed", "rowmajor"],
                    help="layout of W for --verify lmhead (packed once, before timing, as at weight load)")
@@ -103,22 +111,68 @@ def attention_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, or None when absent or taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
+def _kv_file(path):
     kv = {}
-    for line in open(TRAFFIC_FILE):
-        if "=" in line and not line.lstrip().startswith("#"):
-            key, val = line.split("=", 1)
-            kv[key.strip()] = val.strip()
-    if kv.get("kernel_source_sha") != attention_source_sha():
+    if os.path.exists(path):
+        for line in open(path):
+            if "=" in line and not line.lstrip().startswith("#"):
+                key, val = line.split("=", 1)
+                kv[key.strip()] = val.strip()
+    return kv
+
+
+def read_traffic(path=None, sha=None, key="hbm_bytes_per_launch"):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or
+    None when absent or taken on a different kernel source."""
+    kv = _kv_file(path or TRAFFIC_FILE)
+    if kv.get("kernel_source_sha") != (sha or attention_source_sha)():
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
+
+
+def lmhead_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in LM_SOURCES:
+        h.update(_code_only(open(f, encoding="utf-8").read()).encode())
+    return h.hexdigest()[:16]
+
+
+def summarize_lmhead(dirname):
+    """HBM traffic of the fused LM head (packed W, 8B-shaped step) from
+    FETCH_SIZE / WRITE_SIZE runs under dirname; written under profiles/."""
+    import statistics
+    cal = _kv_file(TRAFFIC_FILE)
+    f_fetch, f_write = float(cal["copy_scale_fetch"]), float(cal["copy_scale_write"])
+    out = ["# HBM traffic of the fused LM head + greedy verify, packed W, 8B-shaped step (rocprofv3 counters)",
+           "# Commands (from the repository root, MI355X), one counter per run:",
+           "#   rocprofv3 --pmc FETCH_SIZE -d DIR/pmc_FETCH_SIZE -o p --output-format csv -- "
+           "python3 bench.py --verify lmhead --steps 3 --warmup 1 --no-cpu-baseline",
+           "#   rocprofv3 --pmc WRITE_SIZE -d DIR/pmc_WRITE_SIZE -o p --output-format csv -- "
+           "python3 bench.py --verify lmhead --steps 3 --warmup 1 --no-cpu-baseline",
+           "# Counter values are KiB per dispatch, scaled by the plain-copy factors of the attention traffic",
+           "# summary (the same counters on a 1 GiB device copy).",
+           f"copy_scale_fetch = {f_fetch:.4f}",
+           f"copy_scale_write = {f_write:.4f}"]
+    total = 0.0
+    for mt, what in ((9, "ar_pass"), (7, "draft_pass")):
+        key = f"lmhead_argmax_kernel<{mt}, true>"
+        res = {}
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            vals = [float(r["Counter_Value"]) for r in
+                    _csv_rows(os.path.join(dirname, f"pmc_{counter}", "*counter_collection.csv"))
+                    if key in r["Kernel_Name"]]
+            res[counter] = statistics.mean(vals)
+        hbm = res["FETCH_SIZE"] * 1024 * f_fetch + res["WRITE_SIZE"] * 1024 * f_write
+        total += hbm
+        out += [f"{what}_fetch_kib = {res['FETCH_SIZE']:.1f}", f"{what}_write_kib = {res['WRITE_SIZE']:.1f}",
+                f"{what}_hbm_bytes = {hbm:.0f}"]
+    out += [f"hbm_bytes_per_verify = {total:.0f}", f"kernel_source_sha = {lmhead_source_sha()}", ""]
+    with open(LM_TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(out))
+    print("\n".join(out))
 
 
 def step_bytes(shape, V, accept, verify_kind="greedy", d_model=0):
@@ -498,6 +552,9 @@ def main():
     if args.summarize:
         summarize(args.summarize)
         return
+    if args.summarize_lmhead:
+        summarize_lmhead(args.summarize_lmhead)
+        return
     if args.workload == "train_8b":
         bench_train(args)
         return
@@ -749,7 +806,9 @@ def main():
                               "kernel": "tidar_lmhead_verify_greedy" + ("_packed" if packed_w else ""),
                               "achieved": round(lm_gbps, 2),
                               "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(lm_gbps / HBM_PEAK_GBPS, 4),
-                              "traffic": None, "algorithmic_bytes": ver_b}
+                              "traffic": (read_traffic(LM_TRAFFIC_FILE, lmhead_source_sha, "hbm_bytes_per_verify")
+                                          if packed_w and wl.name == "step_8b" else None),
+                              "algorithmic_bytes": ver_b}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, d, v, a_planted, args)
     print(json.dumps(result))
