@@ -531,6 +531,7 @@ def bench_loop(args, wl, d, v, a_planted, reps, n_rep, attention, verify_commit,
         "attention_gbps_mean": round(attn_gbps, 2),
         "attention_hbm_frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
         "attention_tflops_mean": round(sum(flops) / (attn_ms.sum() * 1e-3) / 1e12, 2),
+        "attention_mfma_frac": round(sum(flops) / (attn_ms.sum() * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": {"bound": "hbm", "kernel": "tidar_step_attention", "achieved": round(attn_gbps, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None, "algorithmic_bytes": int(np.mean(attn_b))},
@@ -790,6 +791,7 @@ def main():
         "achievable_read_gbps": round(read_gbps, 1),
         "attention_achievable_frac": round(attn_gbps / read_gbps, 4),
         "attention_tflops": round((flops + flops_step) / (attn_ms_mean * 1e-3) / 1e12, 2),
+        "attention_mfma_frac": round((flops + flops_step) / (attn_ms_mean * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "verify_commit_us": round((step_ms - attn_ms_mean) * 1e3, 2),
         "roofline": {"bound": "hbm", "kernel": "tidar_step_attention", "achieved": round(attn_gbps, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
