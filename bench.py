@@ -61,7 +61,7 @@ HBM_PEAK_GBPS = 8000.0
 COPY_CALIB_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_step_8b_traffic.txt")
 ATTN_SOURCES = [os.path.join(ROOT, "diffusion_drafted_self_amd", "csrc", n)
-                for n in ("attention.hip", "common.h", "launch.h", "lds_dma.h")]
+                for n in ("attention.hip", "attention_pp.hip", "attn_tile.h", "common.h", "launch.h", "lds_dma.h")]
 LM_SOURCES = [os.path.join(ROOT, "diffusion_drafted_self_amd", "csrc", n)
               for n in ("lmhead.hip", "common.h", "launch.h", "lds_dma.h")]
 LM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_verify_8b_traffic.txt")
@@ -78,6 +78,9 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--kv-chunk", type=int, default=0, help="key positions per attention chunk (0: library plan)")
     p.add_argument("--summarize", metavar="DIR", help="write profiles/ summaries from rocprofv3 outputs in DIR")
+    p.add_argument("--summarize-counters", metavar="DIR",
+                   help="write the attention counter summary of --workload from the passes under DIR")
+    p.add_argument("--counters-kernel", default="", help="TIDAR_ATTN_KERNEL value the counter runs used")
     p.add_argument("--summarize-lmhead", metavar="DIR",
                    help="write the fused LM head's traffic summary from FETCH_SIZE / WRITE_SIZE runs in DIR")
     p.add_argument("--verify", default="greedy", choices=["greedy", "sample", "lmhead"])
@@ -199,6 +202,24 @@ def step_bytes(shape, V, accept, verify_kind="greedy", d_model=0):
     return attn, verify, commit, kv_prefix + kv_step, flops
 
 
+def attention_roofline(attn_bytes, attn_flops, attn_ms, traffic):
+    """Roofline entry of the step-attention kernel: against HBM when its
+    arithmetic intensity (flops per algorithmic byte) is below the ridge of
+    the dense bf16 MFMA peak over the HBM peak (2500 TFLOP/s / 8 TB/s =
+    312.5 flop/B), against the MFMA peak above it."""
+    ai = attn_flops / attn_bytes
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    gbps = attn_bytes / (attn_ms * 1e-3) / 1e9
+    tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    common = {"kernel": "tidar_step_attention", "traffic": traffic, "algorithmic_bytes": int(attn_bytes),
+              "algorithmic_flops": int(attn_flops), "arithmetic_intensity": round(ai, 1), "ridge": round(ridge, 1)}
+    if ai > ridge:
+        return dict(bound="mfma", achieved=round(tflops, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), **common)
+    return dict(bound="hbm", achieved=round(gbps, 2), peak=HBM_PEAK_GBPS, unit="GB/s",
+                frac=round(gbps / HBM_PEAK_GBPS, 4), **common)
+
+
 def visible_step_pairs(k, n_groups):
     """Visible (row, step key) pairs of the step block: candidates k(k+1)/2,
     group g: k*(g+1) own-candidate + k*k own-group entries."""
@@ -285,6 +306,77 @@ def summarize(dirname):
         f.write("\n".join(out))
     print("\n".join(lines))
     print("\n".join(out))
+
+
+# Counter passes of the attention kernel (one rocprofv3 --pmc run each, at
+# most 8 SQ counters and GRBM_GUI_ACTIVE per pass).
+COUNTER_PASSES = {
+    "busy": ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CU_CYCLES",
+             "GRBM_GUI_ACTIVE"],
+    "insts": ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE"],
+    "lds": ["SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "GRBM_GUI_ACTIVE"],
+    "wait": ["SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", "SQ_LDS_DATA_FIFO_FULL", "GRBM_GUI_ACTIVE"],
+}
+N_CU, N_XCD, N_SIMD = 256, 8, 4
+
+
+def summarize_counters(dirname, workload, kernel_env):
+    """Derived utilisation figures of the step-attention kernel from the
+    counter passes under dirname/pmc_<pass>/; written under profiles/."""
+    import statistics
+    vals, durs = {}, []
+    for pas, names in COUNTER_PASSES.items():
+        for r in _csv_rows(os.path.join(dirname, f"pmc_{pas}", "*counter_collection.csv")):
+            if "attn_" not in r["Kernel_Name"] or "merge" in r["Kernel_Name"]:
+                continue
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            if pas == "busy" and r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                durs.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+            kname = r["Kernel_Name"]
+    m = {k: statistics.mean(v) for k, v in vals.items()}
+    gui = m["GRBM_GUI_ACTIVE"] / N_XCD  # cycles per XCD (the counter sums the XCDs)
+    simd_cycles = gui * N_CU * N_SIMD
+    dur_us = statistics.mean(durs) if durs else float("nan")
+    mfma_busy = m["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles
+    rows = [
+        ("kernel", kname.split("(")[0].replace("(anonymous namespace)::", "")),
+        ("dispatches averaged", len(durs)),
+        ("duration under counters, us", f"{dur_us:.2f}"),
+        ("GRBM_GUI_ACTIVE per XCD, cycles", f"{gui:.0f}"),
+        ("shader clock over the dispatch, MHz (cycles / duration)", f"{gui / dur_us:.0f}"),
+        ("MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (cycles x CUs x 4))", f"{100 * mfma_busy:.1f} %"),
+        ("MFMA busy cycles with VALU co-issue (COEXEC / MFMA_BUSY)",
+         f"{100 * m['SQ_VALU_MFMA_COEXEC_CYCLES'] / m['SQ_VALU_MFMA_BUSY_CYCLES']:.1f} %"),
+        ("VALU active (SQ_ACTIVE_INST_VALU / (cycles x CUs))",
+         f"{100 * m['SQ_ACTIVE_INST_VALU'] / (gui * N_CU):.1f} %"),
+        ("CU busy (SQ_BUSY_CU_CYCLES x 4 / (cycles x CUs))", f"{100 * 4 * m['SQ_BUSY_CU_CYCLES'] / (gui * N_CU):.1f} %"),
+        ("LDS active (SQ_LDS_IDX_ACTIVE / (cycles x CUs))", f"{100 * m['SQ_LDS_IDX_ACTIVE'] / (gui * N_CU):.1f} %"),
+        ("LDS bank-conflict cycles / LDS active cycles",
+         f"{100 * m['SQ_LDS_BANK_CONFLICT'] / max(m['SQ_LDS_IDX_ACTIVE'], 1):.2f} %"),
+        ("wave-cycles waiting for LDS issue / wave cycles",
+         f"{100 * 4 * m['SQ_WAIT_INST_LDS'] / max(m['SQ_WAVE_CYCLES'], 1):.1f} %"),
+        ("wave-cycles waiting for any issue / wave cycles",
+         f"{100 * 4 * m['SQ_WAIT_INST_ANY'] / max(m['SQ_WAVE_CYCLES'], 1):.1f} %"),
+        ("LDS data FIFO full / (cycles x CUs)", f"{100 * m['SQ_LDS_DATA_FIFO_FULL'] / (gui * N_CU):.1f} %"),
+        ("instructions per dispatch: VALU / MFMA / LDS",
+         f"{m['SQ_INSTS_VALU']:.3e} / {m['SQ_INSTS_MFMA']:.3e} / {m['SQ_INSTS_LDS']:.3e}"),
+        ("bf16 MFMA flops per dispatch (MOPS x 512)", f"{m['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.4e}"),
+    ]
+    cmd = (f"{'TIDAR_ATTN_KERNEL=' + kernel_env + ' ' if kernel_env else ''}rocprofv3 --pmc <pass counters> "
+           f"-d DIR/pmc_<pass> -o p --output-format csv -- python3 bench.py --workload {workload} "
+           "--steps 3 --warmup 1 --no-cpu-baseline")
+    lines = [f"# Counters of the step-attention kernel, workload {workload}"
+             + (f" (TIDAR_ATTN_KERNEL={kernel_env})" if kernel_env else " (library plan)"), "",
+             f"Command (from the repository root, MI355X), one run per pass: `{cmd}`", "",
+             "Passes: " + "; ".join(f"`{p}`: {', '.join(c)}" for p, c in COUNTER_PASSES.items()), "",
+             "| figure | value |", "|---|---|"] + [f"| {a} | {b} |" for a, b in rows] + [
+             "", "Raw means per dispatch:", ""] + [f"- {k} = {v:.6g}" for k, v in sorted(m.items())] + [
+             "", f"kernel_source_sha = {attention_source_sha()}", ""]
+    tag = workload + (f"_{kernel_env}" if kernel_env else "")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"attention_{tag}_counters.md"), "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
 
 
 def cpu_baseline(wl, d, v, a_planted, args):
@@ -513,7 +605,7 @@ def bench_loop(args, wl, d, v, a_planted, reps, n_rep, attention, verify_commit,
     step_gbps = sum(step_b) / (total_ms * 1e-3) / 1e9
     attn_gbps = sum(attn_b) / (attn_ms.sum() * 1e-3) / 1e9
     result = {
-        "metric": METRIC, "value": round(step_gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": N,
+        "metric": METRIC, "value": round(attn_gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": N,
         "warmup": args.warmup, "ms_per_step": round(total_ms / N, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name + "_loop", "batch": s.B, "q_heads": s.Hq, "kv_heads": s.Hkv,
@@ -521,6 +613,7 @@ def bench_loop(args, wl, d, v, a_planted, reps, n_rep, attention, verify_commit,
                    "prefix_end_mean": float(lens_h.mean()), "k": s.k, "draft_groups": s.n_groups,
                    "step_rows": s.R, "vocab": wl.V, "accept": wl.accept, "verify": "greedy",
                    "kv_layout": "contiguous", "input_replicas": n_rep},
+        "step_gbps": round(step_gbps, 2),
         "step_us_mean": round(total_ms / N * 1e3, 2),
         "step_us_p50": round(float(np.percentile(step_ms, 50)) * 1e3, 2),
         "step_us_p99": round(float(np.percentile(step_ms, 99)) * 1e3, 2),
@@ -532,9 +625,7 @@ def bench_loop(args, wl, d, v, a_planted, reps, n_rep, attention, verify_commit,
         "attention_hbm_frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
         "attention_tflops_mean": round(sum(flops) / (attn_ms.sum() * 1e-3) / 1e12, 2),
         "attention_mfma_frac": round(sum(flops) / (attn_ms.sum() * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-        "roofline": {"bound": "hbm", "kernel": "tidar_step_attention", "achieved": round(attn_gbps, 2),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "algorithmic_bytes": int(np.mean(attn_b))},
+        "roofline": attention_roofline(sum(attn_b) / N, sum(flops) / N, attn_ms.sum() / N, None),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, d, v, a_planted, args)
@@ -552,6 +643,9 @@ def main():
         return
     if args.summarize:
         summarize(args.summarize)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload, args.counters_kernel)
         return
     if args.summarize_lmhead:
         summarize_lmhead(args.summarize_lmhead)
@@ -765,7 +859,7 @@ def main():
     traffic = read_traffic()
     result = {
         "metric": METRIC,
-        "value": round(step_gbps, 2),
+        "value": round(attn_gbps, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
@@ -781,6 +875,7 @@ def main():
                    "accept": wl.accept if args.verify == "greedy" else "sampled", "verify": args.verify,
                    "kv_layout": "paged" if args.paged else "contiguous",
                    "cold_replicas": n_rep},
+        "step_gbps": round(step_gbps, 2),
         "step_us": round(step_ms * 1e3, 2),
         "step_us_graph": round(graph_ms * 1e3, 2) if graph_ms is not None else None,
         "attention_us": round(attn_ms_mean * 1e3, 2),
@@ -793,9 +888,8 @@ def main():
         "attention_tflops": round((flops + flops_step) / (attn_ms_mean * 1e-3) / 1e12, 2),
         "attention_mfma_frac": round((flops + flops_step) / (attn_ms_mean * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "verify_commit_us": round((step_ms - attn_ms_mean) * 1e3, 2),
-        "roofline": {"bound": "hbm", "kernel": "tidar_step_attention", "achieved": round(attn_gbps, 2),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "algorithmic_bytes": attn_b},
+        "roofline": attention_roofline(attn_b, flops + flops_step, attn_ms_mean,
+                                       traffic if wl.name == "step_8b" and not args.paged else None),
     }
     if args.verify == "lmhead":
         lm_ms = sum(ev_a[i][1].elapsed_time(ev_v[i]) for i in range(K)) / K

@@ -40,6 +40,7 @@ SIGNATURES = {
     "tidar_strerror": (ctypes.c_char_p, [_c_int]),
     "tidar_abi_version": (_c_int, []),
     "tidar_step_attention_workspace": (_c_int, [_c_int] * 10 + [ctypes.POINTER(_c_size)]),
+    "tidar_step_attention_plan": (_c_int, [_c_int] * 10 + [ctypes.POINTER(_c_int)]),
     "tidar_step_attention": (_c_int, [_c_int] * 9 + [_f, _c_int] + [_p] * 9 + [_c_size, _p]),
     "tidar_verify_workspace": (_c_int, [_c_int] * 3 + [ctypes.POINTER(_c_size)]),
     "tidar_verify_greedy": (_c_int, [_c_int] * 3 + [_p] * 6 + [_c_size, _p]),
@@ -158,6 +159,19 @@ def step_attention_workspace_bytes(dtype_code: int, B: int, Hq: int, Hkv: int, D
            lib().tidar_step_attention_workspace(dtype_code, B, Hq, Hkv, D, S_max, max_len, k, n_groups,
                                                kv_chunk, ctypes.byref(n)))
     return n.value
+
+
+PLAN_KERNELS = {0: "four_wave", 1: "eight_wave", 2: "f32"}
+
+
+def step_attention_plan(dtype_code: int, B: int, Hq: int, Hkv: int, D: int, S_max: int, max_len: int, k: int,
+                        n_groups: int, kv_chunk: int = 0) -> dict:
+    """The launch plan of tidar_step_attention for these arguments (host only)."""
+    arr = (_c_int * 6)()
+    _check("tidar_step_attention_plan",
+           lib().tidar_step_attention_plan(dtype_code, B, Hq, Hkv, D, S_max, max_len, k, n_groups, kv_chunk, arr))
+    return {"kernel": PLAN_KERNELS[arr[0]], "tiles_per_wave": arr[1], "shared_tiles": arr[2],
+            "row_blocks": arr[3], "chunk": arr[4], "chunks": arr[5]}
 
 
 def step_attention(q, k_step, v_step, k_cache, v_cache, lens, k: int, n_groups: int, sm_scale: float,

@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "launch.h"
@@ -25,7 +26,7 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 long cdiv(long a, long b) { return (a + b - 1) / b; }
 
 struct AttnPlan {
-  int R, G, M, n16, nf, ns, n_rowblk, chunk, n_split;
+  int R, G, M, n16, nf, ns, n_rowblk, chunk, n_split, pp;
   size_t o_bytes, ml_bytes, total;
 };
 
@@ -49,6 +50,25 @@ struct AttnPlan {
 //
 // f32: one wave per query row and chunk, chunks of at most kMaxChunkF32.
 double body_clk(int nf, int ns) { return 700.0 + 400.0 * nf + 300.0 * ns; }
+
+// The eight-wave kernel (two waves per SIMD, head dim 128): one tile per
+// wave and at most one tile shared by the four SIMDs, so a workgroup takes
+// at most nine tiles.  Per 64-key tile it costs the two waves' MFMA
+// clusters of a SIMD (2 x 36 MFMAs of ~16 clocks) plus what of the softmax
+// and load issue they do not hide.
+double body_clk_pp(int ns) { return 1400.0 + 150.0 * ns; }
+
+// Which step-attention kernel the planner may choose: both (default), or
+// one of them when TIDAR_ATTN_KERNEL is "pp" (eight waves) or "pipe" (four
+// waves), for measurements and tests of one against the other.  Read at
+// every plan, so a process can switch between calls.
+int kernel_choice() {
+  const char* e = std::getenv("TIDAR_ATTN_KERNEL");
+  if (!e) return 0;
+  if (!std::strcmp(e, "pp")) return 1;
+  if (!std::strcmp(e, "pipe")) return 2;
+  return 0;
+}
 
 bool shape_built(int nf, int ns) {
   if (nf < 0 || nf > 3 || ns < 0 || ns > 3 || nf + ns == 0) return false;
@@ -77,6 +97,7 @@ int plan_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_
     p->chunk = kv_chunk ? kv_chunk : (int)std::min<long>(kMaxChunkF32, (long)round_up(keys, kTileKeys));
     p->nf = 1;
     p->ns = 0;
+    p->pp = 0;
     p->n_rowblk = 1;
   } else {
     const long n_key_tiles = cdiv(keys, kTileKeys);
@@ -84,8 +105,10 @@ int plan_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_
     const double hbm_clk = (double)pairs * keys * D * 4 / 6.0e6 * kClkPerUs;  // K+V bytes at ~6 TB/s
     double best = 1e300;
     long best_chunk = 0;
-    int best_wr = 1, best_nf = 1, best_ns = 0;
+    int best_wr = 1, best_nf = 1, best_ns = 0, best_pp = 0;
     long best_wgs = 0;
+    const bool allow_pp = D == 128 && kernel_choice() != 2;
+    const bool allow_pipe = !(allow_pp && kernel_choice() == 1);
     const long ns_max = kv_chunk ? 1 : std::min<long>(n_key_tiles, 64);
     for (long ns_try = 1; ns_try <= ns_max; ++ns_try) {
       const long chunk = kv_chunk ? kv_chunk : (long)round_up(cdiv(keys, ns_try), kTileKeys);
@@ -94,13 +117,15 @@ int plan_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_
       const long kt = cdiv(chunk, kTileKeys) + 1;  // + the step tile staged through registers
       for (int wr = 1; wr <= p->n16; ++wr) {
         const int t_max = (int)cdiv(p->n16, wr);
-        const int layouts[2][2] = {{t_max / 4, t_max % 4}, {(int)cdiv(t_max, 4), 0}};
+        // (full tiles per wave, shared tiles, eight-wave kernel)
+        const int layouts[3][3] = {{t_max / 4, t_max % 4, 0}, {(int)cdiv(t_max, 4), 0, 0}, {1, t_max > 8, 1}};
         for (const auto& lay : layouts) {
-          const int nf = lay[0], nsh = lay[1];
-          if (!shape_built(nf, nsh)) continue;
+          const int nf = lay[0], nsh = lay[1], pp = lay[2];
+          if (pp ? (!allow_pp || t_max > 9) : (!allow_pipe || !shape_built(nf, nsh))) continue;
           const long wgs = pairs * wr * ns;
           const long rounds = cdiv(wgs, kCUs);
-          double cost = std::max((double)rounds * body_clk(nf, nsh) * kt, hbm_clk) + 20000.0 * rounds;
+          const double body = pp ? body_clk_pp(nsh) : body_clk(nf, nsh);
+          double cost = std::max((double)rounds * body * kt, hbm_clk) + 20000.0 * rounds;
           if (ns > 1) cost += (14.0 + (double)pairs * ns * p->M * (D * 4 + 8) * 2 / 5.0e6) * kClkPerUs;
           const bool better = cost < best * 0.999 || (cost <= best * 1.001 && wgs > best_wgs && wgs <= rounds * kCUs);
           if (better) {
@@ -109,21 +134,25 @@ int plan_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_
             best_wr = wr;
             best_nf = nf;
             best_ns = nsh;
+            best_pp = pp;
             best_wgs = wgs;
           }
         }
       }
     }
+    if (best_chunk == 0) return TIDAR_EUNSUPPORTED;  // no built layout fits
     p->chunk = (int)best_chunk;
     p->nf = best_nf;
     p->ns = best_ns;
+    p->pp = best_pp;
     p->n_rowblk = best_wr;
   }
   p->n_split = (int)cdiv(keys, p->chunk);
 
   const long blocks = pairs * p->n_split * (dtype == TIDAR_F32 ? p->M : p->n_rowblk);
   if (blocks > 0x7fffffffL) return TIDAR_EUNSUPPORTED;
-  if (dtype == TIDAR_BF16 && !shape_built(p->nf, p->ns)) return TIDAR_EUNSUPPORTED;
+  if (dtype == TIDAR_BF16 && !p->pp && !shape_built(p->nf, p->ns)) return TIDAR_EUNSUPPORTED;
+  if (p->pp && (p->ns > 1 || cdiv(p->n16, p->n_rowblk) > 8 + p->ns)) return TIDAR_EUNSUPPORTED;
 
   // workspace: [partial outputs][partial (max, sum)]; none is needed when
   // every sequence fits one chunk (bf16 path)
@@ -159,9 +188,11 @@ struct LmPlan {
 int plan_lmhead(int B, int k, int V, int d, bool packed, LmPlan* p) {
   if (k > kMaxK) return TIDAR_EUNSUPPORTED;
   if (B < 0 || k < 1 || V < 1 || d < 64 || d % 64 != 0) return TIDAR_EINVAL;
-  // direct loads address the hidden rows, and a row-major W, with 32-bit
-  // byte offsets (a packed W from the start of each chunk's tiles)
-  if ((!packed && (double)V * d * 2 >= 4294967296.0) || (double)B * k * k * d * 2 >= 4294967296.0)
+  // direct loads address the hidden rows of either pass (B*(k+1) AR rows,
+  // B*k*k draft rows), and a row-major W, with 32-bit byte offsets (a
+  // packed W from the start of each chunk's tiles)
+  if ((!packed && (double)V * d * 2 >= 4294967296.0) ||
+      (double)B * std::max(k + 1, k * k) * d * 2 >= 4294967296.0)
     return TIDAR_EUNSUPPORTED;
   p->n_chunks = (int)cdiv(V, tidar::kLmChunk);
   if (cdiv((long)B * (k + 1), tidar::kLmRows) > 65535) return TIDAR_EUNSUPPORTED;
@@ -236,6 +267,7 @@ int step_attention_impl(int dtype, int B, int Hq, int Hkv, int D, int S_max, int
   a.nf = p.nf;
   a.ns = p.ns;
   a.n_rowblk = p.n_rowblk;
+  a.pp = p.pp;
   a.scale_log2 = sm_scale * 1.44269504088896340736f;
   a.single_chunk_direct = dtype == TIDAR_BF16;
   a.block_table = block_table;
@@ -252,6 +284,9 @@ int kv_commit_impl(int dtype, int B, int Hkv, int D, int S_max, int R, int k, vo
                    const void* v_step, const int32_t* accept_len, int32_t* err_flags, void* stream) {
   if (dtype != TIDAR_BF16 && dtype != TIDAR_F32) return TIDAR_EUNSUPPORTED;
   if (D != 64 && D != 128) return TIDAR_EUNSUPPORTED;
+  // at most kMaxK (< 64) accepted rows: their positions span at most two
+  // 64-position pages, the two the paged commit resolves
+  if (k > kMaxK) return TIDAR_EUNSUPPORTED;
   if (B < 0 || Hkv < 1 || S_max < 1 || S_max % kValuePage != 0 || R < 1 || k < 1 || k > R) return TIDAR_EINVAL;
   if (B == 0) return TIDAR_OK;
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_step, 16) || !aligned(v_step, 16) ||
@@ -305,6 +340,21 @@ int tidar_step_attention_workspace(int dtype, int B, int Hq, int Hkv, int D, int
   const int st = plan_attention(dtype, B, Hq, Hkv, D, S_max, max_len, k, n_groups, kv_chunk, &p);
   if (st != TIDAR_OK) return st;
   *bytes = p.total;
+  return TIDAR_OK;
+}
+
+int tidar_step_attention_plan(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_len,
+                              int k, int n_groups, int kv_chunk, int* plan) {
+  if (!plan) return TIDAR_EINVAL;
+  AttnPlan p;
+  const int st = plan_attention(dtype, B, Hq, Hkv, D, S_max, max_len, k, n_groups, kv_chunk, &p);
+  if (st != TIDAR_OK) return st;
+  plan[0] = dtype == TIDAR_F32 ? 2 : p.pp;
+  plan[1] = p.nf;
+  plan[2] = p.ns;
+  plan[3] = p.n_rowblk;
+  plan[4] = p.chunk;
+  plan[5] = p.n_split;
   return TIDAR_OK;
 }
 

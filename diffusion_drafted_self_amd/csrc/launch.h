@@ -26,6 +26,8 @@ struct AttnArgs {
   int chunk, n_split;
   int n16, nf, ns, n_rowblk;  // bf16 path: 16-row tiles of (b, kvh); per workgroup, full tiles per
                               // wave and tiles shared by key block; workgroups per (b, kvh)
+  int pp;                     // bf16 path: the eight-wave (two per SIMD) kernel, one tile per wave
+                              // plus ns (0 or 1) shared tile; nf is then 1
   float scale_log2;     // sm_scale * log2(e)
   int single_chunk_direct;  // the split kernel writes sequences that fit one chunk (bf16 path)
   // paged caches (bf16 path): k_cache / v_cache are pools of n_pages pages,
@@ -38,6 +40,7 @@ struct AttnArgs {
 };
 
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention_pp_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t s);
 hipError_t launch_train_attention_bf16(const AttnArgs& a, hipStream_t s);
 
@@ -54,6 +57,41 @@ struct VerifyArgs {
 };
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
+
+// Greedy verification fused with the KV commit (or without it): two
+// launches over per-row 64-bit argmax keys and per-sequence arrival counters
+// that every call leaves zeroed.
+struct FusedVerifyArgs {
+  const float* ar_logits;     // [B][k+1][V]
+  const float* draft_logits;  // [B][k][k][V]
+  const int32_t* cand;        // [B][k]
+  int32_t* accept_len;        // [B]
+  int32_t* next_cand;         // [B][k]
+  unsigned long long* key;    // [B*(k+1)]          state
+  unsigned long long* dkey;   // [B*n_draft_rows]   state
+  unsigned* cnt;              // [B]                state
+  int B, k, V, n_draft_rows;  // n_draft_rows = max(k-1, 1)
+  // commit (commit != 0)
+  int commit;
+  void* k_cache;
+  void* v_cache;
+  int32_t* lens;
+  const void* k_step;
+  const void* v_step;
+  int32_t* err_flags;
+  int Hkv, D, S_max, R, elem_bytes;
+  const int32_t* block_table;  // paged pools (S_max = 64 * max_pages), or nullptr
+  int max_pages, n_pages;
+};
+
+// Launch shapes of the fused path (the host checks them before launching).
+struct FusedVerifyGeometry {
+  int ar_grid_x, ar_grid_y;        // (chunks, AR rows)
+  int draft_grid_x, draft_grid_y;  // (chunks, sequences x draft rows)
+  int draft_rows, block;
+};
+FusedVerifyGeometry fused_verify_geometry(int B, int k, int V);
+hipError_t launch_fused_verify(const FusedVerifyArgs& a, hipStream_t s);
 hipError_t launch_verify_select(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_draft_finalize(const VerifyArgs& a, hipStream_t s);
 

@@ -20,6 +20,7 @@
 #include <algorithm>
 #include <climits>
 
+#include "argmax_block.h"
 #include "common.h"
 #include "launch.h"
 
@@ -29,8 +30,6 @@ namespace {
 
 template <bool DRAFT>
 __global__ __launch_bounds__(256) void argmax_partial_kernel(VerifyArgs a) {
-  __shared__ float sv[4];
-  __shared__ int si[4];
   const int chunk = blockIdx.x;
   const int row = blockIdx.y;
   const float* src;
@@ -47,73 +46,10 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(VerifyArgs a) {
   }
   const int lo = chunk * a.chunk_elems;
   const int hi = min(a.V, lo + a.chunk_elems);
-  float bv = -INFINITY;
-  int bi = INT_MAX;
-  auto take = [&](float x, int i) {
-    if (x > bv) {
-      bv = x;
-      bi = i;
-    }
-  };
-  if (a.chunk_elems == kArgmaxChunk) {
-    // every load of the thread first (their latencies overlap; nontemporal:
-    // each logit is read once), then the compares in ascending index order
-    // (strict '>' keeps the lowest index)
-    if ((a.V & 3) == 0) {
-      floatx4 x[kArgmaxChunk / 1024];
-#pragma unroll
-      for (int j = 0; j < kArgmaxChunk / 1024; ++j) {
-        const int i = lo + 4 * (int)threadIdx.x + 1024 * j;
-        x[j] = i < hi ? __builtin_nontemporal_load((const floatx4*)(src + i))
-                      : (floatx4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      }
-#pragma unroll
-      for (int j = 0; j < kArgmaxChunk / 1024; ++j) {
-        const int i = lo + 4 * (int)threadIdx.x + 1024 * j;
-        take(x[j].x, i);
-        take(x[j].y, i + 1);
-        take(x[j].z, i + 2);
-        take(x[j].w, i + 3);
-      }
-    } else {
-      float x[kArgmaxChunk / 256];
-#pragma unroll
-      for (int j = 0; j < kArgmaxChunk / 256; ++j) {
-        const int i = lo + (int)threadIdx.x + 256 * j;
-        x[j] = i < hi ? __builtin_nontemporal_load(src + i) : -INFINITY;
-      }
-#pragma unroll
-      for (int j = 0; j < kArgmaxChunk / 256; ++j) take(x[j], lo + (int)threadIdx.x + 256 * j);
-    }
-  } else if ((a.V & 3) == 0) {
-    for (int i = lo + 4 * (int)threadIdx.x; i < hi; i += 4 * 256) {
-      const float4 x = *(const float4*)(src + i);
-      if (x.x > bv) { bv = x.x; bi = i; }
-      if (x.y > bv) { bv = x.y; bi = i + 1; }
-      if (x.z > bv) { bv = x.z; bi = i + 2; }
-      if (x.w > bv) { bv = x.w; bi = i + 3; }
-    }
-  } else {
-    for (int i = lo + (int)threadIdx.x; i < hi; i += 256) {
-      const float x = src[i];
-      if (x > bv) { bv = x; bi = i; }
-    }
-  }
-  argmax_wave(bv, bi);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) {
-    sv[wave] = bv;
-    si[wave] = bi;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < 4; ++w)
-      if (argmax_better(sv[w], si[w], bv, bi)) {
-        bv = sv[w];
-        bi = si[w];
-      }
-    *dst = make_float2(bv, __int_as_float(bi));
-  }
+  float bv;
+  int bi;
+  block_chunk_argmax(src, lo, hi, a.V, a.chunk_elems, bv, bi);
+  if (threadIdx.x == 0) *dst = make_float2(bv, __int_as_float(bi));
 }
 
 // One wave per row: the wave reduces that row's chunk results (one round

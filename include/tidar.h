@@ -112,6 +112,20 @@ int tidar_abi_version(void);
 int tidar_step_attention_workspace(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_len,
                                    int k, int n_groups, int kv_chunk, size_t* bytes);
 
+/* The launch plan tidar_step_attention would use for these arguments (a
+ * host-only query, nothing is enqueued): plan[0] kernel (0: four waves per
+ * workgroup, one per SIMD; 1: eight waves, two per SIMD; 2: the f32
+ * kernel), plan[1] full 16-row tiles per wave, plan[2] tiles shared by the
+ * waves of a workgroup, plan[3] workgroups per (sequence, KV head) over the
+ * rows, plan[4] key positions per chunk, plan[5] chunks.  `plan` is a host
+ * array of 6 ints owned by the caller.  Returns the status the workspace
+ * query returns for the same arguments.  The environment variable
+ * TIDAR_ATTN_KERNEL ("pp" for the eight-wave kernel, "pipe" for the
+ * four-wave one; read at every call) restricts the choice, for tests and
+ * measurements that compare the two. */
+int tidar_step_attention_plan(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_len,
+                              int k, int n_groups, int kv_chunk, int* plan);
+
 int tidar_step_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_len,
                          int k, int n_groups, float sm_scale, int kv_chunk,
                          const void* q, const void* k_step, const void* v_step,

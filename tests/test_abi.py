@@ -115,6 +115,10 @@ def test_commit_validation(T):
     assert L.tidar_kv_commit(0, 2, 8, 128, 60, 72, 8, p, p, p, p, p, p, None, None) == -1
     assert L.tidar_kv_commit(0, 2, 8, 128, 64, 72, 8, p, None, p, p, p, p, None, None) == -1
     assert L.tidar_kv_commit(0, 0, 8, 128, 64, 72, 8, None, None, None, None, None, None, None, None) == 0
+    # k above 16: more accepted rows than the two 64-position pages the paged
+    # commit resolves could hold; refused by both forms even where k <= R
+    assert L.tidar_kv_commit(0, 2, 8, 128, 4096, 400, 17, p, p, p, p, p, p, None, None) == -2
+    assert L.tidar_kv_commit_paged(0, 2, 8, 128, 64, 100, 400, 17, p, p, p, p, p, p, p, None, None) == -2
 
 
 def test_verify_sample_validation_and_size(T):
@@ -204,6 +208,10 @@ def test_lmhead_validation_and_size(T):
         assert f(2, 4, 1000, 64, p, None, p, p, p, p, p, 1 << 20, None) == -1
         assert f(0, 4, 1000, 64, None, None, None, None, None, None, None, 0, None) == 0
     assert L.tidar_lmhead_verify_greedy(1, 1, 600000, 4096, p, p, p, p, p, p, p, 1 << 30, None) == -2
+    # k = 1: the AR pass addresses B*(k+1)*d*2 bytes of hidden rows, twice the
+    # draft rows' B*k*k*d*2; the 32-bit offset bound takes the larger
+    assert L.tidar_lmhead_verify_workspace(200000, 1, 1000, 4096, ctypes.byref(n)) == 0   # 3.3e9 B
+    assert L.tidar_lmhead_verify_workspace(300000, 1, 1000, 4096, ctypes.byref(n)) == -2  # 4.9e9 B
     assert L.tidar_lmhead_verify_greedy_packed(1, 1, 600000, 4096, p, p, p, p, p, p, p, 8, None) == -3
 
 
