@@ -47,6 +47,7 @@ namespace {
 
 constexpr int PPW = 8;         // waves per workgroup, two per SIMD
 constexpr int PPT = PPW * 64;  // threads per workgroup
+constexpr int kPpDepth = 12;   // LDS operand reads in flight per wave in the MFMA phase
 
 // s_waitcnt vmcnt(n) for a wave-uniform n that is not a compile-time
 // constant (the load counts of the last ring steps).
@@ -112,42 +113,38 @@ __device__ __forceinline__ void pp_pv(const lds_char* sV, const bf16x8 (&p)[2], 
 
 // The C phase of the pipelined loop: S(j) from slot sK, then P.V of the
 // previous tile from slot sV, as one fixed sequence of steps.  Each step
-// issues one MFMA of the wave's tile on one LDS operand and reads the
-// operand DEPTH steps ahead; the shared tile's MFMAs ride on the steps of
-// block `simd` (group 0, scores) or of head-dim blocks 2s, 2s+1 (group 1,
-// P.V), with their own operand reads.
-template <int D, int GRP, bool SH, bool DO_S, bool DO_PV>
+// reads one LDS operand and issues the MFMA that consumes it; the operand of
+// the step DEPTH ahead is requested first, so DEPTH reads are in flight
+// (what bounds the phase is the LDS reads' round trip, not their
+// bandwidth).  The shared tile's MFMAs are steps of their own, with their
+// own operand reads: after the four key blocks of each head-dim step, block
+// `simd` again against the shared tile's Q (group 0); after the eight
+// head-dim blocks of each key step, head-dim blocks 2s and 2s+1 again
+// against the shared tile's P^T, read from LDS (group 1).
+template <int D, int GRP, bool SH, bool DO_S, bool DO_PV, int DEPTH>
 __device__ __forceinline__ void pp_c_phase(const lds_char* sK, const lds_char* sV, const lds_char* sP,
                                            const bf16x8 (&q)[D / 32], const bf16x8 (&qs)[D / 32], floatx4 (&s)[4],
                                            floatx4& ss, const bf16x8 (&p)[2], PpState<D>& st, int lane, int simd) {
-  constexpr int NSS = DO_S ? (D / 32) * 4 : 0;
-  constexpr int NPS = DO_PV ? 2 * (D / 16) : 0;
-  constexpr int NSTEP = NSS + NPS;
-  constexpr int DEPTH = 6;
   constexpr bool SH_S = SH && GRP == 0 && DO_S;
   constexpr bool SH_PV = SH && GRP == 1 && DO_PV;
+  constexpr int SPC = 4 + (SH_S ? 1 : 0);        // score steps per head-dim step
+  constexpr int PPK = D / 16 + (SH_PV ? 2 : 0);  // P.V steps per key step
+  constexpr int NSS = DO_S ? (D / 32) * SPC : 0;
+  constexpr int NPS = DO_PV ? 2 * PPK : 0;
+  constexpr int NSTEP = NSS + NPS;
   const floatx4 z = {0.f, 0.f, 0.f, 0.f};
   auto frag = [&](int i) __attribute__((always_inline)) -> bf16x8 {
-    if (i < NSS) return kfrag<D>(sK, i % 4, i / 4, lane);
-    const int j = i - NSS;
-    return vfrag<D>(sV, j % (D / 16), j / (D / 16), lane);
+    if (i < NSS) {
+      const int c = i / SPC, e = i % SPC;
+      return kfrag<D>(sK, e < 4 ? e : simd, c, lane);
+    }
+    const int j = i - NSS, kc = j / PPK, e = j % PPK;
+    return vfrag<D>(sV, e < D / 16 ? e : 2 * simd + (e - D / 16), kc, lane);
   };
-  // shared-tile operands, read up front: K of block `simd` per head-dim
-  // step (group 0); V^T of head-dim blocks 2s, 2s+1 and the shared P^T per
-  // key step (group 1)
-  bf16x8 ksh[SH_S ? D / 32 : 1];
-  bf16x8 vsh[SH_PV ? 4 : 1], psh[SH_PV ? 2 : 1];
-  if constexpr (SH_S) {
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) ksh[c] = kfrag<D>(sK, simd, c, lane);
-  }
+  bf16x8 psh[SH_PV ? 2 : 1];
   if constexpr (SH_PV) {
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      psh[kc] = *(const lds_bf16x8*)(sP + (kc * 64 + lane) * 16);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) vsh[2 * kc + e] = vfrag<D>(sV, 2 * simd + e, kc, lane);
-    }
+    for (int kc = 0; kc < 2; ++kc) psh[kc] = *(const lds_bf16x8*)(sP + (kc * 64 + lane) * 16);
   }
   bf16x8 fr[DEPTH + 1];
 #pragma unroll
@@ -155,21 +152,15 @@ __device__ __forceinline__ void pp_c_phase(const lds_char* sK, const lds_char* s
 #pragma unroll
   for (int i = 0; i < NSTEP; ++i) {
     if (i + DEPTH < NSTEP) fr[(i + DEPTH) % (DEPTH + 1)] = frag(i + DEPTH);
+    const bf16x8 f = fr[i % (DEPTH + 1)];
     if (i < NSS) {
-      const int c = i / 4, kb4 = i % 4;
-      s[kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[i % (DEPTH + 1)], q[c], c == 0 ? z : s[kb4], 0, 0, 0);
-      if constexpr (SH_S) {
-        if (kb4 == 3) ss = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ksh[c], qs[c], c == 0 ? z : ss, 0, 0, 0);
-      }
+      const int c = i / SPC, e = i % SPC;
+      if (e < 4) s[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, q[c], c == 0 ? z : s[e], 0, 0, 0);
+      else ss = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, qs[c], c == 0 ? z : ss, 0, 0, 0);
     } else {
-      const int j = i - NSS, kc = j / (D / 16), db = j % (D / 16);
-      st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[i % (DEPTH + 1)], p[kc], st.o[db], 0, 0, 0);
-      if constexpr (SH_PV) {
-        if (db == 3 || db == 7) {
-          const int e = db == 3 ? 0 : 1;
-          st.os[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vsh[2 * kc + e], psh[kc], st.os[e], 0, 0, 0);
-        }
-      }
+      const int j = i - NSS, kc = j / PPK, e = j % PPK;
+      if (e < D / 16) st.o[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, p[kc], st.o[e], 0, 0, 0);
+      else st.os[e - D / 16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, psh[kc], st.os[e - D / 16], 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -523,9 +514,9 @@ void attn_pp_kernel(AttnArgs a) {
         // C(j): S(j); P.V(j-1)
         __builtin_amdgcn_s_setprio(1);
         if (j > j0)
-          pp_c_phase<D, G, SH, true, true>(kslot(j), vslot(j - 1), sPb(j - 1), q, qs, s, ss, p, st, lane, simd);
+          pp_c_phase<D, G, SH, true, true, kPpDepth>(kslot(j), vslot(j - 1), sPb(j - 1), q, qs, s, ss, p, st, lane, simd);
         else
-          pp_c_phase<D, G, SH, true, false>(kslot(j), vslot(j), sPb(0), q, qs, s, ss, p, st, lane, simd);
+          pp_c_phase<D, G, SH, true, false, kPpDepth>(kslot(j), vslot(j), sPb(0), q, qs, s, ss, p, st, lane, simd);
         __builtin_amdgcn_s_setprio(0);
         if (G == 1) wait_vmcnt_dyn(cnt(j - 1));  // K(j+1), V(j) have landed
         wait_lgkmcnt0();
@@ -546,7 +537,7 @@ void attn_pp_kernel(AttnArgs a) {
       }
       // C(n): P.V(n-1)
       __builtin_amdgcn_s_setprio(1);
-      pp_c_phase<D, G, SH, false, true>(kslot(n), vslot(n - 1), sPb(n - 1), q, qs, s, ss, p, st, lane, simd);
+      pp_c_phase<D, G, SH, false, true, kPpDepth>(kslot(n), vslot(n - 1), sPb(n - 1), q, qs, s, ss, p, st, lane, simd);
       __builtin_amdgcn_s_setprio(0);
       if (G == 0) barrier();
     };
