@@ -87,6 +87,9 @@ def parse():
     p.add_argument("--lm-layout", default="packed", choices=["packed", "rowmajor"],
                    help="layout of W for --verify lmhead (packed once, before timing, as at weight load)")
     p.add_argument("--temperature", type=float, default=1.0)
+    p.add_argument("--separate", action="store_true",
+                   help="greedy verify and the commit as two calls (tidar_verify_greedy, tidar_kv_commit) "
+                        "instead of the fused tidar_verify_commit_greedy")
     p.add_argument("--paged", action="store_true")
     p.add_argument("--loop", type=int, default=0, metavar="N",
                    help="serving loop: N consecutive steps on one cache whose lengths the commit advances in "
@@ -590,10 +593,15 @@ def bench_loop(args, wl, d, v, a_planted, reps, n_rep, attention, verify_commit,
                              s.n_groups, s.sm_scale, max_len=max_lens[t], out=r["out"], lse=r["lse"],
                              workspace=ws_a, kv_chunk=args.kv_chunk)
         ev[t][1].record(stream)
-        tidar.verify_greedy(r["ar_logits"], r["draft_logits"], r["cand"], accept_len=r0["acc"],
-                            next_cand=r0["next"], workspace=r["ws_v"])
-        tidar.kv_commit(r0["k_cache"], r0["v_cache"], r0["lens"], r["k_step"], r["v_step"], r0["acc"], s.k,
-                        r0["err"])
+        if args.separate:
+            tidar.verify_greedy(r["ar_logits"], r["draft_logits"], r["cand"], accept_len=r0["acc"],
+                                next_cand=r0["next"], workspace=r["ws_v"])
+            tidar.kv_commit(r0["k_cache"], r0["v_cache"], r0["lens"], r["k_step"], r["v_step"], r0["acc"], s.k,
+                            r0["err"])
+        else:
+            tidar.verify_commit_greedy(r["ar_logits"], r["draft_logits"], r["cand"], r0["k_cache"], r0["v_cache"],
+                                       r0["lens"], r["k_step"], r["v_step"], accept_len=r0["acc"],
+                                       next_cand=r0["next"], err_flags=r0["err"], state=r0["state"])
         ev[t][2].record(stream)
         lens_h = lens_h + a
     torch.cuda.synchronize()
@@ -612,7 +620,8 @@ def bench_loop(args, wl, d, v, a_planted, reps, n_rep, attention, verify_commit,
                    "head_dim": s.D, "prefix_start_mean": float(np.mean(s.lens)),
                    "prefix_end_mean": float(lens_h.mean()), "k": s.k, "draft_groups": s.n_groups,
                    "step_rows": s.R, "vocab": wl.V, "accept": wl.accept, "verify": "greedy",
-                   "kv_layout": "contiguous", "input_replicas": n_rep},
+                   "kv_layout": "contiguous", "input_replicas": n_rep,
+                   "verify_commit": "separate" if args.separate else "fused"},
         "step_gbps": round(step_gbps, 2),
         "step_us_mean": round(total_ms / N * 1e3, 2),
         "step_us_p50": round(float(np.percentile(step_ms, 50)) * 1e3, 2),
@@ -721,6 +730,7 @@ def main():
         r["acc"] = torch.empty(s.B, dtype=torch.int32, device=dev)
         r["next"] = torch.empty((s.B, s.k), dtype=torch.int32, device=dev)
         r["err"] = torch.empty(s.B, dtype=torch.int32, device=dev)
+        r["state"] = tidar.verify_commit_state(s.B, s.k, dev)
         reps.append(r)
     del base
     torch.cuda.synchronize()
@@ -758,7 +768,21 @@ def main():
                             r["err"])
         r["lens"].copy_(r["lens0"])
 
+    fused = args.verify == "greedy" and not args.separate
+
     def verify_commit(r, step_no, ev=None):
+        if fused:  # one call: greedy verify and the commit
+            if args.paged:
+                tidar.verify_commit_greedy_paged(r["ar_logits"], r["draft_logits"], r["cand"], r["k_pool"],
+                                                 r["v_pool"], r["block_table"], r["lens"], r["k_step"], r["v_step"],
+                                                 accept_len=r["acc"], next_cand=r["next"], err_flags=r["err"],
+                                                 state=r["state"])
+            else:
+                tidar.verify_commit_greedy(r["ar_logits"], r["draft_logits"], r["cand"], r["k_cache"], r["v_cache"],
+                                           r["lens"], r["k_step"], r["v_step"], accept_len=r["acc"],
+                                           next_cand=r["next"], err_flags=r["err"], state=r["state"])
+            r["lens"].copy_(r["lens0"])
+            return
         verify(r, step_no)
         if ev is not None:
             ev.record(stream)
@@ -874,6 +898,9 @@ def main():
                    "prefix": s.lens[0], "k": s.k, "draft_groups": s.n_groups, "step_rows": s.R, "vocab": wl.V,
                    "accept": wl.accept if args.verify == "greedy" else "sampled", "verify": args.verify,
                    "kv_layout": "paged" if args.paged else "contiguous",
+                   "verify_commit": "fused" if fused else "separate",
+                   "attention_plan": tidar.step_attention_plan(0, s.B, s.Hq, s.Hkv, s.D, s.S_max, s.max_len, s.k,
+                                                               s.n_groups, args.kv_chunk),
                    "cold_replicas": n_rep},
         "step_gbps": round(step_gbps, 2),
         "step_us": round(step_ms * 1e3, 2),

@@ -2,8 +2,8 @@
 
 The calls of ``include/tidar.h`` -- ``step_attention``,
 ``step_attention_paged``, ``train_attention``, ``verify_greedy``,
-``lmhead_verify_greedy``, ``verify_sample``, ``kv_commit`` and
-``kv_commit_paged`` -- under the same names, taking torch tensors that
+``lmhead_verify_greedy``, ``verify_sample``, ``kv_commit``,
+``kv_commit_paged`` and ``verify_commit_greedy[_paged]`` -- under the same names, taking torch tensors that
 live on the GPU.  This module only checks shapes and dtypes,
 marshals pointers and the current HIP stream, and allocates outputs /
 workspace with torch when the caller does not pass them.  Every step of the
@@ -56,6 +56,10 @@ SIGNATURES = {
     "tidar_lmhead_packed_bytes": (_c_int, [_c_int] * 2 + [ctypes.POINTER(_c_size)]),
     "tidar_lmhead_pack": (_c_int, [_c_int] * 2 + [_p] * 3),
     "tidar_lmhead_verify_greedy_packed": (_c_int, [_c_int] * 4 + [_p] * 7 + [_c_size, _p]),
+    "tidar_verify_commit_state_bytes": (_c_int, [_c_int] * 2 + [ctypes.POINTER(_c_size)]),
+    "tidar_verify_commit_greedy": (_c_int, [_c_int] * 8 + [_p] * 12 + [_c_size, _p]),
+    "tidar_verify_commit_greedy_paged": (_c_int, [_c_int] * 9 + [_p] * 13 + [_c_size, _p]),
+    "tidar_launch_shapes": (_c_int, [_c_int] * 7 + [ctypes.POINTER(_c_int)]),
     "tidar_read_probe": (_c_int, [_p, _c_size, _p, _p]),
 }
 
@@ -521,6 +525,107 @@ def kv_commit_paged(k_pool, v_pool, block_table, lens, k_step, v_step, accept_le
                                       _ptr(v_pool), _ptr(block_table), _ptr(lens), _ptr(k_step), _ptr(v_step),
                                       _ptr(accept_len), _ptr(err_flags), _stream()))
     return err_flags
+
+
+# ------------------------------------------------------------------------ fused verify + commit
+def verify_commit_state_bytes(B: int, k: int) -> int:
+    n = _c_size(0)
+    _check("tidar_verify_commit_state_bytes", lib().tidar_verify_commit_state_bytes(B, k, ctypes.byref(n)))
+    return n.value
+
+
+def verify_commit_state(B: int, k: int, device) -> torch.Tensor:
+    """A zeroed state buffer for the fused calls (every call leaves it zeroed,
+    so one buffer serves a whole decode loop on one stream)."""
+    return torch.zeros(max(verify_commit_state_bytes(B, k), 256), dtype=torch.uint8, device=device)
+
+
+def _verify_commit_common(ar_logits, draft_logits, cand, accept_len, next_cand, err_flags, state, dev, B, k):
+    _need(ar_logits, "ar_logits", torch.float32, 3, dev)
+    if tuple(ar_logits.shape[:2]) != (B, k + 1):
+        raise ValueError("ar_logits must be [B][k+1][V]")
+    V = ar_logits.shape[2]
+    _need(cand, "cand", torch.int32, 2, dev)
+    if tuple(cand.shape) != (B, k):
+        raise ValueError("cand must be [B][k]")
+    if k > 1 or draft_logits is not None:
+        _need(draft_logits, "draft_logits", torch.float32, 4, dev)
+        if tuple(draft_logits.shape) != (B, k, k, V):
+            raise ValueError("draft_logits must be [B][k][k][V]")
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    else:
+        _need(accept_len, "accept_len", torch.int32, 1, dev)
+    if next_cand is None:
+        next_cand = torch.empty((B, k), dtype=torch.int32, device=dev)
+    else:
+        _need(next_cand, "next_cand", torch.int32, 2, dev)
+    if err_flags is not None:
+        _need(err_flags, "err_flags", torch.int32, 1, dev)
+    if state is None:
+        state = verify_commit_state(B, k, dev)
+    else:
+        _need(state, "state", torch.uint8, 1, dev)
+    return V, accept_len, next_cand, state
+
+
+def verify_commit_greedy(ar_logits, draft_logits, cand, k_cache, v_cache, lens, k_step, v_step, accept_len=None,
+                         next_cand=None, err_flags=None, state=None):
+    """Greedy verification and the KV commit in one call (the results of
+    verify_greedy followed by kv_commit).  ``state`` must be a zeroed buffer
+    (verify_commit_state) or None.  Returns (accept_len, next_cand)."""
+    _need(k_cache, "k_cache", ndim=4)
+    dev, dt = k_cache.device, k_cache.dtype
+    B, Hkv, S_max, D = k_cache.shape
+    _need(v_cache, "v_cache", dt, 5, dev)
+    _need(k_step, "k_step", dt, 4, dev)
+    _need(v_step, "v_step", dt, 4, dev)
+    _need(lens, "lens", torch.int32, 1, dev)
+    R = k_step.shape[1]
+    _check_caches(k_cache, v_cache, B, Hkv, S_max, D)
+    if tuple(k_step.shape) != (B, R, Hkv, D) or tuple(v_step.shape) != (B, R, Hkv, D):
+        raise ValueError("k_step/v_step must be [B][R][Hkv][D]")
+    k = cand.shape[1]
+    V, accept_len, next_cand, state = _verify_commit_common(ar_logits, draft_logits, cand, accept_len, next_cand,
+                                                            err_flags, state, dev, B, k)
+    _check("tidar_verify_commit_greedy",
+           lib().tidar_verify_commit_greedy(_dtype_code(k_cache), B, Hkv, D, S_max, R, k, V, _ptr(ar_logits),
+                                           _ptr(draft_logits), _ptr(cand), _ptr(k_cache), _ptr(v_cache), _ptr(lens),
+                                           _ptr(k_step), _ptr(v_step), _ptr(accept_len), _ptr(next_cand),
+                                           _ptr(err_flags), _ptr(state), state.numel(), _stream()))
+    return accept_len, next_cand
+
+
+def verify_commit_greedy_paged(ar_logits, draft_logits, cand, k_pool, v_pool, block_table, lens, k_step, v_step,
+                               accept_len=None, next_cand=None, err_flags=None, state=None):
+    """verify_commit_greedy into a paged cache (the pools and block table of
+    step_attention_paged).  Returns (accept_len, next_cand)."""
+    _need(k_pool, "k_pool", ndim=4)
+    dev, dt = k_pool.device, k_pool.dtype
+    n_pages, Hkv, _, D = k_pool.shape
+    _need(v_pool, "v_pool", dt, 4, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(k_step, "k_step", dt, 4, dev)
+    _need(v_step, "v_step", dt, 4, dev)
+    _need(lens, "lens", torch.int32, 1, dev)
+    B, R = k_step.shape[0], k_step.shape[1]
+    max_pages = block_table.shape[1]
+    if tuple(k_pool.shape) != (n_pages, Hkv, VALUE_PAGE, D) or tuple(v_pool.shape) != (n_pages, Hkv, D, VALUE_PAGE):
+        raise ValueError("k_pool must be [n_pages][Hkv][64][D] and v_pool [n_pages][Hkv][D][64]")
+    if tuple(k_step.shape) != (B, R, Hkv, D) or tuple(v_step.shape) != (B, R, Hkv, D):
+        raise ValueError("k_step/v_step must be [B][R][Hkv][D]")
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must be [B][max_pages]")
+    k = cand.shape[1]
+    V, accept_len, next_cand, state = _verify_commit_common(ar_logits, draft_logits, cand, accept_len, next_cand,
+                                                            err_flags, state, dev, B, k)
+    _check("tidar_verify_commit_greedy_paged",
+           lib().tidar_verify_commit_greedy_paged(_dtype_code(k_pool), B, Hkv, D, max_pages, n_pages, R, k, V,
+                                                 _ptr(ar_logits), _ptr(draft_logits), _ptr(cand), _ptr(k_pool),
+                                                 _ptr(v_pool), _ptr(block_table), _ptr(lens), _ptr(k_step),
+                                                 _ptr(v_step), _ptr(accept_len), _ptr(next_cand), _ptr(err_flags),
+                                                 _ptr(state), state.numel(), _stream()))
+    return accept_len, next_cand
 
 
 READ_PROBE_BLOCKS = 16384  # TIDAR_READ_PROBE_BLOCKS

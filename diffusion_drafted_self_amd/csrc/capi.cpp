@@ -316,6 +316,79 @@ int kv_commit_impl(int dtype, int B, int Hkv, int D, int S_max, int R, int k, vo
   return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
 }
 
+// State of the fused verify + commit: AR keys, then draft keys (one 8-byte
+// key per 128-byte line).
+struct FusedPlan {
+  size_t key_bytes, dkey_bytes, total;
+};
+
+int plan_fused(int B, int k, FusedPlan* p) {
+  if (k > kMaxK) return TIDAR_EUNSUPPORTED;
+  if (B < 0 || k < 1) return TIDAR_EINVAL;
+  if ((long)B * (k + 1) > 65535) return TIDAR_EUNSUPPORTED;  // grid y limit
+  p->key_bytes = round_up((size_t)B * (k + 1) * tidar::kFusedKeyBytes, 256);
+  p->dkey_bytes = round_up((size_t)B * std::max(k - 1, 1) * tidar::kFusedKeyBytes, 256);
+  p->total = p->key_bytes + p->dkey_bytes;
+  return TIDAR_OK;
+}
+
+int verify_commit_impl(int dtype, int B, int Hkv, int D, int S_max, int R, int k, int V, const float* ar_logits,
+                       const float* draft_logits, const int32_t* cand, void* k_cache, void* v_cache,
+                       const int32_t* block_table, int max_pages, int n_pages, int32_t* lens, const void* k_step,
+                       const void* v_step, int32_t* accept_len, int32_t* next_cand, int32_t* err_flags,
+                       void* state, size_t state_bytes, void* stream) {
+  // the verification's checks, then the commit's
+  VerifyPlan vp;
+  int st = plan_verify(B, k, V, &vp);
+  if (st != TIDAR_OK) return st;
+  FusedPlan fp;
+  st = plan_fused(B, k, &fp);
+  if (st != TIDAR_OK) return st;
+  if (dtype != TIDAR_BF16 && dtype != TIDAR_F32) return TIDAR_EUNSUPPORTED;
+  if (D != 64 && D != 128) return TIDAR_EUNSUPPORTED;
+  if (Hkv < 1 || S_max < 1 || S_max % kValuePage != 0 || R < k) return TIDAR_EINVAL;
+  if (B == 0) return TIDAR_OK;
+  if (!aligned(ar_logits, 16) || !aligned(cand, 4) || !aligned(accept_len, 4) || !aligned(next_cand, 4))
+    return TIDAR_EINVAL;
+  if (k > 1 && !aligned(draft_logits, 16)) return TIDAR_EINVAL;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_step, 16) || !aligned(v_step, 16) ||
+      !aligned(lens, 4))
+    return TIDAR_EINVAL;
+  if (err_flags && !aligned(err_flags, 4)) return TIDAR_EINVAL;
+  if (!aligned(state, 8) || state_bytes < fp.total) return TIDAR_EWORKSPACE;
+
+  tidar::FusedVerifyArgs a = {};
+  a.ar_logits = ar_logits;
+  a.draft_logits = draft_logits;
+  a.cand = cand;
+  a.accept_len = accept_len;
+  a.next_cand = next_cand;
+  char* ws = static_cast<char*>(state);
+  a.key = reinterpret_cast<unsigned long long*>(ws);
+  a.dkey = reinterpret_cast<unsigned long long*>(ws + fp.key_bytes);
+  a.B = B;
+  a.k = k;
+  a.V = V;
+  a.n_draft_rows = std::max(k - 1, 1);
+  a.commit = 1;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.lens = lens;
+  a.k_step = k_step;
+  a.v_step = v_step;
+  a.err_flags = err_flags;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.S_max = S_max;
+  a.R = R;
+  a.elem_bytes = dtype == TIDAR_BF16 ? 2 : 4;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.n_pages = n_pages;
+  const hipError_t e = tidar::launch_fused_verify(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -639,6 +712,69 @@ int tidar_kv_commit_paged(int dtype, int B, int Hkv, int D, int max_pages, int n
   if (B > 0 && !aligned(block_table, 4)) return TIDAR_EINVAL;
   return kv_commit_impl(dtype, B, Hkv, D, max_pages * kValuePage, R, k, k_pool, v_pool, block_table, max_pages,
                         n_pages, lens, k_step, v_step, accept_len, err_flags, stream);
+}
+
+int tidar_verify_commit_state_bytes(int B, int k, size_t* bytes) {
+  if (!bytes) return TIDAR_EINVAL;
+  FusedPlan p;
+  const int st = plan_fused(B, k, &p);
+  if (st != TIDAR_OK) return st;
+  *bytes = p.total;
+  return TIDAR_OK;
+}
+
+int tidar_verify_commit_greedy(int dtype, int B, int Hkv, int D, int S_max, int R, int k, int V,
+                               const float* ar_logits, const float* draft_logits, const int32_t* cand,
+                               void* k_cache, void* v_cache, int32_t* lens, const void* k_step, const void* v_step,
+                               int32_t* accept_len, int32_t* next_cand, int32_t* err_flags, void* state,
+                               size_t state_bytes, void* stream) {
+  return verify_commit_impl(dtype, B, Hkv, D, S_max, R, k, V, ar_logits, draft_logits, cand, k_cache, v_cache,
+                            nullptr, 0, 0, lens, k_step, v_step, accept_len, next_cand, err_flags, state,
+                            state_bytes, stream);
+}
+
+int tidar_verify_commit_greedy_paged(int dtype, int B, int Hkv, int D, int max_pages, int n_pages, int R, int k,
+                                     int V, const float* ar_logits, const float* draft_logits,
+                                     const int32_t* cand, void* k_pool, void* v_pool, const int32_t* block_table,
+                                     int32_t* lens, const void* k_step, const void* v_step, int32_t* accept_len,
+                                     int32_t* next_cand, int32_t* err_flags, void* state, size_t state_bytes,
+                                     void* stream) {
+  if (max_pages < 1 || max_pages > (1 << 24) || n_pages < 1) return TIDAR_EINVAL;
+  if (B > 0 && !aligned(block_table, 4)) return TIDAR_EINVAL;
+  return verify_commit_impl(dtype, B, Hkv, D, max_pages * kValuePage, R, k, V, ar_logits, draft_logits, cand, k_pool,
+                            v_pool, block_table, max_pages, n_pages, lens, k_step, v_step, accept_len, next_cand,
+                            err_flags, state, state_bytes, stream);
+}
+
+int tidar_launch_shapes(int path, int B, int k, int V, int Hkv, int D, int dtype, int* shapes) {
+  if (!shapes) return TIDAR_EINVAL;
+  tidar::LaunchShape sh[tidar::kMaxLaunches];
+  int n = 0, st;
+  if (path == 0 || path == 2) {  // the entry points' own checks first
+    VerifyPlan vp;
+    if ((st = plan_verify(B, k, V, &vp)) != TIDAR_OK) return st;
+  }
+  if (path == 1 || path == 2) {
+    if (dtype != TIDAR_BF16 && dtype != TIDAR_F32) return TIDAR_EUNSUPPORTED;
+    if (D != 64 && D != 128) return TIDAR_EUNSUPPORTED;
+    if (k > kMaxK) return TIDAR_EUNSUPPORTED;
+    if (B < 0 || Hkv < 1 || k < 1) return TIDAR_EINVAL;
+  }
+  if (path == 0) n = tidar::verify_launch_shapes(B, k, V, sh);
+  else if (path == 1) n = tidar::commit_launch_shapes(B, Hkv, D, k, dtype == TIDAR_BF16 ? 2 : 4, sh);
+  else if (path == 2) {
+    FusedPlan fp;
+    if ((st = plan_fused(B, k, &fp)) != TIDAR_OK) return st;
+    n = tidar::fused_launch_shapes(B, k, V, sh);
+  } else {
+    return TIDAR_EINVAL;
+  }
+  for (int i = 0; i < n; ++i) {
+    shapes[3 * i] = sh[i].gx;
+    shapes[3 * i + 1] = sh[i].gy;
+    shapes[3 * i + 2] = sh[i].block;
+  }
+  return n;
 }
 
 static_assert(TIDAR_READ_PROBE_BLOCKS == tidar::kReadProbeBlocks, "read probe sink size");

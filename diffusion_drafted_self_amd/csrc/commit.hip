@@ -118,11 +118,19 @@ void launch_typed(const CommitArgs& a, hipStream_t s, int threads) {
 
 }  // namespace
 
+// one workgroup per sequence, one thread per 16 B piece of a candidate row
+// (keys and values side by side), at most 1024
+int commit_launch_shapes(int B, int Hkv, int D, int k, int elem_bytes, LaunchShape* out) {
+  const int pieces = Hkv * k * D * elem_bytes / 16;
+  out[0] = {B, 1, std::min(1024, std::max(64, ((pieces + 63) / 64) * 64))};
+  return 1;
+}
+
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
-  const int pieces = a.Hkv * a.k * a.D * a.elem_bytes / 16;
-  const int threads = std::min(1024, std::max(64, ((pieces + 63) / 64) * 64));
-  launch_typed(a, s, threads);  // bf16 elements move as raw 16-bit words
+  LaunchShape sh[kMaxLaunches];
+  commit_launch_shapes(a.B, a.Hkv, a.D, a.k, a.elem_bytes, sh);
+  launch_typed(a, s, sh[0].block);  // bf16 elements move as raw 16-bit words
   return hipGetLastError();
 }
 

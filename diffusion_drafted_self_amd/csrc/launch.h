@@ -58,18 +58,31 @@ struct VerifyArgs {
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
 
-// Greedy verification fused with the KV commit (or without it): two
-// launches over per-row 64-bit argmax keys and per-sequence arrival counters
-// that every call leaves zeroed.
+// One kernel launch: grid (gx, gy) of workgroups of `block` threads.  The
+// launchers take their shapes from the functions below, which the C ABI
+// also exports (tidar_launch_shapes), so every shape can be checked on the
+// host: a block over 1024 threads does not launch at all.
+struct LaunchShape {
+  int gx, gy, block;
+};
+constexpr int kMaxLaunches = 4;
+// greedy verification: AR argmax, selection, draft argmax, finalisation
+// (the last two only for k > 1); returns the number of launches
+int verify_launch_shapes(int B, int k, int V, LaunchShape* out);
+int commit_launch_shapes(int B, int Hkv, int D, int k, int elem_bytes, LaunchShape* out);
+
+// Greedy verification fused with the KV commit (or without it): three
+// launches over per-row 64-bit argmax keys that every call leaves zeroed.
+constexpr int kFusedKeyBytes = 128;  // one 64-bit argmax key per 128-byte line
+
 struct FusedVerifyArgs {
   const float* ar_logits;     // [B][k+1][V]
   const float* draft_logits;  // [B][k][k][V]
   const int32_t* cand;        // [B][k]
   int32_t* accept_len;        // [B]
   int32_t* next_cand;         // [B][k]
-  unsigned long long* key;    // [B*(k+1)]          state
-  unsigned long long* dkey;   // [B*n_draft_rows]   state
-  unsigned* cnt;              // [B]                state
+  unsigned long long* key;    // [B*(k+1)] keys, kFusedKeyBytes apart         state
+  unsigned long long* dkey;   // [B*n_draft_rows] keys, kFusedKeyBytes apart  state
   int B, k, V, n_draft_rows;  // n_draft_rows = max(k-1, 1)
   // commit (commit != 0)
   int commit;
@@ -91,6 +104,7 @@ struct FusedVerifyGeometry {
   int draft_rows, block;
 };
 FusedVerifyGeometry fused_verify_geometry(int B, int k, int V);
+int fused_launch_shapes(int B, int k, int V, LaunchShape* out);
 hipError_t launch_fused_verify(const FusedVerifyArgs& a, hipStream_t s);
 hipError_t launch_verify_select(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_draft_finalize(const VerifyArgs& a, hipStream_t s);

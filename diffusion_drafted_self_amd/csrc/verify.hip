@@ -114,18 +114,32 @@ __global__ __launch_bounds__(64 * kMaxWaves) void draft_finalize_kernel(VerifyAr
 
 }  // namespace
 
+int verify_launch_shapes(int B, int k, int V, LaunchShape* out) {
+  const int n_chunks = (V + kArgmaxChunk - 1) / kArgmaxChunk;
+  out[0] = {n_chunks, B * (k + 1), 256};
+  out[1] = {B, 1, 64 * std::min(k + 1, kMaxWaves)};
+  if (k == 1) return 2;
+  out[2] = {n_chunks, B * (k - 1), 256};
+  out[3] = {B, 1, 64 * std::min(k - 1, kMaxWaves)};
+  return 4;
+}
+
 // The selection and the draft finalisation on their own, for producers of
 // the chunk results other than argmax_partial_kernel (the fused LM head).
 hipError_t launch_verify_select(const VerifyArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
   if (a.k + 1 > kMaxRows) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(verify_select_kernel, dim3(a.B), dim3(64 * std::min(a.k + 1, kMaxWaves)), 0, s, a);
+  LaunchShape sh[kMaxLaunches];
+  verify_launch_shapes(a.B, a.k, a.V, sh);
+  hipLaunchKernelGGL(verify_select_kernel, dim3(sh[1].gx, sh[1].gy), dim3(sh[1].block), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_draft_finalize(const VerifyArgs& a, hipStream_t s) {
   if (a.B == 0 || a.k == 1) return hipSuccess;
-  hipLaunchKernelGGL(draft_finalize_kernel, dim3(a.B), dim3(64 * std::min(a.k - 1, kMaxWaves)), 0, s, a);
+  LaunchShape sh[kMaxLaunches];
+  verify_launch_shapes(a.B, a.k, a.V, sh);
+  hipLaunchKernelGGL(draft_finalize_kernel, dim3(sh[3].gx, sh[3].gy), dim3(sh[3].block), 0, s, a);
   return hipGetLastError();
 }
 
@@ -134,16 +148,18 @@ hipError_t launch_draft_finalize(const VerifyArgs& a, hipStream_t s) {
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
   if (a.k + 1 > kMaxRows) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(argmax_partial_kernel<false>, dim3(a.n_chunks, a.B * (a.k + 1)), dim3(256), 0, s, a);
+  LaunchShape sh[kMaxLaunches];
+  const int n = verify_launch_shapes(a.B, a.k, a.V, sh);
+  hipLaunchKernelGGL(argmax_partial_kernel<false>, dim3(sh[0].gx, sh[0].gy), dim3(sh[0].block), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(verify_select_kernel, dim3(a.B), dim3(64 * std::min(a.k + 1, kMaxWaves)), 0, s, a);
+  hipLaunchKernelGGL(verify_select_kernel, dim3(sh[1].gx, sh[1].gy), dim3(sh[1].block), 0, s, a);
   e = hipGetLastError();
-  if (e != hipSuccess || a.k == 1) return e;
-  hipLaunchKernelGGL(argmax_partial_kernel<true>, dim3(a.n_chunks, a.B * (a.k - 1)), dim3(256), 0, s, a);
+  if (e != hipSuccess || n == 2) return e;
+  hipLaunchKernelGGL(argmax_partial_kernel<true>, dim3(sh[2].gx, sh[2].gy), dim3(sh[2].block), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(draft_finalize_kernel, dim3(a.B), dim3(64 * std::min(a.k - 1, kMaxWaves)), 0, s, a);
+  hipLaunchKernelGGL(draft_finalize_kernel, dim3(sh[3].gx, sh[3].gy), dim3(sh[3].block), 0, s, a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,269 @@
+// Greedy verification, next-draft selection and the KV commit of one TiDAR
+// step in three launches (gfx950).
+//
+// The pass scores the carried candidates strictly left to right; the
+// drafts prepared for the confirmed outcome become the next candidates; the
+// accepted entries are appended to the settled cache and the rejected ones
+// evicted ("TiDAR : l'hybride de NVIDIA qui rédige par diffusion et parle de
+// manière autorégressive", nodesdaily.com, paragraphs on the three zones
+// and on drafting for every outcome).  Same results as the separate
+// verification and commit calls; three launches instead of five:
+//
+//   ar_key_kernel     (chunk, AR row): the chunk's (max, lower index) folded
+//       into one 64-bit key per row by an atomic max; a key orders by value,
+//       then by lower index.
+//   draft_commit_kernel  (chunk, draft slot) per sequence: every workgroup
+//       reads the k+1 row keys of its sequence and the candidates and takes
+//       the accept length itself (72 bytes, the same in all of them),
+//       reduces its chunk of the selected group's draft row into that row's
+//       key, and copies its share of the accepted step rows into the cache.
+//   finalize_kernel   one wave per sequence: accept length, bonus token and
+//       next drafts from the keys, the new settled length, and the keys
+//       cleared for the next call.
+// Work across workgroups meets only at kernel boundaries: the atomics are
+// coherent across the XCDs, and nothing waits on another workgroup inside a
+// kernel (an in-kernel arrival counter needs a device-scope release and
+// acquire per workgroup, which write back and invalidate the XCD's L2).
+//
+// State: [B*(k+1)] AR keys and [B*max(k-1,1)] draft keys, one per 128-byte
+// line, zero between
+// calls (each call leaves them so; the memory must be zero before its
+// first use).
+#include <algorithm>
+
+#include "argmax_block.h"
+#include "common.h"
+#include "launch.h"
+
+namespace tidar {
+
+namespace {
+
+typedef unsigned long long u64;
+
+// Each row key sits in its own 128-byte line: the atomics of one row's
+// chunks then never queue behind another row's at the coherence point.
+constexpr int kKeyStride = kFusedKeyBytes / 8;
+
+// Orders (value, index) as the greedy rule does: larger value first, then
+// lower index; -0.0 is folded onto +0.0 so the two tie.  Never 0 for a
+// finite value, so 0 is below every key.
+__device__ __forceinline__ u64 argmax_key(float v, int i) {
+  unsigned u = __float_as_uint(v + 0.0f);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((u64)u << 32) | (u64)(0xFFFFFFFFu - (unsigned)i);
+}
+__device__ __forceinline__ int key_index(u64 key) { return (int)(0xFFFFFFFFu - (unsigned)key); }
+
+__device__ __forceinline__ u64 load_key(const u64* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_zero(u64* p) {
+  __hip_atomic_store(p, (u64)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(256) void ar_key_kernel(FusedVerifyArgs a) {
+  const int chunk = blockIdx.x;
+  const int row = blockIdx.y;  // b * (k+1) + i
+  const int lo = chunk * kArgmaxChunk;
+  const int hi = min(a.V, lo + kArgmaxChunk);
+  float bv;
+  int bi;
+  block_chunk_argmax(a.ar_logits + (size_t)row * a.V, lo, hi, a.V, kArgmaxChunk, bv, bi);
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_max(&a.key[(size_t)row * kKeyStride], argmax_key(bv, bi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Copy of accepted step row i, KV head h, into the cache at position pos:
+// keys into their row, values into column pos % 64 of their transposed page.
+// PER elements per 16 B piece; threads [0, PPR) move key pieces, [PPR,
+// 2*PPR) value pieces.
+template <typename E, int D, bool PAGED>
+__device__ __forceinline__ void commit_row(const FusedVerifyArgs& a, int b, int i, int h, int pos, int page) {
+  constexpr int PER = 16 / sizeof(E);
+  constexpr int PPR = D / PER;
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const int t = threadIdx.x;
+  if (t >= 2 * PPR) return;
+  const bool is_v = t >= PPR;
+  const int c = is_v ? t - PPR : t;
+  const size_t src = (((size_t)b * a.R + i) * a.Hkv + h) * D + (size_t)c * PER;
+  const u32x4 piece = *(const u32x4*)((const E*)(is_v ? a.v_step : a.k_step) + src);
+  if (!is_v) {
+    E* dk = PAGED ? (E*)a.k_cache + (((size_t)page * a.Hkv + h) * 64 + pos % 64) * D + c * PER
+                  : (E*)a.k_cache + (((size_t)b * a.Hkv + h) * a.S_max + pos) * D + c * PER;
+    *(u32x4*)dk = piece;
+  } else {
+    E* dv = PAGED ? (E*)a.v_cache + ((size_t)page * a.Hkv + h) * D * 64 + pos % 64
+                  : (E*)a.v_cache + ((size_t)b * a.Hkv + h) * a.S_max * D + (size_t)(pos / 64) * D * 64 + pos % 64;
+    const E* ve = (const E*)&piece;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) dv[(size_t)(c * PER + j) * 64] = ve[j];
+  }
+}
+
+// Accept length of sequence b from its AR row keys: the first i < k with
+// cand[i] != argmax of AR row i, k if none; and the bonus token, the argmax
+// of AR row acc.  One wave; every lane gets both.
+__device__ __forceinline__ void accept_from_keys(const FusedVerifyArgs& a, int b, int lane, int& acc, int& bonus) {
+  const int k = a.k;
+  const u64 key = lane <= k ? load_key(&a.key[((size_t)b * (k + 1) + lane) * kKeyStride]) : 0;
+  const int cand = lane < k ? a.cand[(size_t)b * k + lane] : 0;
+  const int t = key_index(key);
+  const bool miss = (lane < k && cand != t) || lane == k;
+  acc = __ffsll((long long)__ballot(miss)) - 1;
+  bonus = __shfl(t, acc);
+}
+
+// The commit's decision for sequence b: flag 1 (capacity or a negative
+// length) or 3 (a page outside the pools) leaves it unwritten; pg0, pg1
+// are the (at most two) pages positions L .. L+acc-1 fall in.
+template <bool PAGED>
+__device__ __forceinline__ int commit_flag(const FusedVerifyArgs& a, int b, int L, int acc, int& pg0, int& pg1) {
+  int flag = (L < 0 || L + acc > a.S_max) ? 1 : 0;
+  pg0 = pg1 = 0;
+  if (PAGED && !flag && acc > 0) {
+    const int32_t* tbl = a.block_table + (size_t)b * a.max_pages;
+    pg0 = tbl[L / 64];
+    pg1 = tbl[(L + acc - 1) / 64];
+    if ((unsigned)pg0 >= (unsigned)a.n_pages || (unsigned)pg1 >= (unsigned)a.n_pages) flag = 3;
+  }
+  return flag;
+}
+
+template <typename E, int D, bool PAGED, bool COMMIT>
+__global__ __launch_bounds__(256) void draft_commit_kernel(FusedVerifyArgs a) {
+  __shared__ int s_acc;
+  const int chunk = blockIdx.x;
+  const int b = blockIdx.y / a.n_draft_rows;
+  const int m = blockIdx.y % a.n_draft_rows;  // draft slot m + 1
+  const int k = a.k;
+  if (threadIdx.x < 64) {
+    int acc, bonus;
+    accept_from_keys(a, b, threadIdx.x, acc, bonus);
+    if (threadIdx.x == 0) s_acc = acc;
+  }
+  __syncthreads();
+  const int acc = s_acc;
+  const int g = (acc > 0 ? acc : 1) - 1;
+
+  if (k > 1) {  // this chunk of draft row (group g, slot m + 1)
+    const float* src = a.draft_logits + (((size_t)b * k + g) * k + m + 1) * a.V;
+    const int lo = chunk * kArgmaxChunk;
+    const int hi = min(a.V, lo + kArgmaxChunk);
+    float bv;
+    int bi;
+    block_chunk_argmax(src, lo, hi, a.V, kArgmaxChunk, bv, bi);
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_max(&a.dkey[((size_t)b * (k - 1) + m) * kKeyStride], argmax_key(bv, bi), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  if (COMMIT) {
+    // every workgroup of the sequence takes the same decision; units
+    // (accepted row i, KV head h) are dealt over them
+    const int L = a.lens[b];
+    int pg0, pg1;
+    if (!commit_flag<PAGED>(a, b, L, acc, pg0, pg1)) {
+      const int n_wg = gridDim.x * a.n_draft_rows;
+      for (int u = m * gridDim.x + chunk; u < acc * a.Hkv; u += n_wg) {
+        const int i = u / a.Hkv, h = u % a.Hkv, pos = L + i;
+        commit_row<E, D, PAGED>(a, b, i, h, pos, pos / 64 == L / 64 ? pg0 : pg1);
+      }
+    }
+  }
+}
+
+// One wave per sequence, after the draft kernel: the results, the new
+// settled length (every copy of the draft kernel is done), and the keys
+// cleared for the next call.
+template <bool PAGED, bool COMMIT>
+__global__ __launch_bounds__(64) void finalize_kernel(FusedVerifyArgs a) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int k = a.k;
+  int acc, bonus;
+  accept_from_keys(a, b, lane, acc, bonus);
+  if (lane < k - 1) {
+    u64* dk = &a.dkey[((size_t)b * (k - 1) + lane) * kKeyStride];
+    a.next_cand[(size_t)b * k + 1 + lane] = key_index(load_key(dk));
+    store_zero(dk);
+  }
+  if (lane == 0) {
+    a.next_cand[(size_t)b * k] = bonus;
+    a.accept_len[b] = acc;
+    if (COMMIT) {
+      const int L = a.lens[b];
+      int pg0, pg1;
+      const int flag = commit_flag<PAGED>(a, b, L, acc, pg0, pg1);
+      if (a.err_flags) a.err_flags[b] = flag;
+      if (!flag) a.lens[b] = L + acc;
+    }
+  }
+  if (lane <= k) store_zero(&a.key[((size_t)b * (k + 1) + lane) * kKeyStride]);  // every lane read its key above
+}
+
+template <typename E, int D, bool PAGED>
+void launch_draft_typed(const FusedVerifyArgs& a, dim3 grid, hipStream_t s) {
+  if (a.commit) hipLaunchKernelGGL((draft_commit_kernel<E, D, PAGED, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((draft_commit_kernel<E, D, PAGED, false>), grid, dim3(256), 0, s, a);
+}
+
+void launch_finalize(const FusedVerifyArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  const bool paged = a.block_table != nullptr;
+  if (!a.commit) hipLaunchKernelGGL((finalize_kernel<false, false>), grid, block, 0, s, a);
+  else if (paged) hipLaunchKernelGGL((finalize_kernel<true, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((finalize_kernel<false, true>), grid, block, 0, s, a);
+}
+
+}  // namespace
+
+FusedVerifyGeometry fused_verify_geometry(int B, int k, int V) {
+  FusedVerifyGeometry g;
+  const int n_chunks = (V + kArgmaxChunk - 1) / kArgmaxChunk;
+  g.ar_grid_x = n_chunks;
+  g.ar_grid_y = B * (k + 1);
+  g.draft_rows = std::max(k - 1, 1);
+  g.draft_grid_x = k > 1 ? n_chunks : 1;
+  g.draft_grid_y = B * g.draft_rows;
+  g.block = 256;
+  return g;
+}
+
+int fused_launch_shapes(int B, int k, int V, LaunchShape* out) {
+  const FusedVerifyGeometry g = fused_verify_geometry(B, k, V);
+  out[0] = {g.ar_grid_x, g.ar_grid_y, g.block};
+  out[1] = {g.draft_grid_x, g.draft_grid_y, g.block};
+  out[2] = {B, 1, 64};  // one wave per sequence; k + 1 <= 17 lanes hold the row keys
+  return 3;
+}
+
+hipError_t launch_fused_verify(const FusedVerifyArgs& a, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  const FusedVerifyGeometry g = fused_verify_geometry(a.B, a.k, a.V);
+  if (g.draft_rows != a.n_draft_rows) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ar_key_kernel, dim3(g.ar_grid_x, g.ar_grid_y), dim3(g.block), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid(g.draft_grid_x, g.draft_grid_y);
+  const bool paged = a.block_table != nullptr;
+  LaunchShape sh[kMaxLaunches];
+  fused_launch_shapes(a.B, a.k, a.V, sh);
+  if (a.elem_bytes == 2) {
+    if (a.D == 128) paged ? launch_draft_typed<uint16_t, 128, true>(a, grid, s)
+                          : launch_draft_typed<uint16_t, 128, false>(a, grid, s);
+    else paged ? launch_draft_typed<uint16_t, 64, true>(a, grid, s)
+               : launch_draft_typed<uint16_t, 64, false>(a, grid, s);
+  } else {
+    if (a.D == 128) paged ? launch_draft_typed<uint32_t, 128, true>(a, grid, s)
+                          : launch_draft_typed<uint32_t, 128, false>(a, grid, s);
+    else paged ? launch_draft_typed<uint32_t, 64, true>(a, grid, s)
+               : launch_draft_typed<uint32_t, 64, false>(a, grid, s);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  launch_finalize(a, dim3(sh[2].gx, sh[2].gy), dim3(sh[2].block), s);
+  return hipGetLastError();
+}
+
+}  // namespace tidar

@@ -387,6 +387,63 @@ int tidar_kv_commit_paged(int dtype, int B, int Hkv, int D, int max_pages, int n
                           const void* k_step, const void* v_step, const int32_t* accept_len,
                           int32_t* err_flags, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Greedy verification fused with the KV commit.
+ *
+ * One call does what tidar_verify_greedy followed by tidar_kv_commit (or
+ * tidar_kv_commit_paged) does, with the same results bit for bit: the accept
+ * length a_b and the next drafts (paragraph on drafting for every outcome of
+ * the nodesdaily.com page), then the a_b accepted candidate rows appended to
+ * the settled cache and lens[b] += a_b, rejected entries evicted (paragraph
+ * on the three zones; "KV Cache" section of the mauroscia.it page).  It runs
+ * in three launches instead of five: per-row argmax keys are folded with
+ * atomics, every workgroup of the draft pass derives the accept length from
+ * them itself and copies a share of the accepted rows, and one wave per
+ * sequence then writes the results and the new length.
+ *
+ *   state        device memory (8-byte aligned) of at least
+ *                tidar_verify_commit_state_bytes(B, k) bytes: per-row
+ *                argmax keys.  It must be ZERO before its
+ *                first use; every call leaves it zero again.  One state must
+ *                not serve two calls that may run at the same time.
+ *   dtype, B, Hkv, D, S_max, R, k, k_cache, v_cache, lens, k_step, v_step,
+ *   err_flags    as for tidar_kv_commit (flags 0 ok, 1 capacity; 2 cannot
+ *                occur: a_b comes from the verification itself).
+ *   V, ar_logits, draft_logits, cand, accept_len, next_cand
+ *                as for tidar_verify_greedy.
+ * Returns the status the two separate calls would (the first failing check).
+ * ---------------------------------------------------------------------- */
+int tidar_verify_commit_state_bytes(int B, int k, size_t* bytes);
+
+int tidar_verify_commit_greedy(int dtype, int B, int Hkv, int D, int S_max, int R, int k, int V,
+                               const float* ar_logits, const float* draft_logits, const int32_t* cand,
+                               void* k_cache, void* v_cache, int32_t* lens,
+                               const void* k_step, const void* v_step,
+                               int32_t* accept_len, int32_t* next_cand, int32_t* err_flags,
+                               void* state, size_t state_bytes, void* stream);
+
+/* The same into a paged cache (flags as for tidar_kv_commit_paged; 3: a
+ * needed page entry outside [0, n_pages)). */
+int tidar_verify_commit_greedy_paged(int dtype, int B, int Hkv, int D, int max_pages, int n_pages, int R, int k,
+                                     int V, const float* ar_logits, const float* draft_logits,
+                                     const int32_t* cand, void* k_pool, void* v_pool,
+                                     const int32_t* block_table, int32_t* lens,
+                                     const void* k_step, const void* v_step,
+                                     int32_t* accept_len, int32_t* next_cand, int32_t* err_flags,
+                                     void* state, size_t state_bytes, void* stream);
+
+/* Launch shapes of the verification and commit paths (a host-only
+ * diagnostic; nothing is enqueued): path 0 tidar_verify_greedy, 1
+ * tidar_kv_commit, 2 tidar_verify_commit_greedy.  For each launch, in order,
+ * shapes receives (grid x, grid y, threads per workgroup); `shapes` is a
+ * host array of at least 12 ints owned by the caller.  Returns the number of
+ * launches, or the negative status the entry point would return for these
+ * sizes (V, Hkv, D, dtype are ignored where the path has no use for them).
+ * A workgroup of more than 1024 threads never launches, and a later kernel
+ * would then read what it should have written; the shapes can be checked
+ * for that on any machine. */
+int tidar_launch_shapes(int path, int B, int k, int V, int Hkv, int D, int dtype, int* shapes);
+
 /* ---------------------------------------------------------------------------
  * Measurement helper (not part of the decode step).
  *

@@ -244,3 +244,38 @@ def test_read_probe_validation(T):
     assert f(a16 + 4, 16, sink, None) == -1   # misaligned source
     assert f(a16, 24, sink, None) == -1       # not a multiple of 16
     assert f(a16, 0, sink, None) == 0         # nothing to read: nothing enqueued
+
+
+@pytest.mark.parametrize("path", [0, 1, 2])
+def test_launch_shapes_fit_the_hardware(T, path):
+    """Every launch of the verify and commit paths, for every k the library
+    accepts, has a workgroup of 64..1024 threads (a multiple of 64) and a grid
+    within the hardware's limits; the selection and finalisation workgroups
+    cover every row of their sequence.  A 17-wave selection workgroup (k = 16
+    with one wave per AR row) once failed to launch and left the draft group
+    unwritten; this catches that class of mistake on the CPU."""
+    L = T.lib()
+    shapes = (ctypes.c_int * 12)()
+    for k in range(1, 17):
+        for B in (1, 16, 65535 // (k + 1)):
+            for V in (64, 4097, 128256, 151936):
+                n = L.tidar_launch_shapes(path, B, k, V, 8, 128, 0, shapes)
+                assert n >= 1, (path, k, B, V, n)
+                for i in range(n):
+                    gx, gy, block = shapes[3 * i], shapes[3 * i + 1], shapes[3 * i + 2]
+                    assert 64 <= block <= 1024 and block % 64 == 0, (path, k, B, i, block)
+                    assert 1 <= gx <= 0x7FFFFFFF and 1 <= gy <= 65535, (path, k, B, i, gx, gy)
+                if path == 0:
+                    assert n == (2 if k == 1 else 4)
+                    assert shapes[0] * 4096 >= V and shapes[1] == B * (k + 1)   # every AR logit chunk
+                    # one selection workgroup per sequence; its waves loop over the k+1 rows
+                    assert shapes[3] == B and shapes[5] == 64 * min(k + 1, 16)
+                    if k > 1:
+                        assert shapes[7] == B * (k - 1)
+                if path == 2:
+                    assert n == 3 and shapes[1] == B * (k + 1) and shapes[4] == B * max(k - 1, 1)
+                    assert shapes[6] == B and shapes[8] >= k + 1  # one lane per AR row key
+    # beyond k = 16 every path refuses
+    for path in (0, 1, 2):
+        assert L.tidar_launch_shapes(path, 4, 17, 1000, 8, 128, 0, shapes) == -2
+    assert L.tidar_launch_shapes(3, 4, 4, 1000, 8, 128, 0, shapes) == -1

@@ -1,7 +1,10 @@
 """GPU parity at the full sizes of the 1.5B-shaped, 8B-shaped and long-context
 8B-shaped steps, in the launch configuration bench.py times (the library's
-own split plan).  Attention on sampled (sequence, head) pairs the oracle
-computes one by one; verify and commit bit-exact on the whole batch."""
+own split plan), and on the 8B step with each of the two attention kernels.
+Attention: every (sequence, head) of the 1.5B and 8B steps, and every head
+of the first and last sequence of the long-context step (the oracle takes
+about a second per 8B step); outputs are pre-filled with NaN so an unwritten
+row shows.  Verify and commit bit-exact on the whole batch."""
 import numpy as np
 import pytest
 import torch
@@ -18,22 +21,29 @@ NAMES = ["step_1p5b", "step_8b", "step_8b_long"]
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("name", NAMES)
-def test_full_size_attention_sampled(name):
+@pytest.mark.parametrize("name,kern", [("step_1p5b", None), ("step_8b", None), ("step_8b", "pipe"),
+                                       ("step_8b", "pp"), ("step_8b_long", None)])
+def test_full_size_attention(monkeypatch, name, kern):
     wl = W.WORKLOADS[name]()
     s = wl.attn
-    print(f"{name}: {wl.description}", flush=True)
+    if kern:
+        monkeypatch.setenv("TIDAR_ATTN_KERNEL", kern)
+    plan = tidar.step_attention_plan(0, s.B, s.Hq, s.Hkv, s.D, s.S_max, s.max_len, s.k, s.n_groups)
+    print(f"{name} ({kern or 'library plan'}): {wl.description}; plan {plan}", flush=True)
     d = W.attention_inputs(s, seed=7, config_id=wl.config_id, tail="nan")  # NaN past lens: never read
     t = attn_to_dev(d, "bf16")
-    out, lse = tidar.step_attention(t["q"], t["k_step"], t["v_step"], t["k_cache"], t["v_cache"], t["lens"], s.k,
-                                    s.n_groups, s.sm_scale, max_len=s.max_len)
-    rng = np.random.default_rng(1)
-    pairs = [(0, 0), (s.B - 1, s.Hq - 1)] + [(int(rng.integers(s.B)), int(rng.integers(s.Hq))) for _ in range(4)]
+    out = torch.full(tuple(t["q"].shape), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((s.B, s.Hq, s.R), float("nan"), dtype=torch.float32, device=DEV)
+    tidar.step_attention(t["q"], t["k_step"], t["v_step"], t["k_cache"], t["v_cache"], t["lens"], s.k, s.n_groups,
+                         s.sm_scale, max_len=s.max_len, out=out, lse=lse)
+    pairs = None
+    if name == "step_8b_long":  # every head of two whole sequences
+        pairs = [(b, h) for b in (0, s.B - 1) for h in range(s.Hq)]
     f = attn_f32(d, "bf16")
     ref, ref_lse = oracle.attention_ref(f["q"], f["k_step"], f["v_step"], f["k_cache"], f["v_cache"], d["lens"], s.k,
                                         s.n_groups, s.sm_scale, pairs=pairs)
     check_attention(out, lse, ref, ref_lse, "bf16", pairs=pairs, what=name)
-    assert torch.isfinite(out.float()).all()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
 
 
 @pytest.mark.timeout(300)

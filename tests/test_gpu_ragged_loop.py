@@ -8,9 +8,11 @@ bound).  Step rows are redrawn from the seed every step.
 
 The oracle keeps its own copy of every committed row (commit_ref applied to
 a window of its own tail cache), so no expected value comes from the GPU:
-verify is compared every step, attention on sampled steps and heads
-(against the initial cache plus the oracle's committed rows), and the final
-caches bit for bit.
+verify is compared every step; attention on every head of every sequence at
+the first and last steps and on 8 sampled heads at every 16th step (against
+the initial cache plus the oracle's committed rows); the final caches bit
+for bit.  The loop runs once with the separate verify and commit calls and
+once with the fused verify + commit call (one state buffer for all steps).
 """
 import math
 
@@ -48,8 +50,9 @@ def _pair_cache(init_k, init_v_nat, tail_k, tail_v_nat, b, kvh, L0, n_tail):
     return kp, W.v_paged(vp)
 
 
-@pytest.mark.timeout(600)
-def test_ragged_serving_loop():
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("fused", [False, True])
+def test_ragged_serving_loop(fused):
     wl = W.ragged_8b(seed=0)
     s = wl.attn
     B, k, V, Hkv, D = s.B, s.k, wl.V, s.Hkv, s.D
@@ -73,6 +76,7 @@ def test_ragged_serving_loop():
     ar_d, dr_d = to_dev(ar_h), to_dev(dr_h)
     ws_a = None
     err = torch.zeros(B, dtype=torch.int32, device=DEV)
+    state = tidar.verify_commit_state(B, k, DEV)
     worst = 0.0
     for t in range(STEPS):
         rows = W.step_rows_device(s, 0, t, DEV, config_id=cid)
@@ -88,8 +92,12 @@ def test_ragged_serving_loop():
                                                                        k, k), 256), dtype=torch.uint8, device=DEV)
         out, lse = tidar.step_attention(rows["q"], rows["k_step"], rows["v_step"], kc, vc, lens, k, k, s.sm_scale,
                                         max_len=max_len, workspace=ws_a)
-        acc, nxt = tidar.verify_greedy(ar_d, dr_d, to_dev(cand))
-        tidar.kv_commit(kc, vc, lens, rows["k_step"], rows["v_step"], acc, k, err)
+        if fused:
+            acc, nxt = tidar.verify_commit_greedy(ar_d, dr_d, to_dev(cand), kc, vc, lens, rows["k_step"],
+                                                  rows["v_step"], err_flags=err, state=state)
+        else:
+            acc, nxt = tidar.verify_greedy(ar_d, dr_d, to_dev(cand))
+            tidar.kv_commit(kc, vc, lens, rows["k_step"], rows["v_step"], acc, k, err)
 
         # oracle: verify
         ra, rn = oracle.verify_ref(ar_h, dr_h, cand)
@@ -105,17 +113,25 @@ def test_ragged_serving_loop():
             got_lse = lse.cpu().numpy()
             rng = np.random.default_rng(t)
             tail_v_nat = W.v_natural(tail_v)
-            for b, h in [(int(rng.integers(B)), int(rng.integers(s.Hq))) for _ in range(3)]:
-                kvh = h // s.G
+            if t in (0, STEPS - 1):  # every head of every sequence
+                heads = {(b, kvh): list(range(s.G)) for b in range(B) for kvh in range(Hkv)}
+            else:  # 8 sampled heads
+                heads = {}
+                for _ in range(8):
+                    b, h = int(rng.integers(B)), int(rng.integers(s.Hq))
+                    heads.setdefault((b, h // s.G), []).append(h % s.G)
+            for (b, kvh), js in heads.items():
                 L = int(lens0[b] + tail_len[b])
                 kp, vp = _pair_cache(init_k, init_v_nat, tail_k, tail_v_nat, b, kvh, int(lens0[b]),
                                      int(tail_len[b]))
-                ref, ref_lse = _ref_gqa(q_h, kst, vst, kp, vp, b, h, kvh, L, s)
-                e = np.abs(got[b, :, h] - ref)
-                worst = max(worst, float(e.max()))
-                assert e.max() <= TOL["bf16"]["max_abs"], f"step {t} (b={b}, h={h}) max-abs {e.max()}"
-                assert e.sum() / np.abs(ref).sum() <= TOL["bf16"]["mean_rel"]
-                assert abs(got_lse[b, h] - ref_lse).max() <= TOL["bf16"]["lse"]
+                ref, ref_lse = _ref_pair(q_h, kst, vst, kp, vp, b, kvh, L, s, sorted(set(js)))
+                for j in sorted(set(js)):
+                    h = kvh * s.G + j
+                    e = np.abs(got[b, :, h] - ref[:, j])
+                    worst = max(worst, float(e.max()))
+                    assert e.max() <= TOL["bf16"]["max_abs"], f"step {t} (b={b}, h={h}) max-abs {e.max()}"
+                    assert e.sum() / np.abs(ref[:, j]).sum() <= TOL["bf16"]["mean_rel"]
+                    assert abs(got_lse[b, h] - ref_lse[j]).max() <= TOL["bf16"]["lse"]
 
         # oracle: commit into its own tail, one sequence window at a time
         for b in range(B):
@@ -150,11 +166,11 @@ def test_ragged_serving_loop():
         assert np.array_equal(gv[b, :, L0:L0 + n], tv[b, :, :n])
 
 
-def _ref_gqa(q_h, kst, vst, kp, vp, b, h, kvh, L, s):
-    """Oracle attention of one query head against one (b, kvh) cache."""
+def _ref_pair(q_h, kst, vst, kp, vp, b, kvh, L, s, js):
+    """Oracle attention of query heads kvh*G + j (j in js) against one
+    (b, kvh) cache: out [R][G][D], lse [G][R] (rows of other heads NaN)."""
     G = s.G
-    j = h % G
     q1 = q_h[b:b + 1, :, kvh * G:(kvh + 1) * G]
     ref, ref_lse = oracle.attention_ref(q1, kst[b:b + 1, :, kvh:kvh + 1], vst[b:b + 1, :, kvh:kvh + 1], kp, vp, [L],
-                                        s.k, s.n_groups, s.sm_scale, pairs=[(0, j)])
-    return ref[0, :, j], ref_lse[0, j]
+                                        s.k, s.n_groups, s.sm_scale, pairs=[(0, j) for j in js])
+    return ref[0], ref_lse[0]

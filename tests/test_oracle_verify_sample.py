@@ -7,6 +7,7 @@ a 1e-4 false-alarm level; all seeds are fixed, so the tests are
 deterministic), plus the low-temperature limit, which must reproduce the
 greedy oracle.
 """
+import math
 import os
 
 import numpy as np
@@ -109,3 +110,72 @@ def test_proposal_equal_to_target_keeps_every_candidate():
     cand = rng.integers(0, V, size=(B, k)).astype(np.int32)
     a, _ = vs.verify_sample_ref(ar, ar[:, :k], rng.normal(size=(B, k, k, V)), cand, 0.7, seed=4, step=2)
     assert a.tolist() == [k] * B
+
+
+# --- _residual_margin: the gap of a residual draw under the worst-case
+# precision loss of p - q (the decision the sampling parity test may exempt)
+
+def test_residual_margin_hand_value():
+    """w = max(0, p - q) = (0.5, 0.25) with u = e^-1 (Gumbel noise 0 for both
+    entries): the drawn entry 0 loses 1e-4 * (p0 + q0) = 1e-4, entry 1 gains
+    1e-4 * (p1 + q1) = 2.5e-5, so the margin is ln(0.4999 / 0.250025)."""
+    p = np.array([0.75, 0.25])
+    q = np.array([0.25, 0.0])
+    w = np.maximum(0.0, p - q)
+    u = np.full(2, np.exp(-1.0))
+    got = vs._residual_margin(w, p, q, u, 0)
+    assert abs(got - math.log(0.4999 / 0.250025)) < 1e-12
+
+
+def test_residual_margin_is_worst_case_brute_force():
+    """Positive exactly when the drawn entry stays the Gumbel argmax after
+    every weight moves by up to eps*(p+q) against it; never above the plain
+    gap; and random perturbations inside that box never change a draw the
+    margin calls safe."""
+    rng = np.random.default_rng(3)
+    eps = vs.RESIDUAL_EPS
+    for trial in range(300):
+        V = int(rng.integers(2, 7))
+        p = rng.dirichlet(np.ones(V))
+        q = p + rng.normal(0, 10 ** rng.uniform(-6, -1), V)  # near-cancelling at times
+        q = np.abs(q) / np.abs(q).sum()
+        w = np.maximum(0.0, p - q)
+        if not w.sum() > 0:
+            continue
+        u = rng.uniform(0.01, 0.99, V)
+        G = -np.log(-np.log(u))
+        with np.errstate(divide="ignore"):
+            first = int(np.argmax(np.log(w) + G))
+        m = vs._residual_margin(w, p, q, u, first)
+        # worst case written out entry by entry
+        wc = w + eps * (p + q)
+        wc[first] = w[first] - eps * (p[first] + q[first])
+        if wc[first] > 0:
+            with np.errstate(divide="ignore"):
+                s = np.log(wc) + G
+            survives = all(s[first] > s[v] for v in range(V) if v != first)
+        else:
+            survives = False
+        assert (m > 0) == survives, (trial, m, survives)
+        _, _, plain = vs.gumbel_top2(w, u)
+        assert m <= plain + 1e-12
+        if m > 0:
+            for _ in range(20):
+                wp = np.maximum(w + rng.uniform(-1, 1, V) * eps * (p + q), 0.0)
+                with np.errstate(divide="ignore"):
+                    assert int(np.argmax(np.log(wp) + G)) == first
+
+
+def test_residual_margin_without_slack_is_the_plain_gap(monkeypatch):
+    rng = np.random.default_rng(4)
+    monkeypatch.setattr(vs, "RESIDUAL_EPS", 0.0)
+    for _ in range(50):
+        V = 9
+        p = rng.dirichlet(np.ones(V))
+        q = rng.dirichlet(np.ones(V))
+        w = np.maximum(0.0, p - q)
+        if not w.sum() > 0:
+            continue
+        u = rng.uniform(0.01, 0.99, V)
+        first, _, gap = vs.gumbel_top2(w, u)
+        assert abs(vs._residual_margin(w, p, q, u, first) - gap) < 1e-12
