@@ -277,7 +277,7 @@ def summarize(dirname):
 
     def per_dispatch(counter, kernel_key):
         vals = [float(r["Counter_Value"]) for r in _csv_rows(os.path.join(dirname, f"pmc_{counter}", "*counter_collection.csv"))
-                if kernel_key in r["Kernel_Name"]]
+                if kernel_key in r["Kernel_Name"] and "merge" not in r["Kernel_Name"]]
         return statistics.mean(vals) if vals else None, len(vals)
 
     def copy_factor(counter):
@@ -287,8 +287,8 @@ def summarize(dirname):
         return (COPY_CALIB_BYTES / 1024.0) / statistics.mean(vals)
 
     f_fetch, f_write = copy_factor("FETCH_SIZE"), copy_factor("WRITE_SIZE")
-    fetch, nf = per_dispatch("FETCH_SIZE", "attn_pipe_bf16")
-    write, nw = per_dispatch("WRITE_SIZE", "attn_pipe_bf16")
+    fetch, nf = per_dispatch("FETCH_SIZE", "attn_")
+    write, nw = per_dispatch("WRITE_SIZE", "attn_")
     hbm = fetch * 1024 * f_fetch + write * 1024 * f_write
     out = ["# HBM traffic of the step-attention kernel, 8B-shaped workload (rocprofv3 counters)",
            "# Commands (from the repository root, MI355X), one counter per run:",

@@ -486,60 +486,83 @@ void attn_pp_kernel(AttnArgs a) {
   }
 
   if (j0 < n) {
-    // ring prologue: K(j0), K(j0+1), V(j0), K(j0+2), V(j0+1) -- the loads the
-    // M phases of iterations j0-3 .. j0-1 would issue
+    // One workgroup barrier per key tile.  Between barriers B(j-1) and B(j)
+    // group 0 runs C(j) then M(j) and group 1 runs M(j-1) then C(j), so the
+    // two waves of a SIMD alternate between MFMA and softmax work without
+    // a second rendezvous.  C(j): S(j) and P.V(j-1); M(i): softmax(i).
+    // Direct loads: each tile's parts are spread over all eight waves; group
+    // 0 issues K(i+3), V(i+2) in iteration i, group 1 K(i+2), V(i+1), into
+    // ring slots whose last reader finished before B(i-1).  Before B(j) a
+    // wave waits for its parts of K(j+1) and V(j), so C(j+1) reads complete
+    // tiles.
     barrier();  // slots of the exact path are free
-    // the loads of M(i): K(i+3), V(i+2)
-    auto issue_step = [&](int i) __attribute__((always_inline)) {
-      if (i + 3 >= j0 && i + 3 < n) issue_k<D, PPW>(kslot(i + 3), kv.ktile(tb + i + 3), plan, wave);
-      if (i + 2 >= j0 && i + 2 < n) issue_v<D, PPW>(vslot(i + 2), kv.vtile(tb + i + 2), plan, wave);
+    auto kt_of = [&](int i) __attribute__((always_inline)) { return grp == 0 ? i + 3 : i + 2; };
+    auto issue_g = [&](int i) __attribute__((always_inline)) {
+      const int tk = kt_of(i), tv = tk - 1;
+      if (tk >= j0 && tk < n) issue_k<D, PPW>(kslot(tk), kv.ktile(tb + tk), plan, wave);
+      if (tv >= j0 && tv < n) issue_v<D, PPW>(vslot(tv), kv.vtile(tb + tv), plan, wave);
     };
-    // direct loads a wave issues in M(i)
+    // direct loads this wave issues in iteration i
     auto cnt = [&](int i) __attribute__((always_inline)) {
-      return T::NKW * (i + 3 >= j0 && i + 3 < n) + T::NVW * (i + 2 >= j0 && i + 2 < n);
+      const int tk = kt_of(i), tv = tk - 1;
+      return T::NKW * (tk >= j0 && tk < n) + T::NVW * (tv >= j0 && tv < n);
     };
-    issue_step(j0 - 3);
-    issue_step(j0 - 2);
-    issue_step(j0 - 1);
-    wait_vmcnt_dyn(cnt(j0 - 2) + cnt(j0 - 1));  // K(j0) has landed
+    // loads still allowed in flight before B(i): those issued after the
+    // ones of K(i+1) and V(i)
+    auto wait_parts = [&](int i) __attribute__((always_inline)) {
+      wait_vmcnt_dyn(grp == 0 ? cnt(i - 1) + cnt(i) : cnt(i));
+    };
+    // ring prologue: the loads of iterations j0-3 .. j0-1
+    issue_g(j0 - 3);
+    issue_g(j0 - 2);
+    issue_g(j0 - 1);
+    wait_parts(j0 - 1);  // K(j0) has landed
     barrier();
 
     // the shared tile's P^T buffer of key tile i
     auto sPb = [&](int i) __attribute__((always_inline)) { return sP0 + (i & 1) * (2 * 64 * 16); };
     bool big = false;
+    auto softmax = [&](auto grp_c, int i) __attribute__((always_inline)) {
+      constexpr int G = decltype(grp_c)::value;
+      const float sum = pp_softmax(s, st.m, sl2, p);
+      big |= sum > kSumLimit;
+      st.l += sum;
+      if (G == 0 && SH) {
+        const float sum_s = pp_softmax_shared(ss, st.ms, sl2, sPb(i), lane, simd);
+        big |= sum_s > kSumLimit;
+        st.ls += sum_s;
+      }
+    };
+    auto cphase = [&](auto grp_c, int j) __attribute__((always_inline)) {
+      constexpr int G = decltype(grp_c)::value;
+      __builtin_amdgcn_s_setprio(1);
+      if (j > j0)
+        pp_c_phase<D, G, SH, true, true, kPpDepth>(kslot(j), vslot(j - 1), sPb(j - 1), q, qs, s, ss, p, st, lane, simd);
+      else
+        pp_c_phase<D, G, SH, true, false, kPpDepth>(kslot(j), vslot(j), sPb(0), q, qs, s, ss, p, st, lane, simd);
+      __builtin_amdgcn_s_setprio(0);
+    };
     auto loop = [&](auto grp_c) __attribute__((always_inline)) {
       constexpr int G = decltype(grp_c)::value;
-      if (G == 1) barrier();  // group 1 runs half a tile behind
       for (int j = j0; j < n; ++j) {
-        // C(j): S(j); P.V(j-1)
-        __builtin_amdgcn_s_setprio(1);
-        if (j > j0)
-          pp_c_phase<D, G, SH, true, true, kPpDepth>(kslot(j), vslot(j - 1), sPb(j - 1), q, qs, s, ss, p, st, lane, simd);
-        else
-          pp_c_phase<D, G, SH, true, false, kPpDepth>(kslot(j), vslot(j), sPb(0), q, qs, s, ss, p, st, lane, simd);
-        __builtin_amdgcn_s_setprio(0);
-        if (G == 1) wait_vmcnt_dyn(cnt(j - 1));  // K(j+1), V(j) have landed
-        wait_lgkmcnt0();
-        barrier();
-        // M(j): softmax(j); loads of K(j+3), V(j+2)
-        issue_step(j);
-        const float sum = pp_softmax(s, st.m, sl2, p);
-        big |= sum > kSumLimit;
-        st.l += sum;
-        if (G == 0 && SH) {
-          const float sum_s = pp_softmax_shared(ss, st.ms, sl2, sPb(j), lane, simd);
-          big |= sum_s > kSumLimit;
-          st.ls += sum_s;
+        if (G == 0) {
+          cphase(grp_c, j);
+          softmax(grp_c, j);
+          issue_g(j);
+        } else {
+          if (j > j0) softmax(grp_c, j - 1);
+          issue_g(j);
+          cphase(grp_c, j);
         }
-        if (G == 0) wait_vmcnt_dyn(cnt(j - 1) + cnt(j));  // K(j+1), V(j) have landed
+        wait_parts(j);
         wait_lgkmcnt0();
         barrier();
       }
-      // C(n): P.V(n-1)
+      // P.V(n-1)
+      if (G == 1) softmax(grp_c, n - 1);
       __builtin_amdgcn_s_setprio(1);
       pp_c_phase<D, G, SH, false, true, kPpDepth>(kslot(n), vslot(n - 1), sPb(n - 1), q, qs, s, ss, p, st, lane, simd);
       __builtin_amdgcn_s_setprio(0);
-      if (G == 0) barrier();
     };
     if (grp == 0) loop(std::integral_constant<int, 0>{});
     else loop(std::integral_constant<int, 1>{});
