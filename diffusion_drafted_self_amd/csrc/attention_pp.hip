@@ -497,10 +497,11 @@ void attn_pp_kernel(AttnArgs a) {
     // tiles.
     barrier();  // slots of the exact path are free
     auto kt_of = [&](int i) __attribute__((always_inline)) { return grp == 0 ? i + 3 : i + 2; };
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // LDS destinations in scalar registers
     auto issue_g = [&](int i) __attribute__((always_inline)) {
       const int tk = kt_of(i), tv = tk - 1;
-      if (tk >= j0 && tk < n) issue_k<D, PPW>(kslot(tk), kv.ktile(tb + tk), plan, wave);
-      if (tv >= j0 && tv < n) issue_v<D, PPW>(vslot(tv), kv.vtile(tb + tv), plan, wave);
+      if (tk >= j0 && tk < n) issue_k<D, PPW>(kslot(tk), kv.ktile(tb + tk), plan, wave_s);
+      if (tv >= j0 && tv < n) issue_v<D, PPW>(vslot(tv), kv.vtile(tb + tv), plan, wave_s);
     };
     // direct loads this wave issues in iteration i
     auto cnt = [&](int i) __attribute__((always_inline)) {
@@ -521,17 +522,10 @@ void attn_pp_kernel(AttnArgs a) {
 
     // the shared tile's P^T buffer of key tile i
     auto sPb = [&](int i) __attribute__((always_inline)) { return sP0 + (i & 1) * (2 * 64 * 16); };
-    bool big = false;
     auto softmax = [&](auto grp_c, int i) __attribute__((always_inline)) {
       constexpr int G = decltype(grp_c)::value;
-      const float sum = pp_softmax(s, st.m, sl2, p);
-      big |= sum > kSumLimit;
-      st.l += sum;
-      if (G == 0 && SH) {
-        const float sum_s = pp_softmax_shared(ss, st.ms, sl2, sPb(i), lane, simd);
-        big |= sum_s > kSumLimit;
-        st.ls += sum_s;
-      }
+      st.l += pp_softmax(s, st.m, sl2, p);
+      if (G == 0 && SH) st.ls += pp_softmax_shared(ss, st.ms, sl2, sPb(i), lane, simd);
     };
     auto cphase = [&](auto grp_c, int j) __attribute__((always_inline)) {
       constexpr int G = decltype(grp_c)::value;
@@ -542,22 +536,40 @@ void attn_pp_kernel(AttnArgs a) {
         pp_c_phase<D, G, SH, true, false, kPpDepth>(kslot(j), vslot(j), sPb(0), q, qs, s, ss, p, st, lane, simd);
       __builtin_amdgcn_s_setprio(0);
     };
+    // one iteration; STEADY: every load of iterations j-1 and j exists
+    // (j + 3 < n), so the loads go out unconditionally and the waits are
+    // constants
+    auto iter = [&](auto grp_c, auto steady_c, int j) __attribute__((always_inline)) {
+      constexpr int G = decltype(grp_c)::value;
+      constexpr bool STEADY = decltype(steady_c)::value;
+      auto issue = [&]() __attribute__((always_inline)) {
+        if (STEADY) {
+          const int tk = G == 0 ? j + 3 : j + 2;
+          issue_k<D, PPW>(kslot(tk), kv.ktile(tb + tk), plan, wave_s);
+          issue_v<D, PPW>(vslot(tk - 1), kv.vtile(tb + tk - 1), plan, wave_s);
+        } else {
+          issue_g(j);
+        }
+      };
+      if (G == 0) {
+        cphase(grp_c, j);
+        softmax(grp_c, j);
+        issue();
+      } else {
+        if (j > j0) softmax(grp_c, j - 1);
+        issue();
+        cphase(grp_c, j);
+      }
+      if (STEADY) wait_vmcnt<(G == 0 ? 2 : 1) * (T::NKW + T::NVW)>();
+      else wait_parts(j);
+      wait_lgkmcnt0();
+      barrier();
+    };
     auto loop = [&](auto grp_c) __attribute__((always_inline)) {
       constexpr int G = decltype(grp_c)::value;
-      for (int j = j0; j < n; ++j) {
-        if (G == 0) {
-          cphase(grp_c, j);
-          softmax(grp_c, j);
-          issue_g(j);
-        } else {
-          if (j > j0) softmax(grp_c, j - 1);
-          issue_g(j);
-          cphase(grp_c, j);
-        }
-        wait_parts(j);
-        wait_lgkmcnt0();
-        barrier();
-      }
+      int j = j0;
+      for (; j + 3 < n; ++j) iter(grp_c, std::true_type{}, j);
+      for (; j < n; ++j) iter(grp_c, std::false_type{}, j);
       // P.V(n-1)
       if (G == 1) softmax(grp_c, n - 1);
       __builtin_amdgcn_s_setprio(1);
@@ -566,6 +578,11 @@ void attn_pp_kernel(AttnArgs a) {
     };
     if (grp == 0) loop(std::integral_constant<int, 0>{});
     else loop(std::integral_constant<int, 1>{});
+    // A tile whose sum of p passed 2^64 leaves the row's total above it (the
+    // sums only grow, and an infinite or NaN sum fails the test too): one
+    // test after the loop.
+    bool big = !(st.l <= kSumLimit);
+    if (SH && grp == 0) big |= !(st.ls <= kSumLimit);
     if (__any(big)) ovf_flag = 1;
     wait_all();
     barrier();
