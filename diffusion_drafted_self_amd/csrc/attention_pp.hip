@@ -47,7 +47,7 @@ namespace {
 
 constexpr int PPW = 8;         // waves per workgroup, two per SIMD
 constexpr int PPT = PPW * 64;  // threads per workgroup
-constexpr int kPpDepth = 12;   // LDS operand reads in flight per wave in the MFMA phase
+constexpr int kPpDepth = 8;   // LDS operand reads in flight per wave in the MFMA phase
 
 // s_waitcnt vmcnt(n) for a wave-uniform n that is not a compile-time
 // constant (the load counts of the last ring steps).
@@ -69,7 +69,8 @@ template <int D>
 struct PpState {  // one wave's accumulators
   floatx4 o[D / 16];  // O^T of its tile: head-dim block db, rows in columns
   floatx4 os[2];      // group 1: O^T of the shared tile, head-dim blocks 2s, 2s+1
-  float m, l;         // its tile: row reference (log2 units), this lane's part of the sum
+  floatx4 lv;         // its tile: row sums of the bf16 p of the pipelined tiles (every entry)
+  float m, l;         // its tile: row reference (log2 units), this lane's part of the exact tiles' sum
   float ms, ls;       // shared tile: reference (same in every wave), group 0: its key block's sum
 };
 
@@ -149,6 +150,16 @@ __device__ __forceinline__ void pp_c_phase(const lds_char* sK, const lds_char* s
   bf16x8 fr[DEPTH + 1];
 #pragma unroll
   for (int i = 0; i < DEPTH && i < NSTEP; ++i) fr[i] = frag(i);
+  if constexpr (DO_PV) {
+    // the row sums of P: an all-ones A operand against both key steps of
+    // P^T (these need no operand read and cover the first read's latency)
+    bf16x8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.f;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) st.lv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, p[kc], st.lv, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int i = 0; i < NSTEP; ++i) {
     if (i + DEPTH < NSTEP) fr[(i + DEPTH) % (DEPTH + 1)] = frag(i + DEPTH);
@@ -167,8 +178,10 @@ __device__ __forceinline__ void pp_c_phase(const lds_char* sK, const lds_char* s
 }
 
 // Softmax of one tile's scores against the held reference m: p =
-// exp2(scale_log2 * s - m), this lane's sum of p, P^T packed to bf16 in the
-// B-operand layout of P.V.  Returns this lane's tile sum.
+// exp2(scale_log2 * s - m), P^T packed to bf16 in the B-operand layout of
+// P.V.  SUM: also returns this lane's sum of p (the pipelined tiles take
+// their sums on the matrix cores instead, from the packed p).
+template <bool SUM = true>
 __device__ __forceinline__ float pp_softmax(const floatx4 (&s)[4], float m, float sl2, bf16x8 (&p)[2]) {
   float sum = 0.f;
 #pragma unroll
@@ -177,7 +190,7 @@ __device__ __forceinline__ float pp_softmax(const floatx4 (&s)[4], float m, floa
     for (int v = 0; v < 4; v += 2) {
       const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb4][v], sl2, -m));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb4][v + 1], sl2, -m));
-      sum += p0 + p1;
+      if (SUM) sum += p0 + p1;
       p[kb4 >> 1][4 * (kb4 & 1) + v] = (bf16)p0;
       p[kb4 >> 1][4 * (kb4 & 1) + v + 1] = (bf16)p1;
     }
@@ -357,6 +370,7 @@ void attn_pp_kernel(AttnArgs a) {
     st.os[0] = st.os[1] = (floatx4){0.f, 0.f, 0.f, 0.f};
     st.m = st.ms = kNoMax;
     st.l = st.ls = 0.f;
+    st.lv = (floatx4){0.f, 0.f, 0.f, 0.f};
   };
   reset();
   const float sl2 = a.scale_log2;
@@ -403,6 +417,7 @@ void attn_pp_kernel(AttnArgs a) {
       const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
       st.m = m_new;
       st.l *= alpha;
+      st.lv *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 16; ++db)
 #pragma unroll
@@ -524,7 +539,7 @@ void attn_pp_kernel(AttnArgs a) {
     auto sPb = [&](int i) __attribute__((always_inline)) { return sP0 + (i & 1) * (2 * 64 * 16); };
     auto softmax = [&](auto grp_c, int i) __attribute__((always_inline)) {
       constexpr int G = decltype(grp_c)::value;
-      st.l += pp_softmax(s, st.m, sl2, p);
+      pp_softmax<false>(s, st.m, sl2, p);
       if (G == 0 && SH) st.ls += pp_softmax_shared(ss, st.ms, sl2, sPb(i), lane, simd);
     };
     auto cphase = [&](auto grp_c, int j) __attribute__((always_inline)) {
@@ -581,7 +596,7 @@ void attn_pp_kernel(AttnArgs a) {
     // A tile whose sum of p passed 2^64 leaves the row's total above it (the
     // sums only grow, and an infinite or NaN sum fails the test too): one
     // test after the loop.
-    bool big = !(st.l <= kSumLimit);
+    bool big = !(st.l <= kSumLimit) || !(st.lv[0] <= kSumLimit);
     if (SH && grp == 0) big |= !(st.ls <= kSumLimit);
     if (__any(big)) ovf_flag = 1;
     wait_all();
@@ -613,7 +628,7 @@ void attn_pp_kernel(AttnArgs a) {
     }
     if (a.lse && lse_lane) *lse_at(m) = (m_ref + log2f(l_tot)) * kLn2;
   };
-  const float l_row = row4_sum(st.l);  // every lane takes part in the swaps
+  const float l_row = row4_sum(st.l) + st.lv[0];  // every lane takes part in the swaps
   if (ok) emit(mrow, st.o, 0, D / 16, st.m, l_row, hi == 0);
   if (SH) {
     wait_all();
