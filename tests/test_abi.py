@@ -34,6 +34,24 @@ def test_exports_every_declared_symbol(T):
         assert getattr(raw, n) is not None
 
 
+def _prototypes():
+    """(name, parameter count) of every prototype the header declares."""
+    text = open(os.path.join(ROOT, "include", "tidar.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(tidar_\w+)\s*\(([^)]*)\)\s*;", text):
+        params = m.group(2).strip()
+        out[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_signatures_match_the_header(T):
+    protos = _prototypes()
+    assert set(protos) == set(T.SIGNATURES)
+    for name, (_, args) in T.SIGNATURES.items():
+        assert len(args) == protos[name], f"{name}: binding has {len(args)} arguments, header {protos[name]}"
+
+
 def test_strerror_and_version(T):
     assert T.lib().tidar_abi_version() == 1
     for code in (0, -1, -2, -3, -4, 7):
