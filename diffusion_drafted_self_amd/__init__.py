@@ -59,6 +59,7 @@ SIGNATURES = {
     "tidar_verify_commit_state_bytes": (_c_int, [_c_int] * 2 + [ctypes.POINTER(_c_size)]),
     "tidar_verify_commit_greedy": (_c_int, [_c_int] * 8 + [_p] * 12 + [_c_size, _p]),
     "tidar_verify_commit_greedy_paged": (_c_int, [_c_int] * 9 + [_p] * 13 + [_c_size, _p]),
+    "tidar_verify_commit_greedy_noalloc": (_c_int, [_c_int] * 8 + [_p] * 11 + [_p]),
     "tidar_launch_shapes": (_c_int, [_c_int] * 7 + [ctypes.POINTER(_c_int)]),
     "tidar_read_probe": (_c_int, [_p, _c_size, _p, _p]),
 }
@@ -593,6 +594,48 @@ def verify_commit_greedy(ar_logits, draft_logits, cand, k_cache, v_cache, lens, 
                                            _ptr(draft_logits), _ptr(cand), _ptr(k_cache), _ptr(v_cache), _ptr(lens),
                                            _ptr(k_step), _ptr(v_step), _ptr(accept_len), _ptr(next_cand),
                                            _ptr(err_flags), _ptr(state), state.numel(), _stream()))
+    return accept_len, next_cand
+
+
+def verify_commit_greedy_noalloc(ar_logits, draft_logits, cand, k_cache, v_cache, lens, k_step, v_step,
+                                 accept_len, next_cand, err_flags=None):
+    """verify_commit_greedy with the library's own per-GPU state: nothing is
+    allocated, so the outputs must be given.  Calls that may overlap on one
+    GPU race.  Returns (accept_len, next_cand)."""
+    _need(k_cache, "k_cache", ndim=4)
+    dev, dt = k_cache.device, k_cache.dtype
+    B, Hkv, S_max, D = k_cache.shape
+    _need(v_cache, "v_cache", dt, 5, dev)
+    _need(k_step, "k_step", dt, 4, dev)
+    _need(v_step, "v_step", dt, 4, dev)
+    _need(lens, "lens", torch.int32, 1, dev)
+    R = k_step.shape[1]
+    _check_caches(k_cache, v_cache, B, Hkv, S_max, D)
+    if tuple(k_step.shape) != (B, R, Hkv, D) or tuple(v_step.shape) != (B, R, Hkv, D):
+        raise ValueError("k_step/v_step must be [B][R][Hkv][D]")
+    k = cand.shape[1]
+    if accept_len is None or next_cand is None:
+        raise ValueError("accept_len and next_cand must be given (this call allocates nothing)")
+    _need(ar_logits, "ar_logits", torch.float32, 3, dev)
+    if tuple(ar_logits.shape[:2]) != (B, k + 1):
+        raise ValueError("ar_logits must be [B][k+1][V]")
+    V = ar_logits.shape[2]
+    _need(cand, "cand", torch.int32, 2, dev)
+    if cand.shape[0] != B:
+        raise ValueError("cand must be [B][k]")
+    if k > 1 or draft_logits is not None:
+        _need(draft_logits, "draft_logits", torch.float32, 4, dev)
+        if tuple(draft_logits.shape) != (B, k, k, V):
+            raise ValueError("draft_logits must be [B][k][k][V]")
+    _need(accept_len, "accept_len", torch.int32, 1, dev)
+    _need(next_cand, "next_cand", torch.int32, 2, dev)
+    if err_flags is not None:
+        _need(err_flags, "err_flags", torch.int32, 1, dev)
+    _check("tidar_verify_commit_greedy_noalloc",
+           lib().tidar_verify_commit_greedy_noalloc(_dtype_code(k_cache), B, Hkv, D, S_max, R, k, V,
+                                                   _ptr(ar_logits), _ptr(draft_logits), _ptr(cand), _ptr(k_cache),
+                                                   _ptr(v_cache), _ptr(lens), _ptr(k_step), _ptr(v_step),
+                                                   _ptr(accept_len), _ptr(next_cand), _ptr(err_flags), _stream()))
     return accept_len, next_cand
 
 

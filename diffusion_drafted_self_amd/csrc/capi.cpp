@@ -733,6 +733,25 @@ int tidar_verify_commit_greedy(int dtype, int B, int Hkv, int D, int S_max, int 
                             state_bytes, stream);
 }
 
+int tidar_verify_commit_greedy_noalloc(int dtype, int B, int Hkv, int D, int S_max, int R, int k, int V,
+                                       const float* ar_logits, const float* draft_logits, const int32_t* cand,
+                                       void* k_cache, void* v_cache, int32_t* lens, const void* k_step,
+                                       const void* v_step, int32_t* accept_len, int32_t* next_cand,
+                                       int32_t* err_flags, void* stream) {
+  FusedPlan fp;
+  const int pst = plan_fused(B, k, &fp);
+  if (pst != TIDAR_OK) return pst;
+  if (fp.total > tidar::kNoAllocScratchBytes) return TIDAR_EWORKSPACE;
+  if (B == 0) return TIDAR_OK;
+  void* state = nullptr;
+  if (tidar::noalloc_scratch(static_cast<hipStream_t>(stream), &state) != hipSuccess) return TIDAR_ELAUNCH;
+  const int st = verify_commit_impl(dtype, B, Hkv, D, S_max, R, k, V, ar_logits, draft_logits, cand, k_cache,
+                                    v_cache, nullptr, 0, 0, lens, k_step, v_step, accept_len, next_cand, err_flags,
+                                    state, tidar::kNoAllocScratchBytes, stream);
+  if (st == TIDAR_ELAUNCH) tidar::noalloc_scratch_dirty();  // part of the state may be left set
+  return st;
+}
+
 int tidar_verify_commit_greedy_paged(int dtype, int B, int Hkv, int D, int max_pages, int n_pages, int R, int k,
                                      int V, const float* ar_logits, const float* draft_logits,
                                      const int32_t* cand, void* k_pool, void* v_pool, const int32_t* block_table,

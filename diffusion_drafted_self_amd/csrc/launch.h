@@ -106,6 +106,14 @@ struct FusedVerifyGeometry {
 FusedVerifyGeometry fused_verify_geometry(int B, int k, int V);
 int fused_launch_shapes(int B, int k, int V, LaunchShape* out);
 hipError_t launch_fused_verify(const FusedVerifyArgs& a, hipStream_t s);
+
+// The allocation-free entry point's state: a file-scope device array per
+// GPU.  noalloc_scratch gives its device address on the current device
+// (clearing it on stream s first when it is not known to be zero);
+// noalloc_scratch_dirty marks it for clearing after a failed launch.
+constexpr size_t kNoAllocScratchBytes = size_t(2) << 20;
+hipError_t noalloc_scratch(hipStream_t s, void** out);
+void noalloc_scratch_dirty();
 hipError_t launch_verify_select(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_draft_finalize(const VerifyArgs& a, hipStream_t s);
 

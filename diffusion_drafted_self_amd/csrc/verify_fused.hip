@@ -30,10 +30,16 @@
 // calls (each call leaves them so; the memory must be zero before its
 // first use).
 #include <algorithm>
+#include <mutex>
 
 #include "argmax_block.h"
 #include "common.h"
 #include "launch.h"
+
+// State of the allocation-free entry point: one array per GPU, alive until
+// the process ends.  Host code never names it except in the address lookup
+// below: its host-side symbol is not the device address.
+static __device__ __align__(256) unsigned char scratch[tidar::kNoAllocScratchBytes];
 
 namespace tidar {
 
@@ -236,6 +242,54 @@ int fused_launch_shapes(int B, int k, int V, LaunchShape* out) {
   out[1] = {g.draft_grid_x, g.draft_grid_y, g.block};
   out[2] = {B, 1, 64};  // one wave per sequence; k + 1 <= 17 lanes hold the row keys
   return 3;
+}
+
+namespace {
+
+__global__ __launch_bounds__(256) void zero_kernel(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  void* ptr = nullptr;  // device address of `scratch` on this device
+  bool zero = false;    // known to be all zero once the work already enqueued on it has run
+};
+std::mutex g_scratch_mu;
+ScratchSlot g_scratch[kMaxDevices];
+
+}  // namespace
+
+hipError_t noalloc_scratch(hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchSlot& sl = g_scratch[dev];
+  if (!sl.ptr) {  // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    sl.ptr = p;
+  }
+  if (!sl.zero) {  // first use on this device, or after a failed launch: clear on the caller's stream
+    hipLaunchKernelGGL(zero_kernel, dim3(256), dim3(256), 0, s, static_cast<uint4*>(sl.ptr),
+                       kNoAllocScratchBytes / 16);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    sl.zero = true;
+  }
+  *out = sl.ptr;
+  return hipSuccess;
+}
+
+void noalloc_scratch_dirty() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  g_scratch[dev].zero = false;
 }
 
 hipError_t launch_fused_verify(const FusedVerifyArgs& a, hipStream_t s) {

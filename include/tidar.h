@@ -422,6 +422,27 @@ int tidar_verify_commit_greedy(int dtype, int B, int Hkv, int D, int S_max, int 
                                int32_t* accept_len, int32_t* next_cand, int32_t* err_flags,
                                void* state, size_t state_bytes, void* stream);
 
+/* tidar_verify_commit_greedy for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and results without `state`.  Its state is
+ * a 2 MiB array inside the library, one per GPU, held until the process
+ * ends; this call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).  The first call on a GPU, and the first after a call
+ * that returned TIDAR_ELAUNCH, also enqueue a clearing kernel before the
+ * three of the step.
+ *   Returns TIDAR_EWORKSPACE when tidar_verify_commit_state_bytes(B, k)
+ *   exceeds 2 MiB (2097152 bytes), before anything is enqueued; otherwise
+ *   what tidar_verify_commit_greedy returns.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (two streams, two host threads) race and must be serialised by the
+ * caller. */
+int tidar_verify_commit_greedy_noalloc(int dtype, int B, int Hkv, int D, int S_max, int R, int k, int V,
+                                       const float* ar_logits, const float* draft_logits,
+                                       const int32_t* cand, void* k_cache, void* v_cache, int32_t* lens,
+                                       const void* k_step, const void* v_step,
+                                       int32_t* accept_len, int32_t* next_cand, int32_t* err_flags,
+                                       void* stream);
+
 /* The same into a paged cache (flags as for tidar_kv_commit_paged; 3: a
  * needed page entry outside [0, n_pages)). */
 int tidar_verify_commit_greedy_paged(int dtype, int B, int Hkv, int D, int max_pages, int n_pages, int R, int k,
