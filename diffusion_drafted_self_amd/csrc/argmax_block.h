@@ -13,13 +13,15 @@ namespace tidar {
 namespace {
 
 // (value, index) of the chunk [lo, hi) of row `src` (V entries); the result
-// is valid in thread 0.  With chunk_elems == kArgmaxChunk every thread issues
-// its loads first (their latencies overlap; nontemporal: each logit is read
-// once), then compares in ascending index order (strict '>' keeps the lowest
-// index), so the wave and workgroup reductions see each thread's first
-// maximum.
+// is valid in thread 0.  With chunk_elems == SPAN every thread issues its
+// loads first (SPAN / 256 values; their latencies overlap; nontemporal: each
+// logit is read once), then compares in ascending index order (strict '>'
+// keeps the lowest index), so the wave and workgroup reductions see each
+// thread's first maximum.
+template <int SPAN = kArgmaxChunk>
 __device__ __forceinline__ void block_chunk_argmax(const float* src, int lo, int hi, int V, int chunk_elems,
                                                    float& out_v, int& out_i) {
+  static_assert(SPAN % 1024 == 0, "whole float4 rounds of 256 threads");
   __shared__ float sv[4];
   __shared__ int si[4];
   float bv = -INFINITY;
@@ -30,17 +32,17 @@ __device__ __forceinline__ void block_chunk_argmax(const float* src, int lo, int
       bi = i;
     }
   };
-  if (chunk_elems == kArgmaxChunk) {
+  if (chunk_elems == SPAN) {
     if ((V & 3) == 0) {
-      floatx4 x[kArgmaxChunk / 1024];
+      floatx4 x[SPAN / 1024];
 #pragma unroll
-      for (int j = 0; j < kArgmaxChunk / 1024; ++j) {
+      for (int j = 0; j < SPAN / 1024; ++j) {
         const int i = lo + 4 * (int)threadIdx.x + 1024 * j;
         x[j] = i < hi ? __builtin_nontemporal_load((const floatx4*)(src + i))
                       : (floatx4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       }
 #pragma unroll
-      for (int j = 0; j < kArgmaxChunk / 1024; ++j) {
+      for (int j = 0; j < SPAN / 1024; ++j) {
         const int i = lo + 4 * (int)threadIdx.x + 1024 * j;
         take(x[j].x, i);
         take(x[j].y, i + 1);
@@ -48,14 +50,14 @@ __device__ __forceinline__ void block_chunk_argmax(const float* src, int lo, int
         take(x[j].w, i + 3);
       }
     } else {
-      float x[kArgmaxChunk / 256];
+      float x[SPAN / 256];
 #pragma unroll
-      for (int j = 0; j < kArgmaxChunk / 256; ++j) {
+      for (int j = 0; j < SPAN / 256; ++j) {
         const int i = lo + (int)threadIdx.x + 256 * j;
         x[j] = i < hi ? __builtin_nontemporal_load(src + i) : -INFINITY;
       }
 #pragma unroll
-      for (int j = 0; j < kArgmaxChunk / 256; ++j) take(x[j], lo + (int)threadIdx.x + 256 * j);
+      for (int j = 0; j < SPAN / 256; ++j) take(x[j], lo + (int)threadIdx.x + 256 * j);
     }
   } else if ((V & 3) == 0) {
     for (int i = lo + 4 * (int)threadIdx.x; i < hi; i += 4 * 256) {

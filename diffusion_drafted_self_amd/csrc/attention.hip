@@ -969,10 +969,15 @@ __global__ __launch_bounds__(64) void attn_split_f32_kernel(AttnArgs a) {
 __device__ __forceinline__ void store_out(float* p, float x) { *p = x; }
 __device__ __forceinline__ void store_out(bf16* p, float x) { *p = (bf16)x; }
 
-// Log-sum-exp merge of the key chunks: one wave per (b, kvh, row m).
+// Log-sum-exp merge of the key chunks: one wave per (b, kvh, row m).  Lane
+// t takes chunk t (and t + 64, ...) for the reference max and the weights,
+// and the chunk outputs are read eight chunks at a time, every load of a
+// batch in flight together: the merge costs a few memory round trips
+// whatever the number of chunks, not one per chunk.
 template <typename OutT, int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   constexpr int E = D / 64;  // elements per lane
+  constexpr int NB = 8;      // chunk outputs per batch of loads
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (w >= a.B * a.Hkv * a.M) return;
@@ -1002,19 +1007,37 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const size_t base = (size_t)pr * a.n_split * a.M + m;
 
   float mx = -INFINITY;
-  for (int s = 0; s < n_valid; ++s) mx = fmaxf(mx, a.ml_part[base + (size_t)s * a.M].x);
+  for (int s = lane; s < n_valid; s += 64) mx = fmaxf(mx, a.ml_part[base + (size_t)s * a.M].x);
+  mx = wave_max(mx);
   float den = 0.f, acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int s = 0; s < n_valid; ++s) {
-    const size_t idx = base + (size_t)s * a.M;
-    const float2 ml = a.ml_part[idx];
-    const float wgt = exp2f(ml.x - mx);
-    den += wgt * ml.y;
-    const float* op = a.o_part + idx * D + lane * E;
+  for (int g0 = 0; g0 < n_valid; g0 += 64) {
+    // this lane's chunk g0 + lane: its weight (0 past the last chunk)
+    float wl = 0.f;
+    if (g0 + lane < n_valid) {
+      const float2 ml = a.ml_part[base + (size_t)(g0 + lane) * a.M];
+      wl = exp2f(ml.x - mx);
+      den = fmaf(wl, ml.y, den);
+    }
+    const int ng = min(64, n_valid - g0);
+    for (int u0 = 0; u0 < ng; u0 += NB) {
+      float o[NB][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = fmaf(wgt, op[e], acc[e]);
+      for (int u = 0; u < NB; ++u) {
+        const float* op = a.o_part + (base + (size_t)(g0 + u0 + u) * a.M) * D + lane * E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[u][e] = u0 + u < ng ? op[e] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const float wu = __shfl(wl, u0 + u);  // lanes past the last chunk hold 0
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = fmaf(wu, o[u][e], acc[e]);
+      }
+    }
   }
+  den = wave_sum(den);
   const float inv = 1.f / den;
 #pragma unroll
   for (int e = 0; e < E; ++e) store_out(orow + lane * E + e, acc[e] * inv);

@@ -317,9 +317,10 @@ int kv_commit_impl(int dtype, int B, int Hkv, int D, int S_max, int R, int k, vo
 }
 
 // State of the fused verify + commit: AR keys, then draft keys (one 8-byte
-// key per 128-byte line).
+// key per 128-byte line), then one arrival counter per sequence (one per
+// 128-byte line).
 struct FusedPlan {
-  size_t key_bytes, dkey_bytes, total;
+  size_t key_bytes, dkey_bytes, arrive_bytes, total;
 };
 
 int plan_fused(int B, int k, FusedPlan* p) {
@@ -328,7 +329,8 @@ int plan_fused(int B, int k, FusedPlan* p) {
   if ((long)B * (k + 1) > 65535) return TIDAR_EUNSUPPORTED;  // grid y limit
   p->key_bytes = round_up((size_t)B * (k + 1) * tidar::kFusedKeyBytes, 256);
   p->dkey_bytes = round_up((size_t)B * std::max(k - 1, 1) * tidar::kFusedKeyBytes, 256);
-  p->total = p->key_bytes + p->dkey_bytes;
+  p->arrive_bytes = round_up((size_t)B * tidar::kFusedKeyBytes, 256);
+  p->total = p->key_bytes + p->dkey_bytes + p->arrive_bytes;
   return TIDAR_OK;
 }
 
@@ -366,6 +368,7 @@ int verify_commit_impl(int dtype, int B, int Hkv, int D, int S_max, int R, int k
   char* ws = static_cast<char*>(state);
   a.key = reinterpret_cast<unsigned long long*>(ws);
   a.dkey = reinterpret_cast<unsigned long long*>(ws + fp.key_bytes);
+  a.arrive = reinterpret_cast<unsigned*>(ws + fp.key_bytes + fp.dkey_bytes);
   a.B = B;
   a.k = k;
   a.V = V;

@@ -83,6 +83,7 @@ struct FusedVerifyArgs {
   int32_t* next_cand;         // [B][k]
   unsigned long long* key;    // [B*(k+1)] keys, kFusedKeyBytes apart         state
   unsigned long long* dkey;   // [B*n_draft_rows] keys, kFusedKeyBytes apart  state
+  unsigned* arrive;           // [B] arrival counters, kFusedKeyBytes apart    state
   int B, k, V, n_draft_rows;  // n_draft_rows = max(k-1, 1)
   // commit (commit != 0)
   int commit;
@@ -100,7 +101,7 @@ struct FusedVerifyArgs {
 // Launch shapes of the fused path (the host checks them before launching).
 struct FusedVerifyGeometry {
   int ar_grid_x, ar_grid_y;        // (chunks, AR rows)
-  int draft_grid_x, draft_grid_y;  // (chunks, sequences x draft rows)
+  int draft_grid_x, draft_grid_y;  // (spans of kDraftSpan, sequences x draft rows)
   int draft_rows, block;
 };
 FusedVerifyGeometry fused_verify_geometry(int B, int k, int V);
@@ -136,6 +137,7 @@ hipError_t launch_read_probe(const void* src, size_t bytes, unsigned* sink, hipS
 
 constexpr int kReadProbeBlocks = 16384;  // workgroups of the streaming-read probe
 constexpr int kArgmaxChunk = 4096;  // logits per workgroup of the greedy argmax
+constexpr int kDraftSpan = 2 * kArgmaxChunk;  // logits per workgroup of the fused path's draft pass
 constexpr int kSampleChunk = 4096;  // vocabulary entries per workgroup of the sampling kernels
 
 struct SampleArgs {

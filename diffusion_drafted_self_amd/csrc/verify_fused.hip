@@ -1,5 +1,5 @@
 // Greedy verification, next-draft selection and the KV commit of one TiDAR
-// step in three launches (gfx950).
+// step in two launches (gfx950).
 //
 // The pass scores the carried candidates strictly left to right; the
 // drafts prepared for the confirmed outcome become the next candidates; the
@@ -7,28 +7,29 @@
 // evicted ("TiDAR : l'hybride de NVIDIA qui rédige par diffusion et parle de
 // manière autorégressive", nodesdaily.com, paragraphs on the three zones
 // and on drafting for every outcome).  Same results as the separate
-// verification and commit calls; three launches instead of five:
+// verification and commit calls; two launches instead of five:
 //
 //   ar_key_kernel     (chunk, AR row): the chunk's (max, lower index) folded
 //       into one 64-bit key per row by an atomic max; a key orders by value,
 //       then by lower index.
-//   draft_commit_kernel  (chunk, draft slot) per sequence: every workgroup
+//   draft_commit_kernel  (span, draft slot) per sequence: every workgroup
 //       reads the k+1 row keys of its sequence and the candidates and takes
 //       the accept length itself (72 bytes, the same in all of them),
-//       reduces its chunk of the selected group's draft row into that row's
-//       key, and copies its share of the accepted step rows into the cache.
-//   finalize_kernel   one wave per sequence: accept length, bonus token and
-//       next drafts from the keys, the new settled length, and the keys
-//       cleared for the next call.
-// Work across workgroups meets only at kernel boundaries: the atomics are
-// coherent across the XCDs, and nothing waits on another workgroup inside a
-// kernel (an in-kernel arrival counter needs a device-scope release and
-// acquire per workgroup, which write back and invalidate the XCD's L2).
+//       reduces its span (two chunks) of the selected group's draft row
+//       into that row's key, and copies its share of the accepted step rows
+//       into the cache.  The last of the sequence's workgroups to arrive
+//       then writes the accept length, bonus token and next drafts, the new
+//       settled length, and clears the sequence's state for the next call.
+// Nothing waits on another workgroup.  The keys and arrival counters are
+// device-scope atomics, performed at the one coherence point for every XCD;
+// a workgroup increments its sequence's counter only after its own key
+// update has returned, so the workgroup that sees the count complete reads
+// final keys.  No fence is needed for that (a device-scope release and
+// acquire per workgroup would write back and invalidate the XCD's L2).
 //
-// State: [B*(k+1)] AR keys and [B*max(k-1,1)] draft keys, one per 128-byte
-// line, zero between
-// calls (each call leaves them so; the memory must be zero before its
-// first use).
+// State: [B*(k+1)] AR keys, [B*max(k-1,1)] draft keys and [B] arrival
+// counters, one per 128-byte line, zero between calls (each call leaves
+// them so; the memory must be zero before its first use).
 #include <algorithm>
 #include <mutex>
 
@@ -50,6 +51,7 @@ typedef unsigned long long u64;
 // Each row key sits in its own 128-byte line: the atomics of one row's
 // chunks then never queue behind another row's at the coherence point.
 constexpr int kKeyStride = kFusedKeyBytes / 8;
+constexpr int kArriveStride = kFusedKeyBytes / 4;
 
 // Orders (value, index) as the greedy rule does: larger value first, then
 // lower index; -0.0 is folded onto +0.0 so the two tie.  Never 0 for a
@@ -67,6 +69,10 @@ __device__ __forceinline__ u64 load_key(const u64* p) {
 __device__ __forceinline__ void store_zero(u64* p) {
   __hip_atomic_store(p, (u64)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Waits until every memory operation this wave has issued has completed
+// (atomics with a result: the result has returned from the coherence point),
+// and keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void wait_memory() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
 
 __global__ __launch_bounds__(256) void ar_key_kernel(FusedVerifyArgs a) {
   const int chunk = blockIdx.x;
@@ -137,56 +143,11 @@ __device__ __forceinline__ int commit_flag(const FusedVerifyArgs& a, int b, int 
   return flag;
 }
 
-template <typename E, int D, bool PAGED, bool COMMIT>
-__global__ __launch_bounds__(256) void draft_commit_kernel(FusedVerifyArgs a) {
-  __shared__ int s_acc;
-  const int chunk = blockIdx.x;
-  const int b = blockIdx.y / a.n_draft_rows;
-  const int m = blockIdx.y % a.n_draft_rows;  // draft slot m + 1
-  const int k = a.k;
-  if (threadIdx.x < 64) {
-    int acc, bonus;
-    accept_from_keys(a, b, threadIdx.x, acc, bonus);
-    if (threadIdx.x == 0) s_acc = acc;
-  }
-  __syncthreads();
-  const int acc = s_acc;
-  const int g = (acc > 0 ? acc : 1) - 1;
-
-  if (k > 1) {  // this chunk of draft row (group g, slot m + 1)
-    const float* src = a.draft_logits + (((size_t)b * k + g) * k + m + 1) * a.V;
-    const int lo = chunk * kArgmaxChunk;
-    const int hi = min(a.V, lo + kArgmaxChunk);
-    float bv;
-    int bi;
-    block_chunk_argmax(src, lo, hi, a.V, kArgmaxChunk, bv, bi);
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_max(&a.dkey[((size_t)b * (k - 1) + m) * kKeyStride], argmax_key(bv, bi), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-  }
-
-  if (COMMIT) {
-    // every workgroup of the sequence takes the same decision; units
-    // (accepted row i, KV head h) are dealt over them
-    const int L = a.lens[b];
-    int pg0, pg1;
-    if (!commit_flag<PAGED>(a, b, L, acc, pg0, pg1)) {
-      const int n_wg = gridDim.x * a.n_draft_rows;
-      for (int u = m * gridDim.x + chunk; u < acc * a.Hkv; u += n_wg) {
-        const int i = u / a.Hkv, h = u % a.Hkv, pos = L + i;
-        commit_row<E, D, PAGED>(a, b, i, h, pos, pos / 64 == L / 64 ? pg0 : pg1);
-      }
-    }
-  }
-}
-
-// One wave per sequence, after the draft kernel: the results, the new
-// settled length (every copy of the draft kernel is done), and the keys
-// cleared for the next call.
+// The results of sequence b once every draft key is final: accept length,
+// bonus token and next drafts; the commit flag and the new settled length;
+// the sequence's keys and counter cleared.  One wave (lane < 64).
 template <bool PAGED, bool COMMIT>
-__global__ __launch_bounds__(64) void finalize_kernel(FusedVerifyArgs a) {
-  const int b = blockIdx.x;
-  const int lane = threadIdx.x;
+__device__ __forceinline__ void finalize_sequence(const FusedVerifyArgs& a, int b, int lane) {
   const int k = a.k;
   int acc, bonus;
   accept_from_keys(a, b, lane, acc, bonus);
@@ -205,21 +166,73 @@ __global__ __launch_bounds__(64) void finalize_kernel(FusedVerifyArgs a) {
       if (a.err_flags) a.err_flags[b] = flag;
       if (!flag) a.lens[b] = L + acc;
     }
+    __hip_atomic_store(&a.arrive[(size_t)b * kArriveStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (lane <= k) store_zero(&a.key[((size_t)b * (k + 1) + lane) * kKeyStride]);  // every lane read its key above
+}
+
+template <typename E, int D, bool PAGED, bool COMMIT>
+__global__ __launch_bounds__(256) void draft_commit_kernel(FusedVerifyArgs a) {
+  __shared__ int s_acc, s_last;
+  const int span = blockIdx.x;
+  const int b = blockIdx.y / a.n_draft_rows;
+  const int m = blockIdx.y % a.n_draft_rows;  // draft slot m + 1
+  const int k = a.k;
+  if (threadIdx.x < 64) {
+    int acc, bonus;
+    accept_from_keys(a, b, threadIdx.x, acc, bonus);
+    if (threadIdx.x == 0) s_acc = acc;
+  }
+  __syncthreads();
+  const int acc = s_acc;
+  const int g = (acc > 0 ? acc : 1) - 1;
+
+  u64 done = 0;  // thread 0: the draft key's old value, once returned
+  if (k > 1) {  // this span of draft row (group g, slot m + 1)
+    const float* src = a.draft_logits + (((size_t)b * k + g) * k + m + 1) * a.V;
+    const int lo = span * kDraftSpan;
+    const int hi = min(a.V, lo + kDraftSpan);
+    float bv;
+    int bi;
+    block_chunk_argmax<kDraftSpan>(src, lo, hi, a.V, kDraftSpan, bv, bi);
+    if (threadIdx.x == 0)
+      done = __hip_atomic_fetch_max(&a.dkey[((size_t)b * (k - 1) + m) * kKeyStride], argmax_key(bv, bi),
+                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  if (COMMIT) {
+    // every workgroup of the sequence takes the same decision; units
+    // (accepted row i, KV head h) are dealt over them
+    const int L = a.lens[b];
+    int pg0, pg1;
+    if (!commit_flag<PAGED>(a, b, L, acc, pg0, pg1)) {
+      const int n_wg = gridDim.x * a.n_draft_rows;
+      for (int u = m * gridDim.x + span; u < acc * a.Hkv; u += n_wg) {
+        const int i = u / a.Hkv, h = u % a.Hkv, pos = L + i;
+        commit_row<E, D, PAGED>(a, b, i, h, pos, pos / 64 == L / 64 ? pg0 : pg1);
+      }
+    }
+  }
+
+  // arrival: after this workgroup's key update has returned (and its reads
+  // of lens and the keys are done), one count on the sequence's counter; the
+  // workgroup that completes the count finalises the sequence
+  __syncthreads();  // every thread's reads of lens are done
+  if (threadIdx.x == 0) {
+    asm volatile("" ::"v"((unsigned)done), "v"((unsigned)(done >> 32)));  // the update's result is used
+    wait_memory();
+    const unsigned n =
+        __hip_atomic_fetch_add(&a.arrive[(size_t)b * kArriveStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = n + 1 == (unsigned)(gridDim.x * a.n_draft_rows);
+  }
+  __syncthreads();
+  if (s_last && threadIdx.x < 64) finalize_sequence<PAGED, COMMIT>(a, b, threadIdx.x);
 }
 
 template <typename E, int D, bool PAGED>
 void launch_draft_typed(const FusedVerifyArgs& a, dim3 grid, hipStream_t s) {
   if (a.commit) hipLaunchKernelGGL((draft_commit_kernel<E, D, PAGED, true>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((draft_commit_kernel<E, D, PAGED, false>), grid, dim3(256), 0, s, a);
-}
-
-void launch_finalize(const FusedVerifyArgs& a, dim3 grid, dim3 block, hipStream_t s) {
-  const bool paged = a.block_table != nullptr;
-  if (!a.commit) hipLaunchKernelGGL((finalize_kernel<false, false>), grid, block, 0, s, a);
-  else if (paged) hipLaunchKernelGGL((finalize_kernel<true, true>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((finalize_kernel<false, true>), grid, block, 0, s, a);
 }
 
 }  // namespace
@@ -230,7 +243,7 @@ FusedVerifyGeometry fused_verify_geometry(int B, int k, int V) {
   g.ar_grid_x = n_chunks;
   g.ar_grid_y = B * (k + 1);
   g.draft_rows = std::max(k - 1, 1);
-  g.draft_grid_x = k > 1 ? n_chunks : 1;
+  g.draft_grid_x = k > 1 ? (V + kDraftSpan - 1) / kDraftSpan : 1;
   g.draft_grid_y = B * g.draft_rows;
   g.block = 256;
   return g;
@@ -239,9 +252,8 @@ FusedVerifyGeometry fused_verify_geometry(int B, int k, int V) {
 int fused_launch_shapes(int B, int k, int V, LaunchShape* out) {
   const FusedVerifyGeometry g = fused_verify_geometry(B, k, V);
   out[0] = {g.ar_grid_x, g.ar_grid_y, g.block};
-  out[1] = {g.draft_grid_x, g.draft_grid_y, g.block};
-  out[2] = {B, 1, 64};  // one wave per sequence; k + 1 <= 17 lanes hold the row keys
-  return 3;
+  out[1] = {g.draft_grid_x, g.draft_grid_y, g.block};  // its last workgroup per sequence finalises with one wave
+  return 2;
 }
 
 namespace {
@@ -301,8 +313,6 @@ hipError_t launch_fused_verify(const FusedVerifyArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const dim3 grid(g.draft_grid_x, g.draft_grid_y);
   const bool paged = a.block_table != nullptr;
-  LaunchShape sh[kMaxLaunches];
-  fused_launch_shapes(a.B, a.k, a.V, sh);
   if (a.elem_bytes == 2) {
     if (a.D == 128) paged ? launch_draft_typed<uint16_t, 128, true>(a, grid, s)
                           : launch_draft_typed<uint16_t, 128, false>(a, grid, s);
@@ -314,9 +324,6 @@ hipError_t launch_fused_verify(const FusedVerifyArgs& a, hipStream_t s) {
     else paged ? launch_draft_typed<uint32_t, 64, true>(a, grid, s)
                : launch_draft_typed<uint32_t, 64, false>(a, grid, s);
   }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  launch_finalize(a, dim3(sh[2].gx, sh[2].gy), dim3(sh[2].block), s);
   return hipGetLastError();
 }
 

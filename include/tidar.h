@@ -396,14 +396,14 @@ int tidar_kv_commit_paged(int dtype, int B, int Hkv, int D, int max_pages, int n
  * the nodesdaily.com page), then the a_b accepted candidate rows appended to
  * the settled cache and lens[b] += a_b, rejected entries evicted (paragraph
  * on the three zones; "KV Cache" section of the mauroscia.it page).  It runs
- * in three launches instead of five: per-row argmax keys are folded with
+ * in two launches instead of five: per-row argmax keys are folded with
  * atomics, every workgroup of the draft pass derives the accept length from
- * them itself and copies a share of the accepted rows, and one wave per
- * sequence then writes the results and the new length.
+ * them itself and copies a share of the accepted rows, and the last of a
+ * sequence's workgroups to finish writes its results and new length.
  *
  *   state        device memory (8-byte aligned) of at least
  *                tidar_verify_commit_state_bytes(B, k) bytes: per-row
- *                argmax keys.  It must be ZERO before its
+ *                argmax keys and per-sequence arrival counters.  It must be ZERO before its
  *                first use; every call leaves it zero again.  One state must
  *                not serve two calls that may run at the same time.
  *   dtype, B, Hkv, D, S_max, R, k, k_cache, v_cache, lens, k_step, v_step,
@@ -429,7 +429,7 @@ int tidar_verify_commit_greedy(int dtype, int B, int Hkv, int D, int S_max, int 
  * ends; this call allocates nothing (no hipMalloc, hipFree or allocating
  * library routine).  The first call on a GPU, and the first after a call
  * that returned TIDAR_ELAUNCH, also enqueue a clearing kernel before the
- * three of the step.
+ * two of the step.
  *   Returns TIDAR_EWORKSPACE when tidar_verify_commit_state_bytes(B, k)
  *   exceeds 2 MiB (2097152 bytes), before anything is enqueued; otherwise
  *   what tidar_verify_commit_greedy returns.

@@ -291,8 +291,11 @@ def test_launch_shapes_fit_the_hardware(T, path):
                     if k > 1:
                         assert shapes[7] == B * (k - 1)
                 if path == 2:
-                    assert n == 3 and shapes[1] == B * (k + 1) and shapes[4] == B * max(k - 1, 1)
-                    assert shapes[6] == B and shapes[8] >= k + 1  # one lane per AR row key
+                    assert n == 2 and shapes[1] == B * (k + 1) and shapes[4] == B * max(k - 1, 1)
+                    assert shapes[0] * 4096 >= V  # every AR logit chunk
+                    if k > 1:
+                        assert shapes[3] * 8192 >= V  # every draft logit span
+                    assert shapes[5] >= 64  # the finalising wave
     # beyond k = 16 every path refuses
     for path in (0, 1, 2):
         assert L.tidar_launch_shapes(path, 4, 17, 1000, 8, 128, 0, shapes) == -2
