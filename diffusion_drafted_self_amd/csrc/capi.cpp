@@ -126,7 +126,7 @@ int plan_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_
           const long rounds = cdiv(wgs, kCUs);
           const double body = pp ? body_clk_pp(nsh) : body_clk(nf, nsh);
           double cost = std::max((double)rounds * body * kt, hbm_clk) + 20000.0 * rounds;
-          if (ns > 1) cost += (14.0 + (double)pairs * ns * p->M * (D * 4 + 8) * 2 / 5.0e6) * kClkPerUs;
+          if (ns > 1) cost += (5.0 + (double)pairs * ns * p->M * (D * 4 + 8) * 2 / 5.0e6) * kClkPerUs;
           const bool better = cost < best * 0.999 || (cost <= best * 1.001 && wgs > best_wgs && wgs <= rounds * kCUs);
           if (better) {
             best = cost;
