@@ -817,10 +817,10 @@ def main():
 
     assert int(reps[0]["err"].abs().sum()) == 0
 
-    # The same steps replayed from HIP graphs (reported beside the eager
-    # figure as step_us_graph): one captured step per input replica, so the
-    # launches cost no host time between kernels.  The sampling step takes
-    # its draw counter as a launch argument and is not replayed.
+    # The same steps replayed from HIP graphs (one captured step per input
+    # replica, so the launches cost no host time between kernels): the
+    # whole-step figure step_us_graph.  The sampling step takes its draw
+    # counter as a launch argument and is not replayed.
     graph_ms = None
     if args.verify != "sample":
         side = torch.cuda.Stream()
@@ -853,6 +853,42 @@ def main():
                 assert r["acc"].cpu().numpy().tolist() == a_planted.tolist()
             assert torch.equal(r["lens"], r["lens0"]) and int(r["err"].abs().sum()) == 0
         del graphs
+
+    # The attention calls alone and the verify + commit calls alone, each K
+    # in a row on the rotating replicas, queued behind a short spin kernel so
+    # the host has enqueued all of them before the GPU reaches the first:
+    # the event pair around each attention call then times the GPU's work,
+    # the kernel's launch duration (what rocprofv3 reports for it), not the
+    # host's launch overhead.
+    vc_ms = None
+    attn_ms_pair_mean = None
+    queued = args.verify == "greedy"
+    if queued:
+        def queued_run(fn, per_call):
+            torch.cuda.synchronize()
+            torch.cuda._sleep(20_000_000)  # ~10 ms at the shader clock
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+            q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            q0.record(stream)
+            for i in range(K):
+                r = reps[(Wu + i) % n_rep]
+                if per_call:
+                    evs[i][0].record(stream)
+                fn(r)
+                if per_call:
+                    evs[i][1].record(stream)
+            q1.record(stream)
+            torch.cuda.synchronize()
+            return q0.elapsed_time(q1) / K, sorted(e0.elapsed_time(e1) for e0, e1 in evs) if per_call else None
+
+        _, attn_ms = queued_run(attention, True)
+        attn_ms_pair_mean = sum(attn_ms) / K
+        attn_ms_mean, _ = queued_run(attention, False)
+        vc_ms, _ = queued_run(lambda r: verify_commit(r, 0), False)
+        for r in reps:
+            if a_planted is not None:
+                assert r["acc"].cpu().numpy().tolist() == a_planted.tolist()
+            assert torch.equal(r["lens"], r["lens0"]) and int(r["err"].abs().sum()) == 0
     read_gbps = achievable_read_gbps(tidar, torch, dev, stream)
     if args.verify == "sample":
         # sampling is a function of (inputs, seed, step): replay the timed
@@ -914,7 +950,11 @@ def main():
         "attention_achievable_frac": round(attn_gbps / read_gbps, 4),
         "attention_tflops": round((flops + flops_step) / (attn_ms_mean * 1e-3) / 1e12, 2),
         "attention_mfma_frac": round((flops + flops_step) / (attn_ms_mean * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-        "verify_commit_us": round((step_ms - attn_ms_mean) * 1e3, 2),
+        "verify_commit_us": round((vc_ms if vc_ms is not None else step_ms - attn_ms_mean) * 1e3, 2),
+        "attention_us_event_pairs": round(attn_ms_pair_mean * 1e3, 2) if vc_ms is not None else None,
+        "timing": ("attention_us / verify_commit_us: each call alone, K in a row queued behind a spin kernel "
+                   "(GPU time); step_us: eager whole steps; step_us_graph: replayed whole steps"
+                   if vc_ms is not None else "eager steps, an event pair around each attention call"),
         "roofline": attention_roofline(attn_b, flops + flops_step, attn_ms_mean,
                                        traffic if wl.name == "step_8b" and not args.paged else None),
     }
