@@ -8,10 +8,16 @@ verify over a 128256-entry vocabulary with planted accept lengths U{0..8}),
 bf16, synthetic seeded inputs already resident in HBM.
 
 Timing: W untimed warmup steps, then K steps between HIP events on the
-launch stream.  Inputs rotate over replicas totalling >= 2 GB so the 256 MB
+launch stream (step_us), and the same K steps replayed from HIP graphs
+(step_us_graph).  Inputs rotate over replicas totalling >= 2 GB so the 256 MB
 Infinity Cache cannot serve them warm.  After each step the settled lengths
 are restored (a 64-byte device copy) so every step is the same workload.
-The attention call is bracketed by its own events for the roofline figure.
+The attention calls alone, and the verify + commit calls alone, are then
+timed as K calls in a row queued behind a short spin kernel, so the host has
+enqueued them all before the GPU starts: one event pair around the K calls
+gives the GPU time per call (the value and the roofline figure; it agrees
+with the kernel's average duration in a rocprofv3 trace), an event pair
+around each call gives p50/p99.
 
 Prints ONE JSON line.  Options:
   --gpus N          only N = 1 is supported (one GPU per process, no collectives)
@@ -78,6 +84,8 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--kv-chunk", type=int, default=0, help="key positions per attention chunk (0: library plan)")
     p.add_argument("--summarize", metavar="DIR", help="write profiles/ summaries from rocprofv3 outputs in DIR")
+    p.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "NAME"),
+                   help="write profiles/NAME_kernel_trace.md from the kernel-trace run under DIR/kt")
     p.add_argument("--summarize-counters", metavar="DIR",
                    help="write the attention counter summary of --workload from the passes under DIR")
     p.add_argument("--counters-kernel", default="", help="TIDAR_ATTN_KERNEL value the counter runs used")
@@ -252,28 +260,10 @@ def _csv_rows(pattern):
 
 def summarize(dirname):
     """Summaries of a profiling session (see the module docstring for the
-    commands); written under profiles/."""
+    commands); written under profiles/: the 8B step's kernel trace (under
+    dirname/kt) and the attention kernel's HBM traffic."""
     import statistics
-    cmd_kt = ("rocprofv3 --kernel-trace --stats -d DIR/kt -o kt --output-format csv -- "
-              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline")
-    stats = _csv_rows(os.path.join(dirname, "kt", "*kernel_stats.csv"))
-    lines = ["# Kernel trace: one TiDAR step on the 8B-shaped workload", "",
-             f"Command (from the repository root, MI355X): `{cmd_kt}`", "",
-             "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
-    for r in stats:
-        if "tidar" not in r["Name"] and "copyBuffer" not in r["Name"]:
-            continue
-        name = r["Name"].replace("(anonymous namespace)::", "").replace("tidar::", "")
-        lines.append(f"| `{name[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
-    lines += ["", "Each step kernel runs once per eager step (warm-up and timed), once more per input "
-              "replica as the warm-up before its graph capture, and once per graph replay (warm-up and timed). "
-              "`copyBuffer` is the 64-byte restore of the settled lengths after each timed step (harness). "
-              "`read_probe_kernel` is the achievable-bandwidth measurement after the timed steps "
-              "(a streaming read of 4 GiB, six calls).", ""]
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", "attention_step_8b_kernel_trace.md"), "w") as f:
-        f.write("\n".join(lines))
+    summarize_trace(dirname, "attention_step_8b")
 
     def per_dispatch(counter, kernel_key):
         vals = [float(r["Counter_Value"]) for r in _csv_rows(os.path.join(dirname, f"pmc_{counter}", "*counter_collection.csv"))
@@ -307,8 +297,71 @@ def summarize(dirname):
            f"kernel_source_sha = {attention_source_sha()}", ""]
     with open(TRAFFIC_FILE, "w") as f:
         f.write("\n".join(out))
-    print("\n".join(lines))
     print("\n".join(out))
+
+
+# Kernel-trace summaries kept under profiles/: name -> (title, bench
+# arguments of the traced run, the workload, where the calls come from)
+_STEP_CALLS = ("The step's kernels run in the warm-up and timed eager steps, once per input replica before its graph "
+               "capture, in the graph replays (warm-up and timed), and in the queued runs of the attention calls "
+               "alone and the verify + commit calls alone.")
+TRACES = {
+    "attention_step_8b": ("one TiDAR step on the 8B-shaped workload", "--steps 20 --warmup 5",
+                          "B=16, 32/8 heads of 128, prefix 4096, k=8 (+64 draft slots), greedy verify over 128256 "
+                          "entries with planted accept lengths, fused verify + commit.", _STEP_CALLS),
+    "step_1p5b": ("one TiDAR step on the 1.5B-shaped workload", "--workload step_1p5b --steps 20 --warmup 5",
+                  "B=8, 12/2 heads of 128, prefix 2048, k=4 (+16 draft slots), greedy verify over 151936 entries, "
+                  "fused verify + commit.", _STEP_CALLS),
+    "step_8b_long": ("one long-context TiDAR step, 8B heads", "--workload step_8b_long --steps 10 --warmup 3",
+                     "B=4, 32/8 heads of 128, prefix 32768, k=16 (+256 draft slots), greedy verify over 128256 "
+                     "entries, fused verify + commit.", _STEP_CALLS),
+    "train_attention_8b": ("training-mask attention, 8B heads", "--workload train_8b --steps 10 --warmup 3",
+                           "B=4, Hq=32, Hkv=8, D=128, N=4096 clean + 4096 masked positions (T=8192), block 8.",
+                           "One call per warm-up and timed step (3 + 10)."),
+    "verify_sample_step_8b": ("one TiDAR step with stochastic verification, 8B-shaped workload",
+                              "--verify sample --steps 20 --warmup 5",
+                              "the 8B step with the rejection-sampling verify at T=1 (inputs from the sampling "
+                              "generator) and the separate commit.",
+                              "Eager steps only (the draw counter is a launch argument, so nothing is replayed); "
+                              "after the timed steps the verification runs once more per timed step to read the "
+                              "accept lengths the bytes depend on."),
+    "lmhead_verify_8b": ("one TiDAR step with the LM head fused into greedy verification, 8B-shaped workload",
+                         "--verify lmhead --steps 10 --warmup 3",
+                         "the 8B step with hidden states and a random-init head of d_model 4096 x 128256 packed "
+                         "before timing; two passes over the head per step.",
+                         "The step's kernels run in the warm-up and timed eager steps, once per input replica before "
+                         "its graph capture, and in the graph replays (warm-up and timed)."),
+    "attention_ragged_loop": ("the ragged serving loop, 256 steps",
+                              "--workload ragged_8b --loop 256 --warmup 5",
+                              "batch 32, 32/8 heads of 128, lengths drawn U{512..8192} and advanced in place by "
+                              "each step's commit, k=8, greedy verify over 128256 entries.",
+                              "5 ordinary warm-up steps (lengths restored), then the 256 loop steps."),
+}
+
+
+def summarize_trace(dirname, name):
+    """profiles/<name>_kernel_trace.md from the kernel-trace run under
+    dirname/kt (the command in TRACES[name])."""
+    title, bench_args, what, calls = TRACES[name]
+    cmd = (f"rocprofv3 --kernel-trace --stats -d DIR/kt -o kt --output-format csv -- python3 bench.py {bench_args} "
+           "--no-cpu-baseline")
+    lines = [f"# Kernel trace: {title}", "", f"Command (from the repository root, MI355X): `{cmd}`", "",
+             f"Workload: {what}", "",
+             "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in _csv_rows(os.path.join(dirname, "kt", "*kernel_stats.csv")):
+        if "tidar" not in r["Name"] and "copyBuffer" not in r["Name"]:
+            continue
+        kname = r["Name"].replace("(anonymous namespace)::", "").replace("tidar::", "")
+        lines.append(f"| `{kname[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    lines += ["", calls + " `copyBuffer` is the settled lengths' 64-byte "
+              "restore after each step and the replicas' set-up copies (harness). `read_probe_kernel` is the "
+              "achievable-bandwidth measurement (a streaming read of 4 GiB, six calls). Other rows of the run "
+              "(torch elementwise kernels) are the harness's input generation and checks.", ""]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"{name}_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
 
 
 # Counter passes of the attention kernel (one rocprofv3 --pmc run each, at
@@ -655,6 +708,9 @@ def main():
         return
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, args.workload, args.counters_kernel)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
         return
     if args.summarize_lmhead:
         summarize_lmhead(args.summarize_lmhead)
