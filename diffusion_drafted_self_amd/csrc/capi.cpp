@@ -101,7 +101,7 @@ int plan_attention(int dtype, int B, int Hq, int Hkv, int D, int S_max, int max_
     p->n_rowblk = 1;
   } else {
     const long n_key_tiles = cdiv(keys, kTileKeys);
-    constexpr double kClkPerUs = 2200.0;
+    constexpr double kClkPerUs = 2000.0;  // shader clock under this kernel's load (GRBM_GUI_ACTIVE over the dispatch, 8B step)
     const double hbm_clk = (double)pairs * keys * D * 4 / 6.0e6 * kClkPerUs;  // K+V bytes at ~6 TB/s
     double best = 1e300;
     long best_chunk = 0;
