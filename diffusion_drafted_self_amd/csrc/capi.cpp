@@ -334,12 +334,12 @@ int plan_fused(int B, int k, FusedPlan* p) {
   return TIDAR_OK;
 }
 
-int verify_commit_impl(int dtype, int B, int Hkv, int D, int S_max, int R, int k, int V, const float* ar_logits,
-                       const float* draft_logits, const int32_t* cand, void* k_cache, void* v_cache,
-                       const int32_t* block_table, int max_pages, int n_pages, int32_t* lens, const void* k_step,
-                       const void* v_step, int32_t* accept_len, int32_t* next_cand, int32_t* err_flags,
-                       void* state, size_t state_bytes, void* stream) {
-  // the verification's checks, then the commit's
+// The fused path's host checks (the verification's, then the commit's, then
+// the state's); TIDAR_OK also for B == 0, where nothing is enqueued.
+int verify_commit_checks(int dtype, int B, int Hkv, int D, int S_max, int R, int k, int V, const float* ar_logits,
+                         const float* draft_logits, const int32_t* cand, const void* k_cache, const void* v_cache,
+                         const int32_t* lens, const void* k_step, const void* v_step, const int32_t* accept_len,
+                         const int32_t* next_cand, const int32_t* err_flags, const void* state, size_t state_bytes) {
   VerifyPlan vp;
   int st = plan_verify(B, k, V, &vp);
   if (st != TIDAR_OK) return st;
@@ -358,6 +358,20 @@ int verify_commit_impl(int dtype, int B, int Hkv, int D, int S_max, int R, int k
     return TIDAR_EINVAL;
   if (err_flags && !aligned(err_flags, 4)) return TIDAR_EINVAL;
   if (!aligned(state, 8) || state_bytes < fp.total) return TIDAR_EWORKSPACE;
+  return TIDAR_OK;
+}
+
+int verify_commit_impl(int dtype, int B, int Hkv, int D, int S_max, int R, int k, int V, const float* ar_logits,
+                       const float* draft_logits, const int32_t* cand, void* k_cache, void* v_cache,
+                       const int32_t* block_table, int max_pages, int n_pages, int32_t* lens, const void* k_step,
+                       const void* v_step, int32_t* accept_len, int32_t* next_cand, int32_t* err_flags,
+                       void* state, size_t state_bytes, void* stream) {
+  const int st = verify_commit_checks(dtype, B, Hkv, D, S_max, R, k, V, ar_logits, draft_logits, cand, k_cache,
+                                      v_cache, lens, k_step, v_step, accept_len, next_cand, err_flags, state,
+                                      state_bytes);
+  if (st != TIDAR_OK || B == 0) return st;
+  FusedPlan fp;
+  plan_fused(B, k, &fp);
 
   tidar::FusedVerifyArgs a = {};
   a.ar_logits = ar_logits;
@@ -745,7 +759,12 @@ int tidar_verify_commit_greedy_noalloc(int dtype, int B, int Hkv, int D, int S_m
   const int pst = plan_fused(B, k, &fp);
   if (pst != TIDAR_OK) return pst;
   if (fp.total > tidar::kNoAllocScratchBytes) return TIDAR_EWORKSPACE;
-  if (B == 0) return TIDAR_OK;
+  // every check first (a stand-in for the array's address: aligned, large
+  // enough), so a refused call enqueues nothing, not even the first clear
+  const int cst = verify_commit_checks(dtype, B, Hkv, D, S_max, R, k, V, ar_logits, draft_logits, cand, k_cache,
+                                       v_cache, lens, k_step, v_step, accept_len, next_cand, err_flags,
+                                       reinterpret_cast<const void*>(uintptr_t(256)), tidar::kNoAllocScratchBytes);
+  if (cst != TIDAR_OK || B == 0) return cst;
   void* state = nullptr;
   if (tidar::noalloc_scratch(static_cast<hipStream_t>(stream), &state) != hipSuccess) return TIDAR_ELAUNCH;
   const int st = verify_commit_impl(dtype, B, Hkv, D, S_max, R, k, V, ar_logits, draft_logits, cand, k_cache,

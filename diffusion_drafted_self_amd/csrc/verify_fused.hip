@@ -146,11 +146,12 @@ __device__ __forceinline__ int commit_flag(const FusedVerifyArgs& a, int b, int 
 // The results of sequence b once every draft key is final: accept length,
 // bonus token and next drafts; the commit flag and the new settled length;
 // the sequence's keys and counter cleared.  One wave (lane < 64).
+// acc, bonus: what this workgroup derived from the AR keys at its start; L,
+// flag: the settled length it read and the commit decision it took.
 template <bool PAGED, bool COMMIT>
-__device__ __forceinline__ void finalize_sequence(const FusedVerifyArgs& a, int b, int lane) {
+__device__ __forceinline__ void finalize_sequence(const FusedVerifyArgs& a, int b, int lane, int acc, int bonus, int L,
+                                                  int flag) {
   const int k = a.k;
-  int acc, bonus;
-  accept_from_keys(a, b, lane, acc, bonus);
   if (lane < k - 1) {
     u64* dk = &a.dkey[((size_t)b * (k - 1) + lane) * kKeyStride];
     a.next_cand[(size_t)b * k + 1 + lane] = key_index(load_key(dk));
@@ -160,20 +161,18 @@ __device__ __forceinline__ void finalize_sequence(const FusedVerifyArgs& a, int 
     a.next_cand[(size_t)b * k] = bonus;
     a.accept_len[b] = acc;
     if (COMMIT) {
-      const int L = a.lens[b];
-      int pg0, pg1;
-      const int flag = commit_flag<PAGED>(a, b, L, acc, pg0, pg1);
       if (a.err_flags) a.err_flags[b] = flag;
       if (!flag) a.lens[b] = L + acc;
     }
     __hip_atomic_store(&a.arrive[(size_t)b * kArriveStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (lane <= k) store_zero(&a.key[((size_t)b * (k + 1) + lane) * kKeyStride]);  // every lane read its key above
+  // every workgroup of the sequence read the keys before it arrived
+  if (lane <= k) store_zero(&a.key[((size_t)b * (k + 1) + lane) * kKeyStride]);
 }
 
 template <typename E, int D, bool PAGED, bool COMMIT>
 __global__ __launch_bounds__(256) void draft_commit_kernel(FusedVerifyArgs a) {
-  __shared__ int s_acc, s_last;
+  __shared__ int s_acc, s_bonus, s_last;
   const int span = blockIdx.x;
   const int b = blockIdx.y / a.n_draft_rows;
   const int m = blockIdx.y % a.n_draft_rows;  // draft slot m + 1
@@ -181,7 +180,10 @@ __global__ __launch_bounds__(256) void draft_commit_kernel(FusedVerifyArgs a) {
   if (threadIdx.x < 64) {
     int acc, bonus;
     accept_from_keys(a, b, threadIdx.x, acc, bonus);
-    if (threadIdx.x == 0) s_acc = acc;
+    if (threadIdx.x == 0) {
+      s_acc = acc;
+      s_bonus = bonus;
+    }
   }
   __syncthreads();
   const int acc = s_acc;
@@ -200,12 +202,14 @@ __global__ __launch_bounds__(256) void draft_commit_kernel(FusedVerifyArgs a) {
                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
+  int L = 0, flag = 0;
   if (COMMIT) {
     // every workgroup of the sequence takes the same decision; units
     // (accepted row i, KV head h) are dealt over them
-    const int L = a.lens[b];
+    L = a.lens[b];
     int pg0, pg1;
-    if (!commit_flag<PAGED>(a, b, L, acc, pg0, pg1)) {
+    flag = commit_flag<PAGED>(a, b, L, acc, pg0, pg1);
+    if (!flag) {
       const int n_wg = gridDim.x * a.n_draft_rows;
       for (int u = m * gridDim.x + span; u < acc * a.Hkv; u += n_wg) {
         const int i = u / a.Hkv, h = u % a.Hkv, pos = L + i;
@@ -226,7 +230,7 @@ __global__ __launch_bounds__(256) void draft_commit_kernel(FusedVerifyArgs a) {
     s_last = n + 1 == (unsigned)(gridDim.x * a.n_draft_rows);
   }
   __syncthreads();
-  if (s_last && threadIdx.x < 64) finalize_sequence<PAGED, COMMIT>(a, b, threadIdx.x);
+  if (s_last && threadIdx.x < 64) finalize_sequence<PAGED, COMMIT>(a, b, threadIdx.x, acc, s_bonus, L, flag);
 }
 
 template <typename E, int D, bool PAGED>
