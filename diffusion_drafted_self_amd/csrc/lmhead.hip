@@ -90,7 +90,7 @@ void lmhead_argmax_kernel(LmArgs a) {
     auto hrow = [&](int m) -> size_t {
       if (!a.draft) return (size_t)m * a.d;
       const int b = m / (a.k - 1), s = 1 + m % (a.k - 1);
-      const int g = min(max(a.group[b], 0), a.k - 1);  // written by the selection; clamped regardless
+      const int g = min(max(a.group[b], 0), a.k - 1);  // written by the selection; clamped (the draft finalisation flags it)
       return (((size_t)b * a.k + g) * a.k + s) * a.d;
     };
     // this wave's direct loads: lane t of a 1 KB block lands at row 8*blk + t/8,

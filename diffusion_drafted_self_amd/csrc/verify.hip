@@ -40,7 +40,9 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(VerifyArgs a) {
   } else {
     const int b = row / (a.k - 1);
     const int mm = 1 + row % (a.k - 1);
-    const int g = min(max(a.group[b], 0), a.k - 1);  // written by verify_select_kernel; clamped regardless
+    // written by verify_select_kernel; clamped so that no read leaves the
+    // draft logits (draft_finalize_kernel surfaces an out-of-range group)
+    const int g = min(max(a.group[b], 0), a.k - 1);
     src = a.draft_logits + (((size_t)b * a.k + g) * a.k + mm) * a.V;
     dst = a.part_draft + (size_t)row * a.n_chunks + chunk;
   }
@@ -103,12 +105,17 @@ __global__ __launch_bounds__(64 * kMaxWaves) void verify_select_kernel(VerifyArg
 }
 
 // block: min(k-1, kMaxWaves) waves over the k-1 draft rows of sequence blockIdx.x
+// A group outside 0..k-1 can only mean that the selection did not run for
+// this sequence; its drafts are then written as -1, no token id, rather
+// than as the clamped group's argmax.
 __global__ __launch_bounds__(64 * kMaxWaves) void draft_finalize_kernel(VerifyArgs a) {
   const int b = blockIdx.x;
   const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int g = a.group[b];
+  const bool valid = g >= 0 && g < a.k;
   for (int row = wave; row < a.k - 1; row += nw) {
     const int t = reduce_row(a.part_draft + ((size_t)b * (a.k - 1) + row) * a.n_chunks, a.n_chunks);
-    if ((threadIdx.x & 63) == 0) a.next_cand[(size_t)b * a.k + 1 + row] = t;
+    if ((threadIdx.x & 63) == 0) a.next_cand[(size_t)b * a.k + 1 + row] = valid ? t : -1;
   }
 }
 

@@ -139,6 +139,29 @@ def test_commit_validation(T):
     assert L.tidar_kv_commit_paged(0, 2, 8, 128, 64, 100, 400, 17, p, p, p, p, p, p, p, None, None) == -2
 
 
+def test_verify_commit_noalloc_refuses_before_enqueueing(T):
+    """The allocation-free fused verify + commit checks everything on the host
+    first: a refused call returns its own code, never the launch error a
+    first enqueue (the clearing kernel) would give on a machine without a GPU."""
+    L = T.lib()
+    p = ctypes.c_void_p(0x100000)
+    odd = ctypes.c_void_p(0x100002)
+
+    def call(dtype=0, B=16, Hkv=8, D=128, S_max=4224, R=72, k=8, V=128256, ptrs=None):
+        pp = ptrs or [p] * 11
+        return L.tidar_verify_commit_greedy_noalloc(dtype, B, Hkv, D, S_max, R, k, V, *pp, None)
+
+    assert call(dtype=7) == -2                              # dtype
+    assert call(D=96) == -2                                 # head dim
+    assert call(k=17) == -2                                 # k above 16
+    assert call(S_max=4200) == -1                           # not a multiple of the 64-position page
+    assert call(R=4) == -1                                  # fewer step rows than candidates
+    assert call(ptrs=[odd] + [p] * 10) == -1                # misaligned logits
+    assert call(ptrs=[p] * 10 + [odd]) == -1                # misaligned err_flags
+    assert call(B=1024, k=16, V=64) == -3                   # a state beyond the 2 MiB array
+    assert call(B=0) == 0                                   # nothing to do, nothing enqueued
+
+
 def test_verify_sample_validation_and_size(T):
     n = ctypes.c_size_t(0)
     L = T.lib()
