@@ -30,6 +30,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtidar.so")
+LIB_CHECKED_PATH = os.path.join(_HERE, "libtidar_checked.so")  # device-side bounds tests
 
 TIDAR_OK, TIDAR_EINVAL, TIDAR_EUNSUPPORTED, TIDAR_EWORKSPACE, TIDAR_ELAUNCH = 0, -1, -2, -3, -4
 TIDAR_BF16, TIDAR_F32 = 0, 1
@@ -62,6 +63,8 @@ SIGNATURES = {
     "tidar_verify_commit_greedy_noalloc": (_c_int, [_c_int] * 8 + [_p] * 11 + [_p]),
     "tidar_launch_shapes": (_c_int, [_c_int] * 7 + [ctypes.POINTER(_c_int)]),
     "tidar_read_probe": (_c_int, [_p, _c_size, _p, _p]),
+    "tidar_check_enabled": (_c_int, []),
+    "tidar_check_read": (_c_int, [ctypes.POINTER(ctypes.c_uint32), _c_int]),
 }
 
 
@@ -71,30 +74,73 @@ class TidarError(RuntimeError):
         self.status = status
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m diffusion_drafted_self_amd.build` "
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m diffusion_drafted_self_amd.build` "
                           "(the TiDAR path has no fallback implementation)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
     if lib.tidar_abi_version() != 1:
-        raise ImportError("libtidar.so ABI version mismatch; rebuild it")
+        raise ImportError(f"{os.path.basename(path)} ABI version mismatch; rebuild it")
     return lib
 
 
 _LIB = None
+_LOADED = {}
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded libtidar.so (loaded on first use; raises ImportError if it
-    has not been built)."""
+    """The library the calls of this module go through: libtidar.so (loaded
+    on first use; raises ImportError if it has not been built), or the
+    checked build inside ``checked_library()``."""
     global _LIB
     if _LIB is None:
-        _LIB = _load()
+        if LIB_PATH not in _LOADED:
+            _LOADED[LIB_PATH] = _load(LIB_PATH)
+        _LIB = _LOADED[LIB_PATH]
     return _LIB
+
+
+class checked_library:
+    """Context manager: inside it every call of this module goes through
+    libtidar_checked.so, the build with device-side bounds tests.  On entry
+    the checked library's records are cleared; ``check_read()`` returns the
+    first failed test."""
+
+    def __enter__(self):
+        global _LIB
+        self._prev = lib()
+        chk = _LOADED.get(LIB_CHECKED_PATH)
+        if chk is None:
+            chk = _LOADED[LIB_CHECKED_PATH] = _load(LIB_CHECKED_PATH)
+        if chk.tidar_check_enabled() != 1:
+            raise ImportError(f"{LIB_CHECKED_PATH} is not a checked build")
+        _LIB = chk
+        check_read(clear=True)
+        return self
+
+    def __exit__(self, *exc):
+        global _LIB
+        _LIB = self._prev
+        return False
+
+
+def check_read(clear: bool = True):
+    """(code, workgroup, thread, value) of the first failed bounds test the
+    current library recorded on the current device, code 0 if none (always 0
+    in the release library); ``clear`` resets the records.  Synchronises the
+    device in the checked build."""
+    rec = (ctypes.c_uint32 * 4)()
+    _check("tidar_check_read", lib().tidar_check_read(rec, 1 if clear else 0))
+    code, block, thread, value = (int(x) for x in rec)
+    return code, block, thread, ctypes.c_int32(value).value
+
+
+CHECK_CODES = {0: "none", 1: "lens", 2: "page", 3: "key_tile", 4: "row", 5: "chunk", 6: "group", 7: "accept",
+               8: "token", 9: "capacity", 10: "state"}
 
 
 def strerror(status: int) -> str:
@@ -696,4 +742,4 @@ __all__ = ["step_attention", "step_attention_workspace_bytes", "verify_greedy", 
            "step_attention_paged", "kv_commit_paged", "train_attention",
            "lmhead_verify_greedy", "lmhead_verify_workspace_bytes", "lmhead_pack", "lmhead_packed_bytes",
            "lmhead_verify_greedy_packed", "strerror", "lib", "TidarError", "LIB_PATH", "SIGNATURES",
-           "read_probe", "READ_PROBE_BLOCKS"]
+           "read_probe", "READ_PROBE_BLOCKS", "checked_library", "check_read", "CHECK_CODES", "LIB_CHECKED_PATH"]

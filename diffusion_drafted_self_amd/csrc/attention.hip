@@ -28,6 +28,7 @@
 //   attn_merge_kernel<Out, D>  log-sum-exp merge of the chunks, one wave per
 //       query row: normalised output (RNE to the output type) and the LSE.
 #include "attn_tile.h"
+#include "check.h"
 #include "common.h"
 #include "launch.h"
 #include "lds_dma.h"
@@ -412,6 +413,8 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
     kvh = t % a.Hkv;
     b = t / a.Hkv;
   }
+  if (!TIDAR_CHECK(b >= 0 && b < a.B, TIDAR_CHECK_ROW, b)) b = 0;
+  if (!TIDAR_CHECK(split < a.n_split, TIDAR_CHECK_CHUNK, split)) split = 0;
 
   // this workgroup's tiles [T0, T1): wave w owns T0 + w*NF + f (f < NF);
   // the shared tiles T0 + 4*NF + s (s < NS) are split by key block
@@ -442,11 +445,13 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
     ok_s[s2] = ti < T1 && mrow_s[s2] < a.M;
   }
   auto out_row = [&](int m) {
-    const int r = m / a.G, h = kvh * a.G + m % a.G;
+    int r = m / a.G, h = kvh * a.G + m % a.G;
+    if (!TIDAR_CHECK(r < a.R && h < a.Hq, TIDAR_CHECK_ROW, m)) r = h = 0;
     return (bf16*)a.out + ((size_t)(b * a.R + r) * a.Hq + h) * D;
   };
   auto lse_at = [&](int m) {
-    const int r = m / a.G, h = kvh * a.G + m % a.G;
+    int r = m / a.G, h = kvh * a.G + m % a.G;
+    if (!TIDAR_CHECK(r < a.R && h < a.Hq, TIDAR_CHECK_ROW, m)) r = h = 0;
     return a.lse + ((size_t)b * a.Hq + h) * a.R + r;
   };
 
@@ -464,14 +469,22 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
     kv.tbl = nullptr;
     kv.stride = (size_t)TK * D;
   }
+  kv.n_tiles = PAGED ? a.max_pages : a.S_max / TK;
+  kv.n_pages = a.n_pages;
   bool violated = !TRAIN && (L < 0 || L > a.max_len);
   if constexpr (PAGED) {  // every page holding a settled position must be in the pools
     bool bad = false;
     if (!violated)
-      for (int pg = tid; pg < (L + TK - 1) / TK; pg += NWV * 64) bad |= (unsigned)kv.tbl[pg] >= (unsigned)a.n_pages;
+      for (int pg = tid; pg < (L + TK - 1) / TK; pg += NWV * 64) {
+        const int32_t e = kv.tbl[pg];
+        const bool eb = (unsigned)e >= (unsigned)a.n_pages;
+        (void)TIDAR_CHECK(!eb, TIDAR_CHECK_PAGE, e);
+        bad |= eb;
+      }
     violated |= __syncthreads_or(bad) != 0;
   }
   if (violated) {  // contract violation: NaN rows, written once
+    if (tid == 0 && !TRAIN) (void)TIDAR_CHECK(L >= 0 && L <= a.max_len, TIDAR_CHECK_LENS, L);
     if (split == 0) {
       auto nan_row = [&](int m) {
         bf16* orow = out_row(m);
@@ -546,7 +559,8 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
 
   QFrags<D, NF, NS> q;
   auto load_q = [&](int m, bool ok_row, bf16x8 (&dst)[D / 32]) {
-    const int r = m / a.G, h = kvh * a.G + m % a.G;
+    int r = m / a.G, h = kvh * a.G + m % a.G;
+    if (!TIDAR_CHECK(!ok_row || (r < a.R && h < a.Hq), TIDAR_CHECK_ROW, m)) r = h = 0;
     const bf16* qrow = (const bf16*)a.q + ((size_t)(b * a.R + r) * a.Hq + h) * D;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
@@ -794,6 +808,7 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
     if (!ok_row) return;
     if (n_valid > 1) {
       const size_t prow = (pair * a.n_split + split) * a.M + m;
+      if (!TIDAR_CHECK(m < a.M, TIDAR_CHECK_ROW, m)) return;
       float* op = a.o_part + prow * D;
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) *(floatx4*)(op + 16 * db + 4 * hi) = o[db];
@@ -875,6 +890,7 @@ void attn_pipe_bf16_kernel(AttnArgs a) {
       const int m = mrow_s[s2];
       if (n_valid > 1) {
         const size_t prow = (pair * a.n_split + split) * a.M + m;
+        if (!TIDAR_CHECK(m < a.M, TIDAR_CHECK_ROW, m)) continue;
         float* op = a.o_part + prow * D;
 #pragma unroll
         for (int db = 0; db < D / 16; ++db)
@@ -914,12 +930,17 @@ __global__ __launch_bounds__(64) void attn_split_f32_kernel(AttnArgs a) {
   const int b = t / a.Hkv;
 
   const int L = a.lens[b];
-  if (L < 0 || L > a.max_len) return;
+  if (L < 0 || L > a.max_len) {
+    if (lane == 0) (void)TIDAR_CHECK(false, TIDAR_CHECK_LENS, L);
+    return;
+  }
   const int Ltot = L + a.R;
   const int kb = split * a.chunk;
   if (kb >= Ltot) return;
   const int ke = min(kb + a.chunk, Ltot);
   const int r = m / a.G, jh = m % a.G;
+  if (!TIDAR_CHECK(min(ke, L) <= a.S_max, TIDAR_CHECK_KEY_TILE, ke)) return;
+  if (!TIDAR_CHECK(ke - kb <= 1024, TIDAR_CHECK_CHUNK, ke - kb)) return;
 
   const float* qrow = (const float*)a.q + ((size_t)(b * a.R + r) * a.Hq + kvh * a.G + jh) * D;
   for (int d = lane; d < D; d += 64) qs[d] = qrow[d];
@@ -997,12 +1018,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     for (int pg = lane; pg < (L + VPAGE - 1) / VPAGE; pg += 64) bad |= (unsigned)tbl[pg] >= (unsigned)a.n_pages;
     violated = __any(bad);
   }
-  if (violated) {
+  if (violated) {  // (the split kernel recorded it)
     for (int e = 0; e < E; ++e) store_out(orow + lane * E + e, NAN);
     if (lse && lane == 0) *lse = NAN;
     return;
   }
-  const int n_valid = (L + a.R + a.chunk - 1) / a.chunk;
+  int n_valid = (L + a.R + a.chunk - 1) / a.chunk;
+  if (!TIDAR_CHECK(n_valid <= a.n_split, TIDAR_CHECK_CHUNK, n_valid)) n_valid = a.n_split;
   if (n_valid == 1 && a.single_chunk_direct) return;  // the split kernel wrote it
   const size_t base = (size_t)pr * a.n_split * a.M + m;
 
@@ -1121,5 +1143,9 @@ hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   return a.D == 128 ? launch_merge<float, 128>(a, s) : launch_merge<float, 64>(a, s);
 }
+
+#if TIDAR_CHECKED
+TIDAR_CHECK_RECORD_ACCESSOR(check_record_attention)
+#endif
 
 }  // namespace tidar

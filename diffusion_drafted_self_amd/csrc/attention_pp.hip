@@ -271,6 +271,8 @@ void attn_pp_kernel(AttnArgs a) {
     kvh = t % a.Hkv;
     b = t / a.Hkv;
   }
+  if (!TIDAR_CHECK(b >= 0 && b < a.B, TIDAR_CHECK_ROW, b)) b = 0;
+  if (!TIDAR_CHECK(split < a.n_split, TIDAR_CHECK_CHUNK, split)) split = 0;
 
   // tiles [T0, T1) of this workgroup: wave w owns T0 + w; T0 + 8 is shared
   const int T0 = rw * a.n16 / a.n_rowblk;
@@ -282,11 +284,13 @@ void attn_pp_kernel(AttnArgs a) {
   const bool ok_s = SH && T0 + PPW < T1 && mrow_s < a.M;
   const bool sh_s = SH && grp == 0;  // this wave scores a block of the shared tile
   auto out_row = [&](int m) __attribute__((always_inline)) {
-    const int r = m / a.G, h = kvh * a.G + m % a.G;
+    int r = m / a.G, h = kvh * a.G + m % a.G;
+    if (!TIDAR_CHECK(r < a.R && h < a.Hq, TIDAR_CHECK_ROW, m)) r = h = 0;
     return (bf16*)a.out + ((size_t)(b * a.R + r) * a.Hq + h) * D;
   };
   auto lse_at = [&](int m) __attribute__((always_inline)) {
-    const int r = m / a.G, h = kvh * a.G + m % a.G;
+    int r = m / a.G, h = kvh * a.G + m % a.G;
+    if (!TIDAR_CHECK(r < a.R && h < a.Hq, TIDAR_CHECK_ROW, m)) r = h = 0;
     return a.lse + ((size_t)b * a.Hq + h) * a.R + r;
   };
 
@@ -304,14 +308,22 @@ void attn_pp_kernel(AttnArgs a) {
     kv.tbl = nullptr;
     kv.stride = (size_t)TK * D;
   }
+  kv.n_tiles = PAGED ? a.max_pages : a.S_max / TK;
+  kv.n_pages = a.n_pages;
   bool violated = L < 0 || L > a.max_len;
   if constexpr (PAGED) {  // every page holding a settled position must be in the pools
     bool bad = false;
     if (!violated)
-      for (int pg = tid; pg < (L + TK - 1) / TK; pg += PPT) bad |= (unsigned)kv.tbl[pg] >= (unsigned)a.n_pages;
+      for (int pg = tid; pg < (L + TK - 1) / TK; pg += PPT) {
+        const int32_t e = kv.tbl[pg];
+        const bool eb = (unsigned)e >= (unsigned)a.n_pages;
+        (void)TIDAR_CHECK(!eb, TIDAR_CHECK_PAGE, e);
+        bad |= eb;
+      }
     violated |= __syncthreads_or(bad) != 0;
   }
   if (violated) {  // contract violation: NaN rows, written once
+    if (tid == 0) (void)TIDAR_CHECK(L >= 0 && L <= a.max_len, TIDAR_CHECK_LENS, L);
     if (split == 0) {
       auto nan_row = [&](int m) __attribute__((always_inline)) {
         bf16* orow = out_row(m);
@@ -348,7 +360,8 @@ void attn_pp_kernel(AttnArgs a) {
 
   bf16x8 q[D / 32], qs[D / 32];
   auto load_q = [&](int m, bool ok_row, bf16x8 (&dst)[D / 32]) {
-    const int r = m / a.G, h = kvh * a.G + m % a.G;
+    int r = m / a.G, h = kvh * a.G + m % a.G;
+    if (!TIDAR_CHECK(!ok_row || (r < a.R && h < a.Hq), TIDAR_CHECK_ROW, m)) r = h = 0;
     const bf16* qrow = (const bf16*)a.q + ((size_t)(b * a.R + r) * a.Hq + h) * D;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
@@ -613,6 +626,7 @@ void attn_pp_kernel(AttnArgs a) {
                   bool lse_lane) __attribute__((always_inline)) {
     if (n_valid > 1) {
       const size_t prow = (pair * a.n_split + split) * a.M + m;
+      if (!TIDAR_CHECK(m < a.M, TIDAR_CHECK_ROW, m)) return;
       float* op = a.o_part + prow * D;
       for (int i = 0; i < ndb; ++i) *(floatx4*)(op + 16 * (db0 + i) + 4 * hi) = o[i];
       if (lse_lane) a.ml_part[prow] = make_float2(m_ref, l_tot);
@@ -661,5 +675,9 @@ hipError_t launch_attention_pp_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.D != 128) return hipErrorInvalidValue;
   return a.ns ? launch_pp<128, 1>(a, s) : launch_pp<128, 0>(a, s);
 }
+
+#if TIDAR_CHECKED
+TIDAR_CHECK_RECORD_ACCESSOR(check_record_attention_pp)
+#endif
 
 }  // namespace tidar

@@ -4,6 +4,7 @@
 // value page; both reach LDS by direct global->LDS loads in 1 KB pieces.
 #pragma once
 
+#include "check.h"
 #include "common.h"
 #include "lds_dma.h"
 
@@ -52,9 +53,17 @@ struct KvMap {
   const bf16* v;
   const int32_t* tbl;  // this sequence's block-table row (paged)
   size_t stride;       // elements from one page to the next
+  int n_tiles;         // checked build: tiles of the cache (S_max/64) or table slots (max_pages)
+  int n_pages;         // checked build: pages in the pools
   __device__ __forceinline__ size_t page(int t) const {
-    if constexpr (PAGED) return (size_t)scalar_load_i32(tbl + t);
-    else return (size_t)t;
+    if (!TIDAR_CHECK(t >= 0 && t < n_tiles, TIDAR_CHECK_KEY_TILE, t)) t = 0;
+    if constexpr (PAGED) {
+      int32_t pg = scalar_load_i32(tbl + t);
+      if (!TIDAR_CHECK((unsigned)pg < (unsigned)n_pages, TIDAR_CHECK_PAGE, pg)) pg = 0;
+      return (size_t)pg;
+    } else {
+      return (size_t)t;
+    }
   }
   __device__ __forceinline__ const bf16* ktile(int t) const { return k + page(t) * stride; }
   __device__ __forceinline__ const bf16* vtile(int t) const { return v + page(t) * stride; }

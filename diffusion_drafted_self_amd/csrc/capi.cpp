@@ -827,4 +827,26 @@ int tidar_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream
   return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
 }
 
+int tidar_check_enabled(void) { return TIDAR_CHECKED ? 1 : 0; }
+
+int tidar_check_read(uint32_t* rec, int clear) {
+  if (!rec) return TIDAR_EINVAL;
+  rec[0] = rec[1] = rec[2] = rec[3] = 0;
+#if TIDAR_CHECKED
+  if (hipDeviceSynchronize() != hipSuccess) return TIDAR_ELAUNCH;
+  hipError_t (*const files[])(unsigned*, bool) = {
+      tidar::check_record_attention,    tidar::check_record_attention_pp, tidar::check_record_verify,
+      tidar::check_record_verify_fused, tidar::check_record_verify_sample, tidar::check_record_lmhead,
+      tidar::check_record_commit};
+  for (auto read : files) {
+    unsigned r[4];
+    if (read(r, clear != 0) != hipSuccess) return TIDAR_ELAUNCH;
+    if (rec[0] == 0 && r[0] != 0) std::memcpy(rec, r, sizeof(r));
+  }
+#else
+  (void)clear;
+#endif
+  return TIDAR_OK;
+}
+
 }  // extern "C"

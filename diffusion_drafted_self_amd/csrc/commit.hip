@@ -14,6 +14,7 @@
 // the pools (keys [n_pages][Hkv][64][D], values [n_pages][Hkv][D][64]), at
 // row p % 64.  The caller provides the pages; a page entry outside the pools
 // is reported and nothing of that sequence is written.
+#include "check.h"
 #include "common.h"
 #include "launch.h"
 
@@ -95,6 +96,11 @@ __global__ __launch_bounds__(1024) void kv_commit_kernel(CommitArgs a) {
     }
   }
   const int flag = check();
+  if (threadIdx.x == 0 && flag)
+    (void)TIDAR_CHECK(false,
+                      flag == 2 ? TIDAR_CHECK_ACCEPT
+                                : (flag == 3 ? TIDAR_CHECK_PAGE : (L < 0 ? TIDAR_CHECK_LENS : TIDAR_CHECK_CAPACITY)),
+                      flag == 2 ? acc : L + acc);
   if (threadIdx.x == 0 && a.err_flags) a.err_flags[b] = flag;
   __builtin_amdgcn_s_barrier();  // every thread has read lens[b]
   if (threadIdx.x == 0 && !flag) a.lens[b] = L + acc;
@@ -133,5 +139,9 @@ hipError_t launch_commit(const CommitArgs& a, hipStream_t s) {
   launch_typed(a, s, sh[0].block);  // bf16 elements move as raw 16-bit words
   return hipGetLastError();
 }
+
+#if TIDAR_CHECKED
+TIDAR_CHECK_RECORD_ACCESSOR(check_record_commit)
+#endif
 
 }  // namespace tidar

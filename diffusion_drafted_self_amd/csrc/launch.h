@@ -1,6 +1,10 @@
 // Host-side launch interface between the C ABI (capi.cpp) and the kernels.
 #pragma once
 
+#ifndef TIDAR_CHECKED
+#define TIDAR_CHECKED 0  // 1 in the checked build (device-side bounds tests)
+#endif
+
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -172,5 +176,18 @@ struct CommitArgs {
 };
 
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
+
+#if TIDAR_CHECKED
+// Checked build: each kernel source file's record of its first failed
+// bounds test on the current device, {code, workgroup, thread, value};
+// `clear` zeroes it after the copy.  The device must be synchronised.
+hipError_t check_record_attention(unsigned* rec, bool clear);
+hipError_t check_record_attention_pp(unsigned* rec, bool clear);
+hipError_t check_record_verify(unsigned* rec, bool clear);
+hipError_t check_record_verify_fused(unsigned* rec, bool clear);
+hipError_t check_record_verify_sample(unsigned* rec, bool clear);
+hipError_t check_record_lmhead(unsigned* rec, bool clear);
+hipError_t check_record_commit(unsigned* rec, bool clear);
+#endif
 
 }  // namespace tidar

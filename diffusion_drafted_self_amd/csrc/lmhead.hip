@@ -30,6 +30,7 @@
 #include <algorithm>
 #include <climits>
 
+#include "check.h"
 #include "common.h"
 #include "launch.h"
 #include "lds_dma.h"
@@ -90,7 +91,9 @@ void lmhead_argmax_kernel(LmArgs a) {
     auto hrow = [&](int m) -> size_t {
       if (!a.draft) return (size_t)m * a.d;
       const int b = m / (a.k - 1), s = 1 + m % (a.k - 1);
-      const int g = min(max(a.group[b], 0), a.k - 1);  // written by the selection; clamped (the draft finalisation flags it)
+      const int g_read = a.group[b];
+      (void)TIDAR_CHECK(g_read >= 0 && g_read < a.k, TIDAR_CHECK_GROUP, g_read);
+      const int g = min(max(g_read, 0), a.k - 1);  // written by the selection; clamped (the draft finalisation flags it)
       return (((size_t)b * a.k + g) * a.k + s) * a.d;
     };
     // this wave's direct loads: lane t of a 1 KB block lands at row 8*blk + t/8,
@@ -267,5 +270,9 @@ hipError_t launch_lmhead_argmax(const LmArgs& a, hipStream_t s) {
     default: return launch_mt<9>(a, s);
   }
 }
+
+#if TIDAR_CHECKED
+TIDAR_CHECK_RECORD_ACCESSOR(check_record_lmhead)
+#endif
 
 }  // namespace tidar

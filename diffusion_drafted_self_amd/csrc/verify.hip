@@ -21,6 +21,7 @@
 #include <climits>
 
 #include "argmax_block.h"
+#include "check.h"
 #include "common.h"
 #include "launch.h"
 
@@ -42,7 +43,9 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(VerifyArgs a) {
     const int mm = 1 + row % (a.k - 1);
     // written by verify_select_kernel; clamped so that no read leaves the
     // draft logits (draft_finalize_kernel surfaces an out-of-range group)
-    const int g = min(max(a.group[b], 0), a.k - 1);
+    const int g_read = a.group[b];
+    if (threadIdx.x == 0 && chunk == 0) (void)TIDAR_CHECK(g_read >= 0 && g_read < a.k, TIDAR_CHECK_GROUP, g_read);
+    const int g = min(max(g_read, 0), a.k - 1);
     src = a.draft_logits + (((size_t)b * a.k + g) * a.k + mm) * a.V;
     dst = a.part_draft + (size_t)row * a.n_chunks + chunk;
   }
@@ -97,6 +100,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void verify_select_kernel(VerifyArg
     const unsigned long long mm = __ballot(miss || lane == a.k);
     const int acc = __ffsll((long long)mm) - 1;
     if (lane == 0) {
+      (void)TIDAR_CHECK(acc >= 0 && acc <= a.k, TIDAR_CHECK_ACCEPT, acc);
+      (void)TIDAR_CHECK(t_row[acc] >= 0 && t_row[acc] < a.V, TIDAR_CHECK_TOKEN, t_row[acc]);
       a.accept_len[b] = acc;
       a.next_cand[(size_t)b * a.k] = t_row[acc];
       a.group[b] = (acc > 0 ? acc : 1) - 1;
@@ -113,9 +118,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void draft_finalize_kernel(VerifyAr
   const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int g = a.group[b];
   const bool valid = g >= 0 && g < a.k;
+  if (threadIdx.x == 0) (void)TIDAR_CHECK(valid, TIDAR_CHECK_GROUP, g);
   for (int row = wave; row < a.k - 1; row += nw) {
     const int t = reduce_row(a.part_draft + ((size_t)b * (a.k - 1) + row) * a.n_chunks, a.n_chunks);
-    if ((threadIdx.x & 63) == 0) a.next_cand[(size_t)b * a.k + 1 + row] = valid ? t : -1;
+    if ((threadIdx.x & 63) == 0) {
+      if (valid) (void)TIDAR_CHECK(t >= 0 && t < a.V, TIDAR_CHECK_TOKEN, t);
+      a.next_cand[(size_t)b * a.k + 1 + row] = valid ? t : -1;
+    }
   }
 }
 
@@ -169,5 +178,9 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(draft_finalize_kernel, dim3(sh[3].gx, sh[3].gy), dim3(sh[3].block), 0, s, a);
   return hipGetLastError();
 }
+
+#if TIDAR_CHECKED
+TIDAR_CHECK_RECORD_ACCESSOR(check_record_verify)
+#endif
 
 }  // namespace tidar

@@ -34,6 +34,7 @@
 #include <mutex>
 
 #include "argmax_block.h"
+#include "check.h"
 #include "common.h"
 #include "launch.h"
 
@@ -99,6 +100,9 @@ __device__ __forceinline__ void commit_row(const FusedVerifyArgs& a, int b, int 
   if (t >= 2 * PPR) return;
   const bool is_v = t >= PPR;
   const int c = is_v ? t - PPR : t;
+  if (!TIDAR_CHECK(i >= 0 && i < a.R, TIDAR_CHECK_ROW, i)) return;
+  if (!TIDAR_CHECK(pos >= 0 && pos < (PAGED ? a.max_pages * 64 : a.S_max), TIDAR_CHECK_CAPACITY, pos)) return;
+  if (PAGED && !TIDAR_CHECK((unsigned)page < (unsigned)a.n_pages, TIDAR_CHECK_PAGE, page)) return;
   const size_t src = (((size_t)b * a.R + i) * a.Hkv + h) * D + (size_t)c * PER;
   const u32x4 piece = *(const u32x4*)((const E*)(is_v ? a.v_step : a.k_step) + src);
   if (!is_v) {
@@ -154,10 +158,16 @@ __device__ __forceinline__ void finalize_sequence(const FusedVerifyArgs& a, int 
   const int k = a.k;
   if (lane < k - 1) {
     u64* dk = &a.dkey[((size_t)b * (k - 1) + lane) * kKeyStride];
-    a.next_cand[(size_t)b * k + 1 + lane] = key_index(load_key(dk));
+    const int t = key_index(load_key(dk));
+    (void)TIDAR_CHECK(t >= 0 && t < a.V, TIDAR_CHECK_TOKEN, t);
+    a.next_cand[(size_t)b * k + 1 + lane] = t;
     store_zero(dk);
   }
   if (lane == 0) {
+    (void)TIDAR_CHECK(acc >= 0 && acc <= k, TIDAR_CHECK_ACCEPT, acc);
+    (void)TIDAR_CHECK(bonus >= 0 && bonus < a.V, TIDAR_CHECK_TOKEN, bonus);
+    if (COMMIT && flag)
+      (void)TIDAR_CHECK(false, flag == 3 ? TIDAR_CHECK_PAGE : (L < 0 ? TIDAR_CHECK_LENS : TIDAR_CHECK_CAPACITY), L + acc);
     a.next_cand[(size_t)b * k] = bonus;
     a.accept_len[b] = acc;
     if (COMMIT) {
@@ -228,6 +238,7 @@ __global__ __launch_bounds__(256) void draft_commit_kernel(FusedVerifyArgs a) {
     const unsigned n =
         __hip_atomic_fetch_add(&a.arrive[(size_t)b * kArriveStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = n + 1 == (unsigned)(gridDim.x * a.n_draft_rows);
+    (void)TIDAR_CHECK(n < (unsigned)(gridDim.x * a.n_draft_rows), TIDAR_CHECK_STATE, n);
   }
   __syncthreads();
   if (s_last && threadIdx.x < 64) finalize_sequence<PAGED, COMMIT>(a, b, threadIdx.x, acc, s_bonus, L, flag);
@@ -330,5 +341,9 @@ hipError_t launch_fused_verify(const FusedVerifyArgs& a, hipStream_t s) {
   }
   return hipGetLastError();
 }
+
+#if TIDAR_CHECKED
+TIDAR_CHECK_RECORD_ACCESSOR(check_record_verify_fused)
+#endif
 
 }  // namespace tidar

@@ -40,6 +40,7 @@
 #include <algorithm>
 #include <climits>
 
+#include "check.h"
 #include "common.h"
 #include "launch.h"
 
@@ -266,7 +267,9 @@ __global__ __launch_bounds__(256) void sample_partial_kernel(SampleArgs a) {
   __shared__ int si[8];
   const int chunk = blockIdx.x, row = blockIdx.y;
   const int b = row / a.k, j = row % a.k;
-  const int acc = min(max(a.accept_len[b], 0), a.k);  // written by sample_select_kernel; clamped regardless
+  const int acc_read = a.accept_len[b];
+  if (threadIdx.x == 0 && chunk == 0) (void)TIDAR_CHECK(acc_read >= 0 && acc_read <= a.k, TIDAR_CHECK_ACCEPT, acc_read);
+  const int acc = min(max(acc_read, 0), a.k);  // written by sample_select_kernel; clamped regardless
   const int lo = chunk * kSampleChunk, hi = min(a.V, lo + kSampleChunk);
   float bv = -INFINITY, fv = -INFINITY;
   int bi = INT_MAX, fi = INT_MAX;
@@ -310,7 +313,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void sample_finalize_kernel(SampleA
     int t = reduce_draw(a.part + ((size_t)b * a.k + j) * a.n_chunks, a.n_chunks);
     // a residual with no positive weight in fp32: the draw from p stands in
     if (j == 0 && acc < a.k && t == INT_MAX) t = reduce_draw(a.part_fb + (size_t)b * a.n_chunks, a.n_chunks);
-    if ((threadIdx.x & 63) == 0) a.next_cand[(size_t)b * a.k + j] = t;
+    if ((threadIdx.x & 63) == 0) {
+      (void)TIDAR_CHECK(t >= 0 && t < a.V, TIDAR_CHECK_TOKEN, t);
+      a.next_cand[(size_t)b * a.k + j] = t;
+    }
   }
 }
 
@@ -333,5 +339,9 @@ hipError_t launch_verify_sample(const SampleArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(sample_finalize_kernel, dim3(a.B), dim3(64 * std::min(a.k, kMaxWaves)), 0, s, a);
   return hipGetLastError();
 }
+
+#if TIDAR_CHECKED
+TIDAR_CHECK_RECORD_ACCESSOR(check_record_verify_sample)
+#endif
 
 }  // namespace tidar

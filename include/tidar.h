@@ -466,6 +466,51 @@ int tidar_verify_commit_greedy_paged(int dtype, int B, int Hkv, int D, int max_p
 int tidar_launch_shapes(int path, int B, int k, int V, int Hkv, int D, int dtype, int* shapes);
 
 /* ---------------------------------------------------------------------------
+ * Checked build (debugging aid, not part of the decode step).
+ *
+ * libtidar_checked.so is this library compiled with device-side bounds
+ * tests, for debugging a caller or the kernels.  Each kernel tests every index it reads from device memory
+ * (settled lengths, block-table entries, draft groups and accept lengths
+ * written by an earlier kernel, arrival counters of the verify + commit
+ * state) and every key tile, query, output and step row and split-K chunk
+ * it derives, against the bound the call's sizes give it, before it
+ * addresses a buffer.  A failed test records {code, workgroup, thread,
+ * value} -- the first failure per kernel source file and GPU is kept -- and
+ * the access is redirected in bounds or skipped, so the kernel runs to its
+ * end (no trap).  The documented outcomes of contract violations (NaN
+ * attention rows, err_flags, -1 next drafts) are those of the release
+ * library, and are recorded as well.  Outputs of a call that fails a test
+ * that the release library does not make (codes ROW, CHUNK, KEY_TILE,
+ * TOKEN, STATE) are undefined.  libtidar.so compiles every test out and
+ * exports the same two calls.
+ */
+enum {
+  TIDAR_CHECK_NONE = 0,
+  TIDAR_CHECK_LENS = 1,     /* settled length < 0, or > max_len (attention) */
+  TIDAR_CHECK_PAGE = 2,     /* block-table entry outside [0, n_pages) */
+  TIDAR_CHECK_KEY_TILE = 3, /* key tile or table slot outside the cache (S_max/64 tiles, max_pages slots) */
+  TIDAR_CHECK_ROW = 4,      /* sequence outside [0, B) or query / output / step row outside its range */
+  TIDAR_CHECK_CHUNK = 5,    /* split-K chunk outside the plan's chunks */
+  TIDAR_CHECK_GROUP = 6,    /* draft group read back outside [0, k) */
+  TIDAR_CHECK_ACCEPT = 7,   /* accept length outside [0, k] */
+  TIDAR_CHECK_TOKEN = 8,    /* token id outside [0, V) (e.g. a logit row with nothing above -inf) */
+  TIDAR_CHECK_CAPACITY = 9, /* commit past the cache (L + accept > S_max) */
+  TIDAR_CHECK_STATE = 10    /* verify + commit state not cleared by the previous call */
+};
+
+/* 1 in libtidar_checked.so, 0 in libtidar.so. */
+int tidar_check_enabled(void);
+
+/* Synchronises the current device, then copies into rec[4] (host array
+ * owned by the caller) the first recorded failure {code, workgroup, thread,
+ * value} -- kernel source files taken in a fixed order -- or all zeros, and
+ * if `clear` is non-zero resets every record of the current device.  In
+ * libtidar.so rec is set to zeros and nothing is synchronised.  Returns
+ * TIDAR_OK, TIDAR_EINVAL for a null rec, TIDAR_ELAUNCH if the runtime
+ * reports an error. */
+int tidar_check_read(uint32_t* rec, int clear);
+
+/* ---------------------------------------------------------------------------
  * Measurement helper (not part of the decode step).
  *
  * tidar_read_probe reads `bytes` of device memory at `src` once, in 16 B

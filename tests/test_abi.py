@@ -52,6 +52,36 @@ def test_binding_signatures_match_the_header(T):
         assert len(args) == protos[name], f"{name}: binding has {len(args)} arguments, header {protos[name]}"
 
 
+def test_checked_build_exports_the_same_calls(T):
+    """libtidar_checked.so (device-side bounds tests) exports every declared
+    call and says it is the checked build; the release library says it is
+    not and returns an empty record without touching a device."""
+    if not os.path.exists(T.LIB_CHECKED_PATH):
+        from diffusion_drafted_self_amd.build import build
+        build()
+    raw = ctypes.CDLL(T.LIB_CHECKED_PATH)
+    for n in _declared():
+        assert getattr(raw, n) is not None
+    chk = T._load(T.LIB_CHECKED_PATH)
+    assert chk.tidar_check_enabled() == 1 and T.lib().tidar_check_enabled() == 0
+    assert chk.tidar_abi_version() == T.lib().tidar_abi_version()
+    rec = (ctypes.c_uint32 * 4)(1, 2, 3, 4)
+    assert T.lib().tidar_check_read(rec, 1) == T.TIDAR_OK and list(rec) == [0, 0, 0, 0]
+    assert T.check_read() == (0, 0, 0, 0)
+    assert chk.tidar_check_read(None, 0) == T.TIDAR_EINVAL  # refused before any device call
+    assert T.lib().tidar_check_read(None, 0) == T.TIDAR_EINVAL
+    # host validation is the same code in both
+    n = ctypes.c_size_t(0)
+    for lib in (chk, T.lib()):
+        assert lib.tidar_step_attention_workspace(0, 2, 6, 4, 128, 256, 100, 4, 4, 0, ctypes.byref(n)) == T.TIDAR_EINVAL
+
+
+def test_check_codes_match_the_header(T):
+    text = open(os.path.join(ROOT, "include", "tidar.h")).read()
+    codes = {int(v): name.lower() for name, v in re.findall(r"\bTIDAR_CHECK_(\w+)\s*=\s*(\d+)", text)}
+    assert codes == T.CHECK_CODES
+
+
 def test_strerror_and_version(T):
     assert T.lib().tidar_abi_version() == 1
     for code in (0, -1, -2, -3, -4, 7):
