@@ -67,9 +67,9 @@ HBM_PEAK_GBPS = 8000.0
 COPY_CALIB_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_step_8b_traffic.txt")
 ATTN_SOURCES = [os.path.join(ROOT, "diffusion_drafted_self_amd", "csrc", n)
-                for n in ("attention.hip", "attention_pp.hip", "attn_tile.h", "common.h", "launch.h", "lds_dma.h")]
+                for n in ("attention.hip", "attention_pp.hip", "attn_tile.h", "check.h", "common.h", "launch.h", "lds_dma.h")]
 LM_SOURCES = [os.path.join(ROOT, "diffusion_drafted_self_amd", "csrc", n)
-              for n in ("lmhead.hip", "common.h", "launch.h", "lds_dma.h")]
+              for n in ("lmhead.hip", "check.h", "common.h", "launch.h", "lds_dma.h")]
 LM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_verify_8b_traffic.txt")
 
 
@@ -395,7 +395,7 @@ def summarize_counters(dirname, workload, kernel_env):
     dur_us = statistics.mean(durs) if durs else float("nan")
     mfma_busy = m["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles
     rows = [
-        ("kernel", kname.split("(")[0].replace("(anonymous namespace)::", "")),
+        ("kernel", kname.replace("(anonymous namespace)::", "").split("(")[0]),
         ("dispatches averaged", len(durs)),
         ("duration under counters, us", f"{dur_us:.2f}"),
         ("GRBM_GUI_ACTIVE per XCD, cycles", f"{gui:.0f}"),
