@@ -95,12 +95,14 @@ _LOADED = {}
 def lib() -> ctypes.CDLL:
     """The library the calls of this module go through: libtidar.so (loaded
     on first use; raises ImportError if it has not been built), or the
-    checked build inside ``checked_library()``."""
+    checked build inside ``checked_library()`` -- or throughout, when the
+    environment sets TIDAR_LIBRARY=checked (a debugging run)."""
     global _LIB
     if _LIB is None:
-        if LIB_PATH not in _LOADED:
-            _LOADED[LIB_PATH] = _load(LIB_PATH)
-        _LIB = _LOADED[LIB_PATH]
+        path = LIB_CHECKED_PATH if os.environ.get("TIDAR_LIBRARY") == "checked" else LIB_PATH
+        if path not in _LOADED:
+            _LOADED[path] = _load(path)
+        _LIB = _LOADED[path]
     return _LIB
 
 

@@ -62,17 +62,16 @@ def test_checked_build_exports_the_same_calls(T):
     raw = ctypes.CDLL(T.LIB_CHECKED_PATH)
     for n in _declared():
         assert getattr(raw, n) is not None
-    chk = T._load(T.LIB_CHECKED_PATH)
-    assert chk.tidar_check_enabled() == 1 and T.lib().tidar_check_enabled() == 0
-    assert chk.tidar_abi_version() == T.lib().tidar_abi_version()
+    chk, rel = T._load(T.LIB_CHECKED_PATH), T._load(T.LIB_PATH)
+    assert chk.tidar_check_enabled() == 1 and rel.tidar_check_enabled() == 0
+    assert chk.tidar_abi_version() == rel.tidar_abi_version()
     rec = (ctypes.c_uint32 * 4)(1, 2, 3, 4)
-    assert T.lib().tidar_check_read(rec, 1) == T.TIDAR_OK and list(rec) == [0, 0, 0, 0]
-    assert T.check_read() == (0, 0, 0, 0)
+    assert rel.tidar_check_read(rec, 1) == T.TIDAR_OK and list(rec) == [0, 0, 0, 0]
     assert chk.tidar_check_read(None, 0) == T.TIDAR_EINVAL  # refused before any device call
-    assert T.lib().tidar_check_read(None, 0) == T.TIDAR_EINVAL
+    assert rel.tidar_check_read(None, 0) == T.TIDAR_EINVAL
     # host validation is the same code in both
     n = ctypes.c_size_t(0)
-    for lib in (chk, T.lib()):
+    for lib in (chk, rel):
         assert lib.tidar_step_attention_workspace(0, 2, 6, 4, 128, 256, 100, 4, 4, 0, ctypes.byref(n)) == T.TIDAR_EINVAL
 
 

@@ -8,6 +8,7 @@ commit state that was not cleared -- are recorded with their code while
 every kernel runs to its end (the outcomes the release library documents
 for them are unchanged)."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -254,6 +255,7 @@ def test_checked_records_a_state_that_was_not_cleared():
     assert rec[0] == CODE["state"], rec
 
 
+@pytest.mark.skipif(os.environ.get("TIDAR_LIBRARY") == "checked", reason="the whole run uses the checked build")
 def test_release_library_reports_no_checks():
     assert tidar.lib().tidar_check_enabled() == 0
     assert tidar.check_read() == (0, 0, 0, 0)
