@@ -435,6 +435,17 @@ def summarize_counters(dirname, workload, kernel_env):
     print("\n".join(lines))
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the oracle baseline."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, d, v, a_planted, args):
     """The oracle (as it stands) on the same workload: three full steps."""
     import numpy as np
@@ -485,7 +496,7 @@ def cpu_baseline(wl, d, v, a_planted, args):
             ctx.__exit__(None, None, None)
     attn, ver, com, _, _ = step_bytes(s, wl.V, a_planted, args.verify, wl.d_model)
     return {"value": round((attn + ver + com) / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle", "seconds_per_step": round(dt, 3),
+            "kind": "oracle", "seconds_per_step": round(dt, 3), "cpu_model": cpu_model(), "host_cores": cores,
             "sample": f"{n_steps} full {wl.name} steps (attention over all {s.B}x{s.Hq} heads, {args.verify} verify, "
                       "commit" + (", the LM head on 2 sequences scaled to the batch" if args.verify == "lmhead" else "")
                       + "), "
@@ -584,6 +595,7 @@ def cpu_baseline_train(d, N, bs, scale, B, Hq, D):
     dt = time.perf_counter() - t0
     flops = 4 * D * train_pairs(N, bs) * len(heads)
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "seconds": round(dt, 2),
             "sample": f"{len(heads)} of {B * Hq} heads of train_8b (dense float64 over the full T x T mask)"}
 
@@ -918,6 +930,7 @@ def main():
     # host's launch overhead.
     vc_ms = None
     attn_ms_pair_mean = None
+    attn_ms_warm = None
     queued = args.verify == "greedy"
     if queued:
         def queued_run(fn, per_call):
@@ -940,6 +953,8 @@ def main():
         _, attn_ms = queued_run(attention, True)
         attn_ms_pair_mean = sum(attn_ms) / K
         attn_ms_mean, _ = queued_run(attention, False)
+        # warm: the same replica every call (what caches keep of it between calls is reused)
+        attn_ms_warm, _ = queued_run(lambda r: attention(reps[0]), False)
         vc_ms, _ = queued_run(lambda r: verify_commit(r, 0), False)
         for r in reps:
             if a_planted is not None:
@@ -1006,10 +1021,12 @@ def main():
         "attention_achievable_frac": round(attn_gbps / read_gbps, 4),
         "attention_tflops": round((flops + flops_step) / (attn_ms_mean * 1e-3) / 1e12, 2),
         "attention_mfma_frac": round((flops + flops_step) / (attn_ms_mean * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "attention_us_warm": None if attn_ms_warm is None else round(attn_ms_warm * 1e3, 2),
         "verify_commit_us": round((vc_ms if vc_ms is not None else step_ms - attn_ms_mean) * 1e3, 2),
         "attention_us_event_pairs": round(attn_ms_pair_mean * 1e3, 2) if vc_ms is not None else None,
-        "timing": ("attention_us / verify_commit_us: each call alone, K in a row queued behind a spin kernel "
-                   "(GPU time); step_us: eager whole steps; step_us_graph: replayed whole steps"
+        "timing": ("attention_us / verify_commit_us: each call alone, K in a row on the rotating (cold) replicas, "
+                   "queued behind a spin kernel (GPU time); attention_us_warm: the same on one replica (warm); "
+                   "step_us: eager whole steps; step_us_graph: replayed whole steps"
                    if vc_ms is not None else "eager steps, an event pair around each attention call"),
         "roofline": attention_roofline(attn_b, flops + flops_step, attn_ms_mean,
                                        traffic if wl.name == "step_8b" and not args.paged else None),
