@@ -62,6 +62,9 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+SUSTAIN_MS = 25.0         # untimed load before the queued timed calls (the clock settles within ~20 ms)
+MAX_SUSTAIN_CALLS = 5000
+HOST_US_PER_CALL = 60.0   # the host's enqueue time per call, generously: sizes the spin that gives it a head start
 METRIC = "KV-cache GB/s and decode-step latency (µs) for TiDAR step attention, % of HBM peak"
 HBM_PEAK_GBPS = 8000.0
 COPY_CALIB_BYTES = 1 << 30
@@ -102,6 +105,9 @@ def parse():
     p.add_argument("--loop", type=int, default=0, metavar="N",
                    help="serving loop: N consecutive steps on one cache whose lengths the commit advances in "
                         "place (no restore), per-step p50/p99 and mean GB/s as the lengths grow")
+    p.add_argument("--clock-trace", type=int, default=0, metavar="N",
+                   help="print the attention time of N back-to-back calls after an idle spell, per 10 calls, in "
+                        "call order (how the part's clock moves with the time under load), then exit")
     p.add_argument("--workload", default="step_8b",
                    choices=["step_8b", "step_1p5b", "step_8b_long", "ragged_8b", "train_8b"],
                    help="synthetic workload (the reported line is the 8B-shaped step; ragged_8b is one step of "
@@ -433,6 +439,32 @@ def summarize_counters(dirname, workload, kernel_env):
     with open(os.path.join(ROOT, "profiles", f"attention_{tag}_counters.md"), "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))
+
+
+def clock_trace(N, name, reps, n_rep, attention, torch, stream):
+    """N attention calls back to back on the rotating replicas after a ~20 ms
+    idle spin, an event between consecutive calls; prints the mean time per
+    call of each group of 10 against the time since the first call."""
+    for i in range(5):
+        attention(reps[i % n_rep])
+    print(f"# attention per call on {name}, back to back after an idle spin (mean of each 10 calls)")
+    for trial in range(2):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(40_000_000)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(N + 1)]
+        ev[0].record(stream)
+        for i in range(N):
+            attention(reps[i % n_rep])
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        d = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(N)]
+        print(f"trial {trial}: | ms since the first call | us per call |")
+        t = 0.0
+        for i in range(0, N, 10):
+            grp = d[i:i + 10]
+            print(f"| {t / 1e3:.1f} | {sum(grp) / len(grp):.1f} |")
+            t += sum(grp)
+        sys.stdout.flush()
 
 
 def cpu_model() -> str:
@@ -861,6 +893,9 @@ def main():
     if args.loop:
         bench_loop(args, wl, d, v, a_planted, reps, n_rep, attention, verify_commit, tidar, torch, np, dev, stream)
         return
+    if args.clock_trace:
+        clock_trace(args.clock_trace, wl.name, reps, n_rep, attention, torch, stream)
+        return
     ev_a = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     # the fused LM head dominates its step: its own end event after verify
     ev_v = [torch.cuda.Event(enable_timing=True) if args.verify == "lmhead" else None for _ in range(K)]
@@ -923,24 +958,33 @@ def main():
         del graphs
 
     # The attention calls alone and the verify + commit calls alone, each K
-    # in a row on the rotating replicas, queued behind a short spin kernel so
-    # the host has enqueued all of them before the GPU reaches the first:
-    # the event pair around each attention call then times the GPU's work,
-    # the kernel's launch duration (what rocprofv3 reports for it), not the
-    # host's launch overhead.
+    # in a row on the rotating replicas, queued behind a spin kernel so the
+    # host has enqueued all of them before the GPU reaches the first: an
+    # event pair around the K calls then times the GPU's work (what
+    # rocprofv3 reports for the kernels), not the host's launch overhead.
+    # The clock the part runs at depends on how long it has been under load
+    # (--clock-trace shows it): after an idle spell the first ~2 ms of calls
+    # run boosted, the power controller then clamps for several ms, and the
+    # clock settles after ~15-20 ms.  So the timed calls follow untimed
+    # calls of the same work lasting SUSTAIN_MS and run at the clock the
+    # part sustains under this load, as in a serving loop; the *_after_idle
+    # figures time the same K calls straight after the spin instead.
     vc_ms = None
     attn_ms_pair_mean = None
-    attn_ms_warm = None
+    attn_ms_warm = attn_ms_after_idle = vc_ms_after_idle = None
     queued = args.verify == "greedy"
     if queued:
-        def queued_run(fn, per_call):
+        def queued_run(fn, per_call, n_pre=0):
             torch.cuda.synchronize()
-            torch.cuda._sleep(20_000_000)  # ~10 ms at the shader clock
+            # the host's head start: it enqueues the untimed and the timed calls while the GPU spins
+            torch.cuda._sleep(int(2e6 * max(10.0, HOST_US_PER_CALL * (n_pre + K) / 1e3)))
+            for i in range(n_pre):
+                fn(reps[(Wu + i) % n_rep])
             evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
             q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             q0.record(stream)
             for i in range(K):
-                r = reps[(Wu + i) % n_rep]
+                r = reps[(Wu + n_pre + i) % n_rep]
                 if per_call:
                     evs[i][0].record(stream)
                 fn(r)
@@ -950,12 +994,18 @@ def main():
             torch.cuda.synchronize()
             return q0.elapsed_time(q1) / K, sorted(e0.elapsed_time(e1) for e0, e1 in evs) if per_call else None
 
-        _, attn_ms = queued_run(attention, True)
+        def sustain_calls(ms_per_call):  # untimed calls that keep the GPU busy for SUSTAIN_MS
+            return int(min(MAX_SUSTAIN_CALLS, math.ceil(SUSTAIN_MS / max(ms_per_call, 1e-3))))
+
+        attn_ms_after_idle, _ = queued_run(attention, False)
+        n_pre = sustain_calls(attn_ms_after_idle)
+        _, attn_ms = queued_run(attention, True, n_pre)
         attn_ms_pair_mean = sum(attn_ms) / K
-        attn_ms_mean, _ = queued_run(attention, False)
+        attn_ms_mean, _ = queued_run(attention, False, n_pre)
         # warm: the same replica every call (what caches keep of it between calls is reused)
-        attn_ms_warm, _ = queued_run(lambda r: attention(reps[0]), False)
-        vc_ms, _ = queued_run(lambda r: verify_commit(r, 0), False)
+        attn_ms_warm, _ = queued_run(lambda r: attention(reps[0]), False, n_pre)
+        vc_ms_after_idle, _ = queued_run(lambda r: verify_commit(r, 0), False)
+        vc_ms, _ = queued_run(lambda r: verify_commit(r, 0), False, sustain_calls(vc_ms_after_idle))
         for r in reps:
             if a_planted is not None:
                 assert r["acc"].cpu().numpy().tolist() == a_planted.tolist()
@@ -1022,11 +1072,14 @@ def main():
         "attention_tflops": round((flops + flops_step) / (attn_ms_mean * 1e-3) / 1e12, 2),
         "attention_mfma_frac": round((flops + flops_step) / (attn_ms_mean * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "attention_us_warm": None if attn_ms_warm is None else round(attn_ms_warm * 1e3, 2),
+        "attention_us_after_idle": None if attn_ms_after_idle is None else round(attn_ms_after_idle * 1e3, 2),
         "verify_commit_us": round((vc_ms if vc_ms is not None else step_ms - attn_ms_mean) * 1e3, 2),
+        "verify_commit_us_after_idle": None if vc_ms_after_idle is None else round(vc_ms_after_idle * 1e3, 2),
         "attention_us_event_pairs": round(attn_ms_pair_mean * 1e3, 2) if vc_ms is not None else None,
-        "timing": ("attention_us / verify_commit_us: each call alone, K in a row on the rotating (cold) replicas, "
-                   "queued behind a spin kernel (GPU time); attention_us_warm: the same on one replica (warm); "
-                   "step_us: eager whole steps; step_us_graph: replayed whole steps"
+        "timing": (f"attention_us / verify_commit_us: each call alone, K in a row on the rotating (cold) replicas, "
+                   f"queued (GPU time) after {SUSTAIN_MS:.0f} ms of untimed calls of the same work (the sustained "
+                   "clock); *_after_idle: the same K calls straight after an idle spin; attention_us_warm: sustained, "
+                   "one replica (warm); step_us: eager whole steps; step_us_graph: replayed whole steps"
                    if vc_ms is not None else "eager steps, an event pair around each attention call"),
         "roofline": attention_roofline(attn_b, flops + flops_step, attn_ms_mean,
                                        traffic if wl.name == "step_8b" and not args.paged else None),
