@@ -310,7 +310,8 @@ def summarize(dirname):
 # arguments of the traced run, the workload, where the calls come from)
 _STEP_CALLS = ("The step's kernels run in the warm-up and timed eager steps, once per input replica before its graph "
                "capture, in the graph replays (warm-up and timed), and in the queued runs of the attention calls "
-               "alone and the verify + commit calls alone.")
+               "alone and the verify + commit calls alone (each straight after an idle spin, and after 25 ms of "
+               "untimed calls of the same work).")
 TRACES = {
     "attention_step_8b": ("one TiDAR step on the 8B-shaped workload", "--steps 20 --warmup 5",
                           "B=16, 32/8 heads of 128, prefix 4096, k=8 (+64 draft slots), greedy verify over 128256 "
@@ -345,6 +346,35 @@ TRACES = {
 }
 
 
+def attention_calls_by_load(dirname, gap_ns=20_000, sustained_ms=SUSTAIN_MS):
+    """The attention kernel's calls of a kernel-trace run, grouped by how
+    long the GPU had been running attention back to back when each started
+    (a run: each call starting within gap_ns of the previous one's end).
+    The bench times the calls at least sustained_ms into such a run."""
+    rows = _csv_rows(os.path.join(dirname, "kt", "*kernel_trace.csv"))
+    calls = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows
+                   if "attn_" in r["Kernel_Name"] and "merge" not in r["Kernel_Name"])
+    if not calls:
+        return []
+    groups = {"first 2 ms": [], f"2 to {sustained_ms:.0f} ms": [], f"{sustained_ms:.0f} ms on (what the bench times)": []}
+    keys = list(groups)
+    t_run = calls[0][0]
+    prev_end = None
+    for s_ns, e_ns in calls:
+        if prev_end is not None and s_ns - prev_end >= gap_ns:
+            t_run = s_ns
+        into = (s_ns - t_run) / 1e6
+        groups[keys[0] if into < 2 else keys[1] if into < sustained_ms else keys[2]].append((e_ns - s_ns) / 1e3)
+        prev_end = e_ns
+    out = ["", "Attention calls by time under load (the part's clock boosts after an idle spell, is clamped by "
+           "its power controller a few ms later and settles after ~20 ms; a run is a sequence of attention calls "
+           f"each starting within {gap_ns / 1e3:.0f} us of the previous one's end):", "",
+           "| time into the run | calls | average us |", "|---|---|---|"]
+    for k, v in groups.items():
+        out.append(f"| {k} | {len(v)} | {sum(v) / len(v):.2f} |" if v else f"| {k} | 0 | - |")
+    return out
+
+
 def summarize_trace(dirname, name):
     """profiles/<name>_kernel_trace.md from the kernel-trace run under
     dirname/kt (the command in TRACES[name])."""
@@ -360,6 +390,7 @@ def summarize_trace(dirname, name):
         kname = r["Name"].replace("(anonymous namespace)::", "").replace("tidar::", "")
         lines.append(f"| `{kname[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    lines += attention_calls_by_load(dirname)
     lines += ["", calls + " `copyBuffer` is the settled lengths' 64-byte "
               "restore after each step and the replicas' set-up copies (harness). `read_probe_kernel` is the "
               "achievable-bandwidth measurement (a streaming read of 4 GiB, six calls). Other rows of the run "
