@@ -612,12 +612,21 @@ def bench_train(args):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(K):
-        call(reps[(Wu + i) % n_rep])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / K
+
+    def timed(n_pre):  # K calls queued behind a spin, after n_pre untimed ones (see the step's queued timing)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2e6 * max(10.0, HOST_US_PER_CALL * (n_pre + K) / 1e3)))
+        for i in range(n_pre):
+            call(reps[(Wu + i) % n_rep])
+        t0.record(stream)
+        for i in range(K):
+            call(reps[(Wu + n_pre + i) % n_rep])
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / K
+
+    ms_after_idle = timed(0)
+    ms = timed(int(min(MAX_SUSTAIN_CALLS, math.ceil(SUSTAIN_MS / ms_after_idle))))  # at the sustained clock
     assert torch.isfinite(reps[0]["out"].float()).all()
     flops = 4 * D * train_pairs(N, bs) * B * Hq
     tflops = flops / (ms * 1e-3) / 1e12
@@ -629,6 +638,9 @@ def bench_train(args):
         "config": {"workload": "train_8b", "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
                    "clean_positions": N, "sequence": 2 * N, "block": bs, "cold_replicas": n_rep},
         "attention_us": round(ms * 1e3, 2),
+        "attention_us_after_idle": round(ms_after_idle * 1e3, 2),
+        "timing": (f"attention_us: K calls queued after {SUSTAIN_MS:.0f} ms of untimed calls (the sustained clock); "
+                   "attention_us_after_idle: the same K calls straight after an idle spin"),
         "roofline": {"bound": "mfma", "kernel": "tidar_train_attention", "achieved": round(tflops, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None, "algorithmic_flops": flops},

@@ -214,7 +214,7 @@ __device__ __forceinline__ float pp_softmax_shared(const floatx4& ss, float ms, 
   return sum;
 }
 
-template <int D, int NS, bool PAGED>
+template <int D, int NS, bool PAGED, bool TRAIN = false>
 __global__ __launch_bounds__(PPT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_pp_kernel(AttnArgs a) {
   static_assert(D == 128, "the two-waves-per-SIMD layout is built for head dim 128");
@@ -238,7 +238,7 @@ void attn_pp_kernel(AttnArgs a) {
   // steps rank the units longest sequence first and deal each group of 8
   // ranks over the 8 XCDs in a snake (see the four-wave kernel)
   int rw, split, kvh, b;
-  if (a.B <= kMaxRankedB && (a.B * a.Hkv) % 8 == 0) {
+  if (!TRAIN && a.B <= kMaxRankedB && (a.B * a.Hkv) % 8 == 0) {
     __shared__ int s_len[kMaxRankedB];
     __shared__ int s_pick;
     const int wpu = a.n_rowblk * a.n_split;
@@ -274,9 +274,20 @@ void attn_pp_kernel(AttnArgs a) {
   if (!TIDAR_CHECK(b >= 0 && b < a.B, TIDAR_CHECK_ROW, b)) b = 0;
   if (!TIDAR_CHECK(split < a.n_split, TIDAR_CHECK_CHUNK, split)) split = 0;
 
-  // tiles [T0, T1) of this workgroup: wave w owns T0 + w; T0 + 8 is shared
-  const int T0 = rw * a.n16 / a.n_rowblk;
-  const int T1 = (rw + 1) * a.n16 / a.n_rowblk;
+  // tiles [T0, T1) of this workgroup: wave w owns T0 + w; T0 + 8 is shared.
+  // TRAIN: PPW + NS tiles per workgroup inside one half of the sequence, H
+  // workgroups per half; workgroup ids alternate between the halves from
+  // their last (heaviest) blocks down
+  int T0, T1;
+  if constexpr (TRAIN) {
+    const int H = a.n_rowblk / 2, n16h = a.n16 / 2, tpw = PPW + NS;
+    const int half = rw & 1, blk = H - 1 - (rw >> 1);
+    T0 = half * n16h + blk * tpw;
+    T1 = min(T0 + tpw, (half + 1) * n16h);
+  } else {
+    T0 = rw * a.n16 / a.n_rowblk;
+    T1 = (rw + 1) * a.n16 / a.n_rowblk;
+  }
   const int ti = T0 + wave;
   const int mrow = 16 * ti + (lane & 15);
   const bool ok = ti < T1 && mrow < a.M;
@@ -294,7 +305,7 @@ void attn_pp_kernel(AttnArgs a) {
     return a.lse + ((size_t)b * a.Hq + h) * a.R + r;
   };
 
-  const int L = a.lens[b];
+  const int L = TRAIN ? a.S_max : a.lens[b];  // TRAIN: every position's keys are in the buffers
   KvMap<D, PAGED> kv;
   const size_t pair = (size_t)b * a.Hkv + kvh;
   if constexpr (PAGED) {
@@ -310,7 +321,7 @@ void attn_pp_kernel(AttnArgs a) {
   }
   kv.n_tiles = PAGED ? a.max_pages : a.S_max / TK;
   kv.n_pages = a.n_pages;
-  bool violated = L < 0 || L > a.max_len;
+  bool violated = !TRAIN && (L < 0 || L > a.max_len);
   if constexpr (PAGED) {  // every page holding a settled position must be in the pools
     bool bad = false;
     if (!violated)
@@ -336,22 +347,46 @@ void attn_pp_kernel(AttnArgs a) {
     }
     return;
   }
-  const int Ltot = L + a.R;
+  const int Ltot = TRAIN ? L : L + a.R;
   const int kb = split * a.chunk;
   if (kb >= Ltot) return;
   const int ke = min(kb + a.chunk, Ltot);
   const int n_valid = (Ltot + a.chunk - 1) / a.chunk;
 
   const size_t step_stride = (size_t)a.Hkv * D;
-  const bf16* ks_base = (const bf16*)a.k_step + (size_t)b * a.R * step_stride + kvh * D;
-  const bf16* vs_base = (const bf16*)a.v_step + (size_t)b * a.R * step_stride + kvh * D;
+  const bf16* ks_base = TRAIN ? nullptr : (const bf16*)a.k_step + (size_t)b * a.R * step_stride + kvh * D;
+  const bf16* vs_base = TRAIN ? nullptr : (const bf16*)a.v_step + (size_t)b * a.R * step_stride + kvh * D;
 
-  // keys [kb, fast_end) through the rings; tiles of [mA0, ke) masked
-  const int fast_end = min(ke, (L / TK) * TK);
-  const int mA0 = max(kb, fast_end);
+  // keys [kb, fast_end) through the rings; the tiles of [mA0, mA1) and
+  // [mB0, mB1) masked.  Decode: [mA0, ke), the tiles reaching past the
+  // prefix.  TRAIN: the key tiles every row of the workgroup sees in full
+  // go through the ring; the few on its causal diagonal (clean half), or
+  // at its blocks' prefix ends and on its own blocks (masked half), are
+  // masked.
+  int fast_end, mA0, mA1, mB0 = 0, mB1 = 0;
+  if constexpr (TRAIN) {
+    const int N = a.train_N, bs = a.train_bs;
+    const int r_lo = 16 * T0 / a.G, r_hi = (min(16 * T1, a.M) - 1) / a.G;
+    if (r_lo < N) {
+      fast_end = (r_lo + 1) / TK * TK;
+      mA1 = (r_hi + TK) / TK * TK;
+    } else {
+      const int lo_min = (r_lo - N) / bs * bs, lo_max = (r_hi - N) / bs * bs;
+      fast_end = lo_min / TK * TK;
+      mA1 = (lo_max + TK - 1) / TK * TK;
+      mB0 = (N + lo_min) / TK * TK;
+      mB1 = (N + min(lo_max + bs, N) + TK - 1) / TK * TK;
+    }
+    mA0 = fast_end;
+  } else {
+    fast_end = min(ke, (L / TK) * TK);
+    mA0 = max(kb, fast_end);
+    mA1 = ke;
+  }
   const int n = fast_end > kb ? (fast_end - kb) / TK : 0;  // ring tiles
   const int tb = kb / TK;
-  const int n_tail = (ke - mA0 + TK - 1) / TK;
+  const int nA = (mA1 - mA0 + TK - 1) / TK, nB = (mB1 - mB0 + TK - 1) / TK;  // a range may end mid-tile
+  const int n_tail = TRAIN ? nA + nB : nA;
   if (tid == 0) ovf_flag = 0;  // published by the first barrier below
   DmaPlan<D, PPW> plan;
   dma_plan<D, PPW>(plan, wave, lane);
@@ -396,24 +431,29 @@ void attn_pp_kernel(AttnArgs a) {
   // The shared tile's four key blocks meet in LDS for their row maximum.
   lds_char* const sKx = kslot(RING - 1);
   lds_char* const sVx = vslot(RING - 1);
+  // zone tests take step-row indices (decode) or positions (training)
+  const int zoff = TRAIN ? 0 : L;
+  auto zone = [&](int m) __attribute__((always_inline)) {
+    return TRAIN ? train_zone(m / a.G, a.train_N, a.train_bs) : step_zone(m / a.G, a.k);
+  };
   auto exact_tile = [&](int t0, bool masked) __attribute__((always_inline)) {
     pp_scores<D>(sKx, q, qs, sh_s, s, ss, lane, simd);
     if (masked) {
-      const StepZone z = step_zone(mrow / a.G, a.k);
+      const StepZone z = zone(mrow);
 #pragma unroll
       for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int c = t0 + krow_of(kb4, 4 * hi + v);
-          const bool vis = (c < ke) & z.sees(c - L);
+          const bool vis = (c < ke) & z.sees(c - zoff);
           s[kb4][v] = vis ? s[kb4][v] : -INFINITY;
         }
       if (sh_s) {
-        const StepZone zs = step_zone(mrow_s / a.G, a.k);
+        const StepZone zs = zone(mrow_s);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int c = t0 + krow_of(simd, 4 * hi + v);
-          const bool vis = (c < ke) & zs.sees(c - L);
+          const bool vis = (c < ke) & zs.sees(c - zoff);
           ss[v] = vis ? ss[v] : -INFINITY;
         }
       }
@@ -474,7 +514,10 @@ void attn_pp_kernel(AttnArgs a) {
 
   // ---- masked tiles, staged through registers into slot RING-1 ----------
   StagedRows<D, PPT> staged;
-  auto tail_t0 = [&](int i) __attribute__((always_inline)) { return mA0 + i * TK; };
+  auto tail_t0 = [&](int i) __attribute__((always_inline)) {
+    if constexpr (TRAIN) return i < nA ? mA0 + i * TK : mB0 + (i - nA) * TK;
+    return mA0 + i * TK;
+  };
   auto tail_issue = [&](int i) __attribute__((always_inline)) {
     const int t0 = tail_t0(i);
     stage_issue<D, PPT>(staged, t0 < L ? kv.ktile(t0 / TK) : nullptr, ks_base, vs_base, step_stride, t0, L, Ltot,
@@ -674,6 +717,16 @@ hipError_t launch_attention_pp_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
   if (a.D != 128) return hipErrorInvalidValue;
   return a.ns ? launch_pp<128, 1>(a, s) : launch_pp<128, 0>(a, s);
+}
+
+// Training-mask attention on the eight-wave kernel: 2 x H workgroups per
+// (sequence, KV head), one row tile per wave (no shared tile).
+hipError_t launch_train_attention_pp_bf16(const AttnArgs& a, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  if (a.D != 128 || a.n_split != 1 || a.ns != 0) return hipErrorInvalidValue;
+  const int nblk = a.B * a.Hkv * a.n_rowblk;
+  hipLaunchKernelGGL((attn_pp_kernel<128, 0, false, true>), dim3(nblk), dim3(PPT), 0, s, a);
+  return hipGetLastError();
 }
 
 #if TIDAR_CHECKED

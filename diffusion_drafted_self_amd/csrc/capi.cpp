@@ -70,6 +70,11 @@ int kernel_choice() {
   return 0;
 }
 
+// The training mask's kernel (head dim 128): the eight-wave one unless
+// TIDAR_ATTN_KERNEL asks for the four-wave one.  On the 8B training shape
+// it took 1138 us against 1370 (sustained clock, one box).
+bool train_kernel_is_pp() { return kernel_choice() != 2; }
+
 bool shape_built(int nf, int ns) {
   if (nf < 0 || nf > 3 || ns < 0 || ns > 3 || nf + ns == 0) return false;
   return !(nf == 3 && ns > 0) && !(nf == 2 && ns == 3);
@@ -487,17 +492,22 @@ int tidar_train_attention(int dtype, int B, int Hq, int Hkv, int D, int N, int b
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return TIDAR_EINVAL;
   if (lse && !aligned(lse, 4)) return TIDAR_EINVAL;
 
-  // row tiles of 16 per half; 4*nf tiles per workgroup, as many as keep
-  // the chip fed at least four workgroups per CU
+  // row tiles of 16 per half.  Four-wave kernel: 4*nf tiles per workgroup,
+  // as many as keep the chip fed at least four workgroups per CU.
+  // Eight-wave kernel (head dim 128): eight tiles per workgroup, one per
+  // wave (a ninth, shared tile measured 8% slower here: the workgroups are
+  // many and the shared tile's extra MFMAs and LDS round trips are not).
   const long n16h = M / 32;
   const long pairs = (long)B * Hkv;
+  const bool pp = D == 128 && train_kernel_is_pp();
   int nf = 1;
-  for (int c = 3; c >= 2; --c)
-    if (pairs * 2 * cdiv(n16h, 4 * c) >= 4L * kCUs) {
-      nf = c;
-      break;
-    }
-  const long H = cdiv(n16h, 4 * nf);
+  if (!pp)
+    for (int c = 3; c >= 2; --c)
+      if (pairs * 2 * cdiv(n16h, 4 * c) >= 4L * kCUs) {
+        nf = c;
+        break;
+      }
+  const long H = pp ? cdiv(n16h, 8) : cdiv(n16h, 4 * nf);
   if (pairs * 2 * H > 0x7fffffffL) return TIDAR_EUNSUPPORTED;
 
   tidar::AttnArgs a = {};
@@ -522,13 +532,15 @@ int tidar_train_attention(int dtype, int B, int Hq, int Hkv, int D, int N, int b
   a.n16 = (int)(M / 16);
   a.nf = nf;
   a.ns = 0;
+  a.pp = pp ? 1 : 0;
   a.n_rowblk = (int)(2 * H);
   a.scale_log2 = sm_scale * 1.44269504088896340736f;
   a.single_chunk_direct = 1;
   a.block_table = nullptr;
   a.train_N = N;
   a.train_bs = block;
-  const hipError_t e = tidar::launch_train_attention_bf16(a, static_cast<hipStream_t>(stream));
+  const hipError_t e = pp ? tidar::launch_train_attention_pp_bf16(a, static_cast<hipStream_t>(stream))
+                          : tidar::launch_train_attention_bf16(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
 }
 

@@ -45,6 +45,7 @@ struct AttnArgs {
 
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_pp_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_train_attention_pp_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t s);
 hipError_t launch_train_attention_bf16(const AttnArgs& a, hipStream_t s);
 

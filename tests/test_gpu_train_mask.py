@@ -1,6 +1,8 @@
 """GPU parity of tidar_train_attention (the duplicated training sequence:
 causal clean half, masked half in blocks) against the oracle: element by
-element at small sizes, on sampled rows at the full training shape."""
+element at small sizes, on sampled rows at the full training shape, with
+each of the two kernels (TIDAR_ATTN_KERNEL: "pipe" four waves, "pp" eight
+waves; head dim 64 has the four-wave kernel only)."""
 import numpy as np
 import pytest
 import torch
@@ -43,9 +45,11 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("kern", ["pipe", "pp"])
 @pytest.mark.parametrize("B,Hq,Hkv,D,N,bs", SMALL)
-def test_train_attention_matches_oracle(B, Hq, Hkv, D, N, bs):
-    print(f"train B={B} Hq={Hq} Hkv={Hkv} D={D} N={N} block={bs}", flush=True)
+def test_train_attention_matches_oracle(monkeypatch, kern, B, Hq, Hkv, D, N, bs):
+    monkeypatch.setenv("TIDAR_ATTN_KERNEL", kern)
+    print(f"train {kern} B={B} Hq={Hq} Hkv={Hkv} D={D} N={N} block={bs}", flush=True)
     d = W.train_inputs(B, Hq, Hkv, D, N, seed=N + bs)
     scale = 1.0 / np.sqrt(D)
     out, lse = _run(d, N, bs, scale)
@@ -56,9 +60,11 @@ def test_train_attention_matches_oracle(B, Hq, Hkv, D, N, bs):
 
 
 @pytest.mark.timeout(300)
-def test_train_attention_full_size_sampled():
+@pytest.mark.parametrize("kern", ["pipe", "pp"])
+def test_train_attention_full_size_sampled(monkeypatch, kern):
+    monkeypatch.setenv("TIDAR_ATTN_KERNEL", kern)
     B, Hq, Hkv, D, N, bs = 4, 32, 8, 128, 4096, 8
-    print(f"train full size B={B} N={N} block={bs}", flush=True)
+    print(f"train full size {kern} B={B} N={N} block={bs}", flush=True)
     d = W.train_inputs(B, Hq, Hkv, D, N, seed=1)
     scale = 1.0 / np.sqrt(D)
     out, lse = _run(d, N, bs, scale)
