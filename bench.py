@@ -62,7 +62,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-SUSTAIN_MS = 25.0         # untimed load before the queued timed calls (the clock settles within ~20 ms)
+SUSTAIN_MS = 40.0         # untimed load before the queued timed calls (the clock settles after ~30 ms)
 MAX_SUSTAIN_CALLS = 5000
 HOST_US_PER_CALL = 60.0   # the host's enqueue time per call, generously: sizes the spin that gives it a head start
 METRIC = "KV-cache GB/s and decode-step latency (µs) for TiDAR step attention, % of HBM peak"
@@ -310,7 +310,7 @@ def summarize(dirname):
 # arguments of the traced run, the workload, where the calls come from)
 _STEP_CALLS = ("The step's kernels run in the warm-up and timed eager steps, once per input replica before its graph "
                "capture, in the graph replays (warm-up and timed), and in the queued runs of the attention calls "
-               "alone and the verify + commit calls alone (each straight after an idle spin, and after 25 ms of "
+               "alone and the verify + commit calls alone (each straight after an idle spin, and after 40 ms of "
                "untimed calls of the same work).")
 TRACES = {
     "attention_step_8b": ("one TiDAR step on the 8B-shaped workload", "--steps 20 --warmup 5",
@@ -367,7 +367,7 @@ def attention_calls_by_load(dirname, gap_ns=20_000, sustained_ms=SUSTAIN_MS):
         groups[keys[0] if into < 2 else keys[1] if into < sustained_ms else keys[2]].append((e_ns - s_ns) / 1e3)
         prev_end = e_ns
     out = ["", "Attention calls by time under load (the part's clock boosts after an idle spell, is clamped by "
-           "its power controller a few ms later and settles after ~20 ms; a run is a sequence of attention calls "
+           "its power controller a few ms later and settles after ~30 ms; a run is a sequence of attention calls "
            f"each starting within {gap_ns / 1e3:.0f} us of the previous one's end):", "",
            "| time into the run | calls | average us |", "|---|---|---|"]
     for k, v in groups.items():
@@ -1008,7 +1008,7 @@ def main():
     # The clock the part runs at depends on how long it has been under load
     # (--clock-trace shows it): after an idle spell the first ~2 ms of calls
     # run boosted, the power controller then clamps for several ms, and the
-    # clock settles after ~15-20 ms.  So the timed calls follow untimed
+    # clock settles after ~30 ms.  So the timed calls follow untimed
     # calls of the same work lasting SUSTAIN_MS and run at the clock the
     # part sustains under this load, as in a serving loop; the *_after_idle
     # figures time the same K calls straight after the spin instead.
