@@ -193,7 +193,9 @@ int tidar_step_attention_paged(int dtype, int B, int Hq, int Hkv, int D, int max
  *                                     positions, each transposed)
  *   out      [B][T][Hq][D] (written);  lse [B][Hq][T] f32 natural-log
  *            softmax denominators (written; may be NULL).
- * No workspace.  Other arguments as for tidar_step_attention.
+ * No workspace.  Other arguments as for tidar_step_attention.  Head dim
+ * 128 runs on the eight-wave kernel unless TIDAR_ATTN_KERNEL is "pipe"
+ * (see tidar_step_attention_plan); head dim 64 on the four-wave one.
  * ---------------------------------------------------------------------- */
 int tidar_train_attention(int dtype, int B, int Hq, int Hkv, int D, int N, int block, float sm_scale,
                           const void* q, const void* k, const void* v, void* out, float* lse, void* stream);
