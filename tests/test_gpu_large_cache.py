@@ -115,3 +115,62 @@ def test_fused_verify_commit_past_4gib_matches_oracle(big):
                                        _host_bf16(t["vs"][b:b + 1]), ra[b:b + 1], K)
     assert int(err[b]) == int(re[0]) and int(lens[b]) == int(rl[0])
     assert np.array_equal(bits(t["kc"][b:b + 1]), rk) and np.array_equal(bits(t["vc"][b:b + 1]), rv)
+
+
+def test_paged_attention_and_commit_past_4gib_match_oracle():
+    """A 4.6 GiB page pool per tensor; the checked sequence's pages lie past
+    4 GiB and are scattered; attention against the oracle on those pages,
+    then a commit into its last page, bit for bit."""
+    Bp, n_pages, max_pages = 8, 36000, 520
+    g = torch.Generator(device=DEV)
+    g.manual_seed(515)
+    kp = (torch.randn(n_pages, HKV, 64, D, device=DEV, generator=g) / math.sqrt(D)).to(torch.bfloat16)
+    vp = torch.randn(n_pages, HKV, D, 64, device=DEV, generator=g).to(torch.bfloat16)
+    q = torch.randn(Bp, R, HQ, D, device=DEV, generator=g).to(torch.bfloat16)
+    ks = (torch.randn(Bp, R, HKV, D, device=DEV, generator=g) / math.sqrt(D)).to(torch.bfloat16)
+    vs = torch.randn(Bp, R, HKV, D, device=DEV, generator=g).to(torch.bfloat16)
+    assert kp.numel() * 2 > (1 << 32)
+    rng = np.random.default_rng(3)
+    lens_h = np.array([max_pages * 64 - R - 100 * i for i in range(Bp)], dtype=np.int32)
+    table = np.full((Bp, max_pages), -1, dtype=np.int32)
+    perm = rng.permutation(n_pages)
+    high = perm[perm >= 33000][:max_pages]  # page byte offsets past 4.3 GB
+    table[Bp - 1] = rng.permutation(high)
+    rest = perm[perm < 33000]
+    for i in range(Bp - 1):
+        table[i] = rest[i * max_pages:(i + 1) * max_pages]
+    lens = torch.from_numpy(lens_h).to(DEV)
+    tbl = torch.from_numpy(table).to(DEV)
+    out, lse = tidar.step_attention_paged(q, ks, vs, kp, vp, tbl, lens, K, NG, 1.0, max_len=max_pages * 64 - R)
+    torch.cuda.synchronize()
+    b = Bp - 1
+    used = torch.from_numpy(table[b]).to(DEV).long()
+    kp_b, vp_b = _f32(_host_bf16(kp.index_select(0, used))), _f32(_host_bf16(vp.index_select(0, used)))
+    local = np.arange(max_pages, dtype=np.int32)[None]
+    ref, ref_lse = oracle.paged_attention_ref(_f32(_host_bf16(q[b:b + 1])), _f32(_host_bf16(ks[b:b + 1])),
+                                              _f32(_host_bf16(vs[b:b + 1])), kp_b, vp_b, local, lens_h[b:b + 1], K,
+                                              NG, 1.0)
+    check_attention(out[b:b + 1], lse[b:b + 1], ref, ref_lse, "bf16", what="paged sequence on pages past 4 GiB")
+    # commit k rows of sequence b at its end (its last used page lies past 4 GiB)
+    acc_h = np.zeros(Bp, dtype=np.int32)
+    acc_h[b] = K
+    last = (int(lens_h[b]) + K - 1) // 64
+    pages = sorted({int(lens_h[b]) // 64, last})
+    before_k = {p: _host_bf16(kp[int(table[b, p])]) for p in pages}
+    before_v = {p: _host_bf16(vp[int(table[b, p])]) for p in pages}
+    err = torch.full((Bp,), -1, dtype=torch.int32, device=DEV)
+    tidar.kv_commit_paged(kp, vp, tbl, lens, ks, vs, torch.from_numpy(acc_h).to(DEV), K, err)
+    torch.cuda.synchronize()
+    assert int(err[b]) == 0 and int(lens[b]) == int(lens_h[b]) + K
+    ksh, vsh = _host_bf16(ks[b]), _host_bf16(vs[b])  # [R][Hkv][D]
+    for p in pages:
+        want_k, want_v = before_k[p].copy(), before_v[p].copy()  # [Hkv][64][D], [Hkv][D][64]
+        for i in range(K):
+            pos = int(lens_h[b]) + i
+            if pos // 64 == p:
+                want_k[:, pos % 64, :] = ksh[i]
+                want_v[:, :, pos % 64] = vsh[i]
+        assert np.array_equal(_host_bf16(kp[int(table[b, p])]), want_k)
+        assert np.array_equal(_host_bf16(vp[int(table[b, p])]), want_v)
+    del kp, vp
+    torch.cuda.empty_cache()
