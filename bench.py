@@ -13,11 +13,16 @@ launch stream (step_us), and the same K steps replayed from HIP graphs
 Infinity Cache cannot serve them warm.  After each step the settled lengths
 are restored (a 64-byte device copy) so every step is the same workload.
 The attention calls alone, and the verify + commit calls alone, are then
-timed as K calls in a row queued behind a short spin kernel, so the host has
-enqueued them all before the GPU starts: one event pair around the K calls
-gives the GPU time per call (the value and the roofline figure; it agrees
-with the kernel's average duration in a rocprofv3 trace), an event pair
-around each call gives p50/p99.
+timed as K calls in a row queued behind a spin kernel, so the host has
+enqueued them all before the GPU starts, and after 40 ms of untimed calls of
+the same work: the part boosts its clock after an idle spell and its power
+controller clamps it a few ms later, so the timed calls run at the clock it
+settles at under continuous load, as in a serving loop (--clock-trace shows
+the transient; the *_after_idle keys time the same calls straight after the
+spin).  One event pair around the K calls gives the GPU time per call (the
+value and the roofline figure; it agrees with the kernel's rocprofv3
+durations for the calls made that far into a run, which each trace summary
+lists), an event pair around each call gives p50/p99.
 
 Prints ONE JSON line.  Options:
   --gpus N          only N = 1 is supported (one GPU per process, no collectives)
@@ -38,6 +43,10 @@ Prints ONE JSON line.  Options:
                     lengths the commit advances in place (no restore); per-step
                     p50/p99 and mean GB/s as the lengths grow (e.g. with
                     --workload ragged_8b --loop 256)
+  --clock-trace N   print the attention time of N back-to-back calls after an
+                    idle spell, per 10 calls, in call order, then exit
+  --workload NAME   step_8b (default), step_1p5b, step_8b_long, ragged_8b,
+                    train_8b (the training-mask attention alone)
   --calibrate-copy  run only a plain device copy of known size (for scaling
                     the FETCH_SIZE / WRITE_SIZE counters)
   --summarize DIR   turn rocprofv3 outputs under DIR (kt/, pmc_FETCH_SIZE/,
