@@ -47,7 +47,7 @@ namespace {
 
 constexpr int PPW = 8;         // waves per workgroup, two per SIMD
 constexpr int PPT = PPW * 64;  // threads per workgroup
-constexpr int kPpDepth = 8;   // LDS operand reads in flight per wave in the MFMA phase
+constexpr int kPpDepth = 4;  // LDS operand reads in flight per wave in the MFMA phase
 
 // s_waitcnt vmcnt(n) for a wave-uniform n that is not a compile-time
 // constant (the load counts of the last ring steps).
@@ -624,8 +624,8 @@ void attn_pp_kernel(AttnArgs a) {
       };
       if (G == 0) {
         cphase(grp_c, j);
+        issue();  // before the softmax, which then runs while the loads are in flight
         softmax(grp_c, j);
-        issue();
       } else {
         if (j > j0) softmax(grp_c, j - 1);
         issue();
