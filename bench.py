@@ -122,6 +122,13 @@ def parse():
                    help="synthetic workload (the reported line is the 8B-shaped step; ragged_8b is one step of "
                         "the serving loop's batch of 32 at its initial lengths; train_8b is the training-mask "
                         "attention over a duplicated sequence, 8B heads, 4 x 2 x 4096 positions, block 8)")
+    p.add_argument("--compare", nargs="+", metavar="LIB",
+                   help="paired timing of the workload's attention call across library builds (libtidar.so "
+                        "first, then each LIB, e.g. a build of another revision): all are loaded in this "
+                        "process and take turns, --steps calls each per round, over --rounds rounds in "
+                        "rotating order after 0.3 s of sustaining calls, so every build runs at the same clock; "
+                        "checks that every build's output equals the first's; one JSON line")
+    p.add_argument("--rounds", type=int, default=40, help="rounds of --compare")
     return p.parse_args()
 
 
@@ -790,6 +797,94 @@ def bench_loop(args, wl, d, v, a_planted, reps, n_rep, attention, verify_commit,
     print(json.dumps(result))
 
 
+def bench_compare(args):
+    """--compare: the attention call of args.workload timed across library
+    builds in one process, interleaved so the part's clock (which moves with
+    the time under load, see --clock-trace) is the same for all of them;
+    single bench lines on one box vary by about +-2 us on the 8B step, more
+    than the differences this resolves."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import diffusion_drafted_self_amd as tidar
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    libs = [tidar.LIB_PATH] + [os.path.abspath(x) for x in args.compare]
+
+    def to_dev(x, bf16):
+        x = np.ascontiguousarray(x)
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16) if bf16 else torch.from_numpy(x).to(dev)
+
+    if args.workload == "train_8b":
+        c = TRAIN
+        d = W.train_inputs(c["B"], c["Hq"], c["Hkv"], c["D"], c["N"], seed=args.seed)
+        base = {n: to_dev(d[n], True) for n in ("q", "k", "v")}
+        n_rep = 2
+        reps = [{**{n: t.clone() for n, t in base.items()}, "out": torch.empty_like(base["q"]),
+                 "lse": torch.empty((c["B"], c["Hq"], 2 * c["N"]), dtype=torch.float32, device=dev)}
+                for _ in range(n_rep)]
+
+        def call(r):
+            tidar.train_attention(r["q"], r["k"], r["v"], c["N"], c["block"], 1.0 / math.sqrt(c["D"]), out=r["out"],
+                                  lse=r["lse"])
+    else:
+        wl = W.WORKLOADS[args.workload]()
+        s = wl.attn
+        d = W.attention_inputs(s, seed=args.seed, config_id=wl.config_id, tail="zero")
+        base = {n: to_dev(x, n != "lens") for n, x in d.items()}
+        n_rep = max(2, math.ceil(args.cold_bytes / sum(t.numel() * t.element_size() for t in base.values())))
+        ws = tidar.step_attention_workspace_bytes(0, s.B, s.Hq, s.Hkv, s.D, s.S_max, s.max_len, s.k, s.n_groups,
+                                                  args.kv_chunk)
+        reps = [{**{n: t.clone() for n, t in base.items()}, "out": torch.empty_like(base["q"]),
+                 "lse": torch.empty((s.B, s.Hq, s.R), dtype=torch.float32, device=dev),
+                 "ws": torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)} for _ in range(n_rep)]
+
+        def call(r):
+            tidar.step_attention(r["q"], r["k_step"], r["v_step"], r["k_cache"], r["v_cache"], r["lens"], s.k,
+                                 s.n_groups, s.sm_scale, max_len=s.max_len, out=r["out"], lse=r["lse"],
+                                 workspace=r["ws"], kv_chunk=args.kv_chunk)
+    del base
+    outs = []
+    for path in libs:
+        with tidar.library(path):
+            call(reps[0])
+            torch.cuda.synchronize()
+            outs.append(reps[0]["out"].float().clone())
+    diffs = [float((o - outs[0]).abs().max().item()) for o in outs[1:]]
+    K, i = args.steps, 0
+    with tidar.library(libs[0]):
+        t0 = time.time()
+        while time.time() - t0 < 0.3:  # sustaining calls: the clock the part settles at under load
+            call(reps[i % n_rep])
+            i += 1
+    times = {p: [] for p in libs}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for rd in range(args.rounds):
+        for path in libs[rd % len(libs):] + libs[:rd % len(libs)]:
+            with tidar.library(path):
+                for j in range(3):  # untimed: the change of code object
+                    call(reps[(i + j) % n_rep])
+                i += 3
+                ev[0].record()
+                for j in range(K):
+                    call(reps[(i + j) % n_rep])
+                ev[1].record()
+                i += K
+                torch.cuda.synchronize()
+            times[path].append(ev[0].elapsed_time(ev[1]) * 1e3 / K)
+    med0 = statistics.median(times[libs[0]])
+    print(json.dumps({
+        "metric": "attention us per call, paired across library builds", "workload": args.workload,
+        "calls_per_round": K, "rounds": args.rounds,
+        "libraries": [{"path": os.path.relpath(p), "median_us": round(statistics.median(times[p]), 2),
+                       "mean_us": round(statistics.mean(times[p]), 2), "min_us": round(min(times[p]), 2),
+                       "vs_first_pct": round(100 * (statistics.median(times[p]) / med0 - 1), 2)} for p in libs],
+        "max_abs_out_diff_vs_first": diffs}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -810,6 +905,9 @@ def main():
         return
     if args.summarize_lmhead:
         summarize_lmhead(args.summarize_lmhead)
+        return
+    if args.compare:
+        bench_compare(args)
         return
     if args.workload == "train_8b":
         bench_train(args)

@@ -130,6 +130,33 @@ class checked_library:
         return False
 
 
+class library:
+    """Context manager: inside it every call of this module goes through the
+    library file at ``path``, another build of these sources with the same
+    ABI version (e.g. to time two builds against each other in one process:
+    ``bench.py --compare``)."""
+
+    def __init__(self, path: str):
+        self.path = os.path.abspath(path)
+
+    def __enter__(self):
+        global _LIB
+        self._prev = lib()
+        h = _LOADED.get(self.path)
+        if h is None:
+            h = _LOADED[self.path] = _load(self.path)
+        if h.tidar_abi_version() != self._prev.tidar_abi_version():
+            raise ImportError(f"{self.path} has ABI version {h.tidar_abi_version()}, "
+                              f"this binding {self._prev.tidar_abi_version()}")
+        _LIB = h
+        return self
+
+    def __exit__(self, *exc):
+        global _LIB
+        _LIB = self._prev
+        return False
+
+
 def check_read(clear: bool = True):
     """(code, workgroup, thread, value) of the first failed bounds test the
     current library recorded on the current device, code 0 if none (always 0
@@ -744,4 +771,4 @@ __all__ = ["step_attention", "step_attention_workspace_bytes", "verify_greedy", 
            "step_attention_paged", "kv_commit_paged", "train_attention",
            "lmhead_verify_greedy", "lmhead_verify_workspace_bytes", "lmhead_pack", "lmhead_packed_bytes",
            "lmhead_verify_greedy_packed", "strerror", "lib", "TidarError", "LIB_PATH", "SIGNATURES",
-           "read_probe", "READ_PROBE_BLOCKS", "checked_library", "check_read", "CHECK_CODES", "LIB_CHECKED_PATH"]
+           "read_probe", "READ_PROBE_BLOCKS", "checked_library", "library", "check_read", "CHECK_CODES", "LIB_CHECKED_PATH"]

@@ -81,6 +81,21 @@ def test_check_codes_match_the_header(T):
     assert codes == T.CHECK_CODES
 
 
+def test_library_switch(T):
+    """tidar.library(path) routes the module's calls through another build of
+    the same ABI (bench.py --compare times builds against each other that
+    way) and restores the previous library on exit; a missing file raises."""
+    before = T.lib()
+    with T.library(T.LIB_CHECKED_PATH):
+        assert T.lib() is not before
+        assert T.lib().tidar_check_enabled() == 1
+    assert T.lib() is before
+    with pytest.raises(ImportError):
+        with T.library(T.LIB_PATH + ".missing"):
+            pass
+    assert T.lib() is before
+
+
 def test_strerror_and_version(T):
     assert T.lib().tidar_abi_version() == 1
     for code in (0, -1, -2, -3, -4, 7):
