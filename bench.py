@@ -129,6 +129,9 @@ def parse():
                         "rotating order after 0.3 s of sustaining calls, so every build runs at the same clock; "
                         "checks that every build's output equals the first's; one JSON line")
     p.add_argument("--rounds", type=int, default=40, help="rounds of --compare")
+    p.add_argument("--compare-call", default="attention", choices=["attention", "verify_commit"],
+                   help="the call --compare times: the step attention, or the fused greedy verify + commit "
+                        "(with the 64-byte restore of the settled lengths after each call, as in the step)")
     return p.parse_args()
 
 
@@ -818,7 +821,30 @@ def bench_compare(args):
         x = np.ascontiguousarray(x)
         return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16) if bf16 else torch.from_numpy(x).to(dev)
 
-    if args.workload == "train_8b":
+    cur = {"path": libs[0]}
+    if args.compare_call == "verify_commit":
+        wl = W.WORKLOADS[args.workload]()
+        s = wl.attn
+        d = W.attention_inputs(s, seed=args.seed, config_id=wl.config_id, tail="zero")
+        v = W.verify_inputs(s.B, s.k, wl.V, seed=args.seed, config_id=wl.config_id, accept=wl.accept)
+        base = {n: to_dev(d[n], n != "lens") for n in ("k_cache", "v_cache", "k_step", "v_step", "lens")}
+        base.update({n: to_dev(v[n], False) for n in ("ar_logits", "draft_logits", "cand")})
+        n_rep = max(2, math.ceil(args.cold_bytes / sum(t.numel() * t.element_size() for t in base.values())))
+        reps = [{**{n: t.clone() for n, t in base.items()}, "lens0": base["lens"].clone(),
+                 "acc": torch.empty(s.B, dtype=torch.int32, device=dev),
+                 "out": torch.empty((s.B, s.k), dtype=torch.int32, device=dev),
+                 "err": torch.empty(s.B, dtype=torch.int32, device=dev)} for _ in range(n_rep)]
+        states = {}
+        for path in libs:
+            with tidar.library(path):
+                states[path] = tidar.verify_commit_state(s.B, s.k, dev)
+
+        def call(r):
+            tidar.verify_commit_greedy(r["ar_logits"], r["draft_logits"], r["cand"], r["k_cache"], r["v_cache"],
+                                       r["lens"], r["k_step"], r["v_step"], accept_len=r["acc"], next_cand=r["out"],
+                                       err_flags=r["err"], state=states[cur["path"]])
+            r["lens"].copy_(r["lens0"])
+    elif args.workload == "train_8b":
         c = TRAIN
         d = W.train_inputs(c["B"], c["Hq"], c["Hkv"], c["D"], c["N"], seed=args.seed)
         base = {n: to_dev(d[n], True) for n in ("q", "k", "v")}
@@ -850,12 +876,16 @@ def bench_compare(args):
     outs = []
     for path in libs:
         with tidar.library(path):
+            cur["path"] = path
             call(reps[0])
             torch.cuda.synchronize()
             outs.append(reps[0]["out"].float().clone())
+            if args.compare_call == "verify_commit":  # accept lengths too, and the cache rows written
+                outs[-1] = torch.cat([outs[-1].flatten(), reps[0]["acc"].float(), reps[0]["err"].float()])
     diffs = [float((o - outs[0]).abs().max().item()) for o in outs[1:]]
     K, i = args.steps, 0
     with tidar.library(libs[0]):
+        cur["path"] = libs[0]
         t0 = time.time()
         while time.time() - t0 < 0.3:  # sustaining calls: the clock the part settles at under load
             call(reps[i % n_rep])
@@ -865,6 +895,7 @@ def bench_compare(args):
     for rd in range(args.rounds):
         for path in libs[rd % len(libs):] + libs[:rd % len(libs)]:
             with tidar.library(path):
+                cur["path"] = path
                 for j in range(3):  # untimed: the change of code object
                     call(reps[(i + j) % n_rep])
                 i += 3
@@ -877,7 +908,7 @@ def bench_compare(args):
             times[path].append(ev[0].elapsed_time(ev[1]) * 1e3 / K)
     med0 = statistics.median(times[libs[0]])
     print(json.dumps({
-        "metric": "attention us per call, paired across library builds", "workload": args.workload,
+        "metric": f"{args.compare_call} us per call, paired across library builds", "workload": args.workload,
         "calls_per_round": K, "rounds": args.rounds,
         "libraries": [{"path": os.path.relpath(p), "median_us": round(statistics.median(times[p]), 2),
                        "mean_us": round(statistics.mean(times[p]), 2), "min_us": round(min(times[p]), 2),
