@@ -129,6 +129,9 @@ def parse():
                         "rotating order after 0.3 s of sustaining calls, so every build runs at the same clock; "
                         "checks that every build's output equals the first's; one JSON line")
     p.add_argument("--rounds", type=int, default=40, help="rounds of --compare")
+    p.add_argument("--probes", action="store_true",
+                   help="only the matrix-core issue probe (tidar_mfma_probe): cycles per MFMA with one and two "
+                        "waves per SIMD, operands in registers or read from LDS; one JSON line")
     p.add_argument("--compare-call", default="attention", choices=["attention", "verify_commit"],
                    help="the call --compare times: the step attention, or the fused greedy verify + commit "
                         "(with the 64-byte restore of the settled lengths after each call, as in the step)")
@@ -916,6 +919,44 @@ def bench_compare(args):
         "max_abs_out_diff_vs_first": diffs}))
 
 
+def bench_probes(args):
+    """--probes: the matrix cores' issue interval (tidar_mfma_probe) with one
+    and two waves per SIMD, operands in registers or read from LDS; one JSON
+    line."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import diffusion_drafted_self_amd as tidar
+
+    dev = torch.device("cuda:0")
+    iters = 4096
+    res = {}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for lds in (0, 1):
+        for w in (1, 2):
+            tidar.mfma_probe(w, lds, 64, dev)  # warm-up (code object, clock)
+            torch.cuda.synchronize()
+            ev[0].record()
+            c = tidar.mfma_probe(w, lds, iters, dev)
+            ev[1].record()
+            torch.cuda.synchronize()
+            cyc = c.cpu().numpy()
+            if (cyc < 0).any():
+                raise RuntimeError("mfma probe: a record carries the impossible-sum mark")
+            med, mx = float(np.median(cyc)), float(cyc.max())
+            us = ev[0].elapsed_time(ev[1]) * 1e3
+            # the waves of a SIMD start together; the SIMD's MFMAs are done when its last wave is
+            res[f"{'lds' if lds else 'registers'}_{w}_waves_per_simd"] = {
+                "simd_cycles_per_mfma": round(mx / (8 * iters * w), 2),
+                "wave_cycles_per_mfma_median": round(med / (8 * iters), 2),
+                "wave_cycles_median": int(med), "wave_cycles_max": int(mx),
+                "kernel_us": round(us, 1), "shader_mhz": round(mx / us, 0)}
+    print(json.dumps({"metric": "issue interval of v_mfma_f32_16x16x32_bf16 (shader-clock cycles)",
+                      "iters": iters, "mfma_per_round": 8, "workgroups": tidar.MFMA_PROBE_BLOCKS, "results": res}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -936,6 +977,9 @@ def main():
         return
     if args.summarize_lmhead:
         summarize_lmhead(args.summarize_lmhead)
+        return
+    if args.probes:
+        bench_probes(args)
         return
     if args.compare:
         bench_compare(args)

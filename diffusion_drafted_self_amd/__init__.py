@@ -63,6 +63,7 @@ SIGNATURES = {
     "tidar_verify_commit_greedy_noalloc": (_c_int, [_c_int] * 8 + [_p] * 11 + [_p]),
     "tidar_launch_shapes": (_c_int, [_c_int] * 7 + [ctypes.POINTER(_c_int)]),
     "tidar_read_probe": (_c_int, [_p, _c_size, _p, _p]),
+    "tidar_mfma_probe": (_c_int, [_c_int, _c_int, _c_int, _p, _p]),
     "tidar_check_enabled": (_c_int, []),
     "tidar_check_read": (_c_int, [ctypes.POINTER(ctypes.c_uint32), _c_int]),
 }
@@ -766,9 +767,23 @@ def read_probe(buf, sink=None):
     return sink
 
 
+MFMA_PROBE_BLOCKS = 256  # TIDAR_MFMA_PROBE_BLOCKS
+
+
+def mfma_probe(waves_per_simd: int, lds_reads: bool, iters: int, device="cuda"):
+    """Shader-clock cycles of ``iters`` rounds of eight independent bf16
+    16x16x32 MFMAs per wave (operands from LDS when ``lds_reads``), one
+    int64 per wave of MFMA_PROBE_BLOCKS workgroups of 4 * waves_per_simd
+    waves (tidar_mfma_probe); enqueued on the current stream."""
+    cycles = torch.zeros(MFMA_PROBE_BLOCKS * 4 * waves_per_simd, dtype=torch.int64, device=device)
+    _check("tidar_mfma_probe", lib().tidar_mfma_probe(int(waves_per_simd), 1 if lds_reads else 0, int(iters),
+                                                      _ptr(cycles), _stream()))
+    return cycles
+
+
 __all__ = ["step_attention", "step_attention_workspace_bytes", "verify_greedy", "verify_workspace_bytes",
            "verify_sample", "verify_sample_workspace_bytes", "kv_commit",
            "step_attention_paged", "kv_commit_paged", "train_attention",
            "lmhead_verify_greedy", "lmhead_verify_workspace_bytes", "lmhead_pack", "lmhead_packed_bytes",
            "lmhead_verify_greedy_packed", "strerror", "lib", "TidarError", "LIB_PATH", "SIGNATURES",
-           "read_probe", "READ_PROBE_BLOCKS", "checked_library", "library", "check_read", "CHECK_CODES", "LIB_CHECKED_PATH"]
+           "read_probe", "READ_PROBE_BLOCKS", "mfma_probe", "MFMA_PROBE_BLOCKS", "checked_library", "library", "check_read", "CHECK_CODES", "LIB_CHECKED_PATH"]

@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtidar.so")
 LIB_CHECKED = os.path.join(HERE, "libtidar_checked.so")
-SOURCES = ["attention.hip", "attention_pp.hip", "verify.hip", "verify_fused.hip", "verify_sample.hip", "lmhead.hip", "commit.hip", "read_probe.hip", "capi.cpp"]
+SOURCES = ["attention.hip", "attention_pp.hip", "verify.hip", "verify_fused.hip", "verify_sample.hip", "lmhead.hip", "commit.hip", "read_probe.hip", "mfma_probe.hip", "capi.cpp"]
 ARCH = "gfx950"
 
 

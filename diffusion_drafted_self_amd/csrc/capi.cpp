@@ -839,6 +839,19 @@ int tidar_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream
   return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
 }
 
+static_assert(TIDAR_MFMA_PROBE_BLOCKS == tidar::kMfmaProbeBlocks, "MFMA probe record count");
+
+int tidar_mfma_probe(int waves_per_simd, int lds_reads, int iters, uint64_t* cycles, void* stream) {
+  if (waves_per_simd != 1 && waves_per_simd != 2) return TIDAR_EINVAL;
+  if (lds_reads != 0 && lds_reads != 1) return TIDAR_EINVAL;
+  if (iters < 1 || iters > (1 << 20)) return TIDAR_EINVAL;
+  if (!aligned(cycles, 8)) return TIDAR_EINVAL;
+  const hipError_t e = tidar::launch_mfma_probe(waves_per_simd, lds_reads, iters,
+                                                reinterpret_cast<unsigned long long*>(cycles),
+                                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TIDAR_OK : TIDAR_ELAUNCH;
+}
+
 int tidar_check_enabled(void) { return TIDAR_CHECKED ? 1 : 0; }
 
 int tidar_check_read(uint32_t* rec, int clear) {

@@ -533,6 +533,28 @@ int tidar_check_read(uint32_t* rec, int clear);
 
 int tidar_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
+/* tidar_mfma_probe measures the issue interval of the matrix cores (a
+ * measurement helper, not part of the decode step).  It launches
+ * TIDAR_MFMA_PROBE_BLOCKS workgroups, one per CU, each of 4 x waves_per_simd
+ * waves (waves_per_simd waves on each SIMD).  Every wave runs `iters` rounds
+ * of eight independent v_mfma_f32_16x16x32_bf16 on eight accumulators.  With
+ * lds_reads = 1 the A operand of each MFMA is read from LDS first (16 B per
+ * lane, one conflict-free 1 KB block per MFMA, four reads ahead), the
+ * operand pattern of the attention loops; with 0 it is held in registers.
+ * Each wave writes the shader-clock cycles of its rounds to
+ * cycles[workgroup * 4 * waves_per_simd + wave]; cycles / (8 * iters) is that
+ * wave's interval between MFMAs, and with two waves per SIMD the SIMD issues
+ * two MFMAs in that interval.
+ *
+ *   waves_per_simd  1 or 2.   lds_reads  0 or 1.   iters  1 .. 2^20.
+ *   cycles  device pointer to TIDAR_MFMA_PROBE_BLOCKS * 4 * waves_per_simd
+ *           uint64 (8-byte aligned), owned by the caller.
+ *   Returns TIDAR_EINVAL for other values or a null or misaligned pointer,
+ *   TIDAR_ELAUNCH if the launch fails. */
+#define TIDAR_MFMA_PROBE_BLOCKS 256
+
+int tidar_mfma_probe(int waves_per_simd, int lds_reads, int iters, uint64_t* cycles, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

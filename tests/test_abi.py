@@ -81,6 +81,20 @@ def test_check_codes_match_the_header(T):
     assert codes == T.CHECK_CODES
 
 
+def test_mfma_probe_validation(T):
+    """tidar_mfma_probe refuses other wave counts, round counts and a null
+    record pointer before anything is enqueued (host checks only)."""
+    L = T.lib()
+    good = ctypes.c_void_p(256)  # an aligned stand-in address; never dereferenced on a refusal
+    assert L.tidar_mfma_probe(3, 0, 16, good, None) == T.TIDAR_EINVAL
+    assert L.tidar_mfma_probe(0, 0, 16, good, None) == T.TIDAR_EINVAL
+    assert L.tidar_mfma_probe(1, 2, 16, good, None) == T.TIDAR_EINVAL
+    assert L.tidar_mfma_probe(1, 0, 0, good, None) == T.TIDAR_EINVAL
+    assert L.tidar_mfma_probe(1, 0, (1 << 20) + 1, good, None) == T.TIDAR_EINVAL
+    assert L.tidar_mfma_probe(1, 0, 16, None, None) == T.TIDAR_EINVAL
+    assert L.tidar_mfma_probe(1, 0, 16, ctypes.c_void_p(260), None) == T.TIDAR_EINVAL
+
+
 def test_library_switch(T):
     """tidar.library(path) routes the module's calls through another build of
     the same ABI (bench.py --compare times builds against each other that

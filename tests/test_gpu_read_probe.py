@@ -20,3 +20,19 @@ def test_read_probe_folds_every_word(n_words):
     sink = tidar.read_probe(buf)
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == np.bitwise_xor.reduce(host)
+
+
+@pytest.mark.parametrize("waves_per_simd", [1, 2])
+@pytest.mark.parametrize("lds_reads", [False, True])
+def test_mfma_probe_records_every_wave(waves_per_simd, lds_reads):
+    """The issue-rate probe writes a cycle count for every wave of its
+    workgroups, no record carries the impossible-sum mark, and twice the
+    rounds take about twice the cycles (the count measures the rounds)."""
+    print(f"mfma probe: {waves_per_simd} waves per SIMD, lds {lds_reads}", flush=True)
+    short = tidar.mfma_probe(waves_per_simd, lds_reads, 256).cpu().numpy()
+    long = tidar.mfma_probe(waves_per_simd, lds_reads, 512).cpu().numpy()
+    assert short.shape == (tidar.MFMA_PROBE_BLOCKS * 4 * waves_per_simd,)
+    assert (short > 0).all() and (long > 0).all()
+    # at least 16 clocks per MFMA (the pipe's own interval) and a round count that scales
+    assert np.median(short) >= 16 * 8 * 256
+    assert 1.5 < np.median(long) / np.median(short) < 2.5
