@@ -12,6 +12,7 @@
 #include <cstring>
 
 #include "launch.h"
+#include "probe.h"
 
 namespace {
 

@@ -141,8 +141,6 @@ hipError_t launch_lmhead_pack(const void* w, void* wp, int V, int d, hipStream_t
 hipError_t launch_read_probe(const void* src, size_t bytes, unsigned* sink, hipStream_t s);
 
 constexpr int kReadProbeBlocks = 16384;  // workgroups of the streaming-read probe
-hipError_t launch_mfma_probe(int waves_per_simd, int lds_reads, int iters, unsigned long long* cycles, hipStream_t s);
-constexpr int kMfmaProbeBlocks = 256;  // workgroups of the MFMA issue-rate probe, one per CU
 constexpr int kArgmaxChunk = 4096;  // logits per workgroup of the greedy argmax
 constexpr int kDraftSpan = 2 * kArgmaxChunk;  // logits per workgroup of the fused path's draft pass
 constexpr int kSampleChunk = 4096;  // vocabulary entries per workgroup of the sampling kernels

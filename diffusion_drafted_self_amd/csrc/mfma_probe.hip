@@ -11,7 +11,7 @@
 // rounds.  Cycles per MFMA of one wave, times the waves that share a SIMD,
 // give the SIMD's issue interval.
 #include "common.h"
-#include "launch.h"
+#include "probe.h"
 
 namespace tidar {
 
