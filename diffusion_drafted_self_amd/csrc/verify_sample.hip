@@ -70,8 +70,11 @@ __device__ __forceinline__ U4 philox4x32_10(U4 c, unsigned k0, unsigned k1) {
       k0 += kPhiloxW0;
       k1 += kPhiloxW1;
     }
-    const unsigned lo0 = kPhiloxM0 * c.x, hi0 = __umulhi(kPhiloxM0, c.x);
-    const unsigned lo1 = kPhiloxM1 * c.z, hi1 = __umulhi(kPhiloxM1, c.z);
+    // one 32 x 32 -> 64-bit product per word (v_mad_u64_u32) gives both halves
+    const unsigned long long p0 = (unsigned long long)kPhiloxM0 * c.x;
+    const unsigned long long p1 = (unsigned long long)kPhiloxM1 * c.z;
+    const unsigned lo0 = (unsigned)p0, hi0 = (unsigned)(p0 >> 32);
+    const unsigned lo1 = (unsigned)p1, hi1 = (unsigned)(p1 >> 32);
     c = U4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
   }
   return c;
